@@ -1,0 +1,269 @@
+"""CPU oracle for NVFP4 block-scaled quantization -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it and shares no code with it.
+
+The arithmetic lives in ``nvfp4_oracle.c`` (plain C, see its header for the
+sources and the precision rules); this module only marshals numpy arrays.
+Inputs are bfloat16 bit patterns (``uint16``) or float32 arrays; bf16 is
+widened to float32 exactly (the bits shifted into the high half).
+
+Parity unpinned: the UE5M3 scale format (no outside definition exists on the
+pages; only its stated closed form is checked).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+FMT_E4M3, FMT_UE5M3 = 0, 1
+SELECT_6, SELECT_4OVER6 = 0, 1
+ROUND_RNE, ROUND_SR = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    src = os.path.join(_HERE, "nvfp4_oracle.c")
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.or_e2m1_value.restype = ctypes.c_double
+    lib.or_e2m1_value.argtypes = [ctypes.c_int]
+    lib.or_e2m1_code.restype = ctypes.c_int
+    lib.or_e2m1_code.argtypes = [ctypes.c_float]
+    lib.or_e2m1_code_sr.restype = ctypes.c_int
+    lib.or_e2m1_code_sr.argtypes = [ctypes.c_float, ctypes.c_uint32]
+    lib.or_scale_decode.restype = ctypes.c_double
+    lib.or_scale_decode.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.or_scale_encode.restype = ctypes.c_int
+    lib.or_scale_encode.argtypes = [ctypes.c_int, ctypes.c_float]
+    lib.or_scale_nan_code.restype = ctypes.c_int
+    lib.or_scale_nan_code.argtypes = [ctypes.c_int]
+    lib.or_fmix32.restype = ctypes.c_uint32
+    lib.or_fmix32.argtypes = [ctypes.c_uint32]
+    lib.or_sr_hash.restype = ctypes.c_uint32
+    lib.or_sr_hash.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    lib.or_tensor_amax.restype = ctypes.c_float
+    lib.or_tensor_amax.argtypes = [_f32p, _i64]
+    lib.or_alpha.restype = ctypes.c_float
+    lib.or_alpha.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.or_quantize.restype = ctypes.c_int
+    lib.or_quantize.argtypes = [_f32p, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                _u8p, _u8p, _u64p, _f32p, _f32p]
+    lib.or_dequantize.restype = ctypes.c_int
+    lib.or_dequantize.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, ctypes.c_float,
+                                  ctypes.c_int, _f32p, _u16p, _f32p]
+    lib.or_sse.restype = ctypes.c_double
+    lib.or_sse.argtypes = [_f32p, _f32p, _i64]
+    lib.or_f32_to_bf16.restype = ctypes.c_uint16
+    lib.or_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.or_fakequant_fwd.restype = ctypes.c_int
+    lib.or_fakequant_fwd.argtypes = [_f32p, _i64, _i64, _f32p, _f32p, _f32p]
+    lib.or_fakequant_bwd.restype = ctypes.c_int
+    lib.or_fakequant_bwd.argtypes = [_f32p, _f32p, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p]
+    lib.or_num_threads.restype = ctypes.c_int
+    lib.or_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a, t):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(t)
+
+
+def as_f32(x):
+    """bf16 bits (uint16) -> float32 exactly; float32 passes through."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x)
+    raise TypeError(f"oracle input must be bf16 bits (uint16) or float32, got {x.dtype}")
+
+
+def _fmt(fmt):
+    if isinstance(fmt, str):
+        return {"e4m3": FMT_E4M3, "ue5m3": FMT_UE5M3}[fmt]
+    return int(fmt)
+
+
+# ---------------------------------------------------------------- scalars
+def e2m1_value(code):
+    return _load().or_e2m1_value(int(code))
+
+
+def e2m1_code(y):
+    return _load().or_e2m1_code(float(y))
+
+
+def e2m1_code_sr(y, h):
+    return _load().or_e2m1_code_sr(float(y), int(h) & 0xFFFFFFFF)
+
+
+def scale_decode(fmt, code):
+    return _load().or_scale_decode(_fmt(fmt), int(code))
+
+
+def scale_encode(fmt, s):
+    return _load().or_scale_encode(_fmt(fmt), float(s))
+
+
+def scale_nan_code(fmt):
+    return _load().or_scale_nan_code(_fmt(fmt))
+
+
+def fmix32(h):
+    return _load().or_fmix32(int(h) & 0xFFFFFFFF)
+
+
+def sr_hash(seed, idx):
+    return _load().or_sr_hash(int(seed), int(idx))
+
+
+def alpha(amax, sg):
+    return _load().or_alpha(float(amax), float(sg))
+
+
+def f32_to_bf16(f):
+    return _load().or_f32_to_bf16(float(f))
+
+
+def num_threads():
+    return _load().or_num_threads()
+
+
+def default_global_max(fmt, select):
+    """The FP8 maximum S_g the outer scale maps the tensor amax to."""
+    fmt = _fmt(fmt)
+    if fmt == FMT_UE5M3:
+        return 114688.0
+    return 256.0 if int(select) == SELECT_4OVER6 else 448.0
+
+
+# ---------------------------------------------------------------- tensors
+def tensor_amax(x):
+    xf = as_f32(x).ravel()
+    return _load().or_tensor_amax(_ptr(xf, _f32p), xf.size)
+
+
+def quantize(x, amax, *, fmt=FMT_E4M3, select=SELECT_4OVER6, rounding=ROUND_RNE, seed=0,
+             global_max=None, row0=0, want_sse=False):
+    """Row-wise quantization of a 2-D array.  Returns (codes, scales, count4)
+    or, with want_sse, (codes, scales, count4, sse_chosen, sse_six)."""
+    xf = as_f32(x)
+    assert xf.ndim == 2
+    rows, cols = xf.shape
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, select) if global_max is None else float(global_max)
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    cnt = np.zeros(1, np.uint64)
+    sse_sel = np.empty((rows, cols // 16), np.float32) if want_sse else None
+    sse6 = np.empty((rows, cols // 16), np.float32) if want_sse else None
+    st = _load().or_quantize(_ptr(xf, _f32p), rows, cols, int(row0), float(amax), sg, fmt,
+                             int(select), int(rounding), int(seed), _ptr(codes, _u8p),
+                             _ptr(scales, _u8p), _ptr(cnt, _u64p), _ptr(sse_sel, _f32p),
+                             _ptr(sse6, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle quantize rejected the arguments (status {st})")
+    if want_sse:
+        return codes, scales, int(cnt[0]), sse_sel, sse6
+    return codes, scales, int(cnt[0])
+
+
+def quantize_cols(x, amax, *, col0=0, **kw):
+    """Column-wise quantization: blocks of 16 consecutive rows of one column,
+    i.e. the row-wise quantization of the transpose (output is X^T's)."""
+    xt = np.ascontiguousarray(as_f32(x).T)
+    return quantize(xt, amax, row0=col0, **kw)
+
+
+def dequantize(codes, scales, amax, *, fmt=FMT_E4M3, select=SELECT_4OVER6, global_max=None,
+               want_bf16=False, want_block_scale=False):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, half = codes.shape
+    cols = 2 * half
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, select) if global_max is None else float(global_max)
+    out = np.empty((rows, cols), np.float32)
+    ob = np.empty((rows, cols), np.uint16) if want_bf16 else None
+    bs = np.empty((rows, cols // 16), np.float32) if want_block_scale else None
+    st = _load().or_dequantize(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, float(amax),
+                               sg, fmt, _ptr(out, _f32p), _ptr(ob, _u16p), _ptr(bs, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle dequantize rejected the arguments (status {st})")
+    res = [out]
+    if want_bf16:
+        res.append(ob)
+    if want_block_scale:
+        res.append(bs)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def sse(x, xhat):
+    xf = np.ascontiguousarray(as_f32(x)).ravel()
+    xh = np.ascontiguousarray(xhat, dtype=np.float32).ravel()
+    assert xf.size == xh.size
+    return _load().or_sse(_ptr(xf, _f32p), _ptr(xh, _f32p), xf.size)
+
+
+def fakequant_fwd(x, s_pre, s_post=None):
+    xf = as_f32(x)
+    rows, cols = xf.shape
+    sp = np.ascontiguousarray(s_pre, dtype=np.float32)
+    so = None if s_post is None else np.ascontiguousarray(s_post, dtype=np.float32)
+    out = np.empty((rows, cols), np.float32)
+    st = _load().or_fakequant_fwd(_ptr(xf, _f32p), rows, cols, _ptr(sp, _f32p),
+                                  _ptr(so, _f32p), _ptr(out, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle fakequant_fwd rejected the arguments (status {st})")
+    return out
+
+
+def fakequant_bwd(x, g, s_pre, s_post=None):
+    """Returns (dx, ds) for tied scales, (dx, ds_pre, ds_post) for dual."""
+    xf = as_f32(x)
+    rows, cols = xf.shape
+    gf = np.ascontiguousarray(g, dtype=np.float32)
+    sp = np.ascontiguousarray(s_pre, dtype=np.float32)
+    so = None if s_post is None else np.ascontiguousarray(s_post, dtype=np.float32)
+    dx = np.empty((rows, cols), np.float32)
+    dpre = np.empty(sp.shape, np.float32)
+    dpost = None if s_post is None else np.empty(sp.shape, np.float32)
+    st = _load().or_fakequant_bwd(_ptr(xf, _f32p), _ptr(gf, _f32p), rows, cols, _ptr(sp, _f32p),
+                                  _ptr(so, _f32p), _ptr(dx, _f32p), _ptr(dpre, _f32p),
+                                  _ptr(dpost, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle fakequant_bwd rejected the arguments (status {st})")
+    if s_post is None:
+        return dx, dpre
+    return dx, dpre, dpost
+
+
+def unpack_codes(codes):
+    """[rows, cols/2] bytes -> [rows, cols] 4-bit codes (low nibble first)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty((codes.shape[0], codes.shape[1] * 2), np.uint8)
+    out[:, 0::2] = codes & 15
+    out[:, 1::2] = codes >> 4
+    return out

@@ -1,0 +1,490 @@
+/*
+ * nvfp4_oracle.c -- TEST INFRASTRUCTURE, NOT PRODUCT CODE.
+ *
+ * A plain, slow CPU statement of NVFP4 block-scaled quantization, the
+ * Four-Over-Six block-scale choice, stochastic rounding, and scale-learning
+ * fake quantization with its straight-through gradients.  Only the tests,
+ * the smoke check and the benchmark's CPU-baseline leg may load it; the
+ * HIP library never links, includes or calls anything here, and nothing
+ * here is shared with it.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [SL]  "Scale Learning: Training NVFP4 Block Scales to Recover Accuracy"
+ *         (NVIDIA Model Optimizer blog), section "How Scale Learning Works".
+ *   [UE]  "UE5M3: 给 FP4 训练算一笔更宽容的账" (blog on the UE5M3 block-scale
+ *         paper), sections 背景, 数学推导, 实现.
+ *   [E2E] "End-to-End 4-Bit Training" (Thinking Machines), sections
+ *         "Low-precision formats on Blackwell", "Block-scaled backward
+ *         passes", "Re-quantization with stochastic rounding".
+ *   [46a] "Four Over Six: More Accurate NVFP4 Quantization with Adaptive
+ *         Block Scaling" (gist.science summary), sections Probleemstelling,
+ *         Methodologie, Implementatiedetails.
+ *   [46b] same title (bud-325 notes), sections "TL;DR", "Method", "Results".
+ *
+ * Precision.  Where a floating-point value decides a code (a scale byte, a
+ * 4-bit element code, the 4-vs-6 choice, the in-range test of the clamp) the
+ * oracle takes that decision in binary32 with the operation order written
+ * below, which is the order the GPU kernels use; the pages fix only that the
+ * outer scale is FP32 ([E2E] Low-precision formats).  Every floating-point
+ * OUTPUT (dequantized values, fake-quantized values, gradients, squared
+ * error) is computed in binary64 from those decisions and rounded once to
+ * binary32 at the end.  Build: gcc -O2 -ffp-contract=off, no fast-math, so
+ * every float operation rounds once and fmaf() is the only fused operation.
+ *
+ * Parity unpinned: the UE5M3 format itself.  The pages say only that it is
+ * unsigned with 5 exponent and 3 mantissa bits ([UE] 数学推导); bias 15,
+ * subnormals, 0xFF = NaN and the 114688 maximum are a reading (the E4M3FN
+ * pattern carried over), checked here only against its own closed form.
+ */
+#include <float.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_FMT_E4M3 0
+#define OR_FMT_UE5M3 1
+#define OR_SELECT_6 0
+#define OR_SELECT_4OVER6 1
+#define OR_ROUND_RNE 0
+#define OR_ROUND_SR 1
+
+#define OR_OK 0
+#define OR_EINVAL 1
+
+/* ------------------------------------------------------------------ */
+/* E2M1 element format: magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} indexed by the
+ * 3-bit code, sign in bit 3 ([E2E] Low-precision formats; [UE] 背景). */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double or_e2m1_value(int code) {
+  double v = E2M1_MAG[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* Nearest E2M1 magnitude to a >= 0; an exact midpoint goes to the even code
+ * (round-to-nearest-even).  Anything above 6 is nearest to 6, which is the
+ * clamp at q_max of [SL] How Scale Learning Works. */
+static int e2m1_nearest_mag(double a) {
+  if (a >= 6.0) return 7; /* nearest is 6; said outright so that huge a,
+                             whose distances all round alike, cannot tie */
+  int best = 0;
+  double best_d = a;
+  for (int k = 1; k < 8; ++k) {
+    double d = fabs(a - E2M1_MAG[k]);
+    if (d < best_d || (d == best_d && (k & 1) == 0)) {
+      best = k;
+      best_d = d;
+    }
+  }
+  return best;
+}
+
+/* Round y to E2M1 (round-to-nearest-even), keeping the sign bit of y. */
+int or_e2m1_code(float y) {
+  int sign = signbit(y) ? 8 : 0;
+  return sign | e2m1_nearest_mag(fabs((double)y));
+}
+
+/* Stochastic rounding of y onto E2M1 ([E2E] Re-quantization with stochastic
+ * rounding; [UE] 实现): |y| goes to the grid point above it with probability
+ * (|y| - lo) / (hi - lo) and to the one below otherwise, so the expectation
+ * is |y|.  The uniform variate is u = (h >> 8) * 2^-24 from the 32-bit hash
+ * h; the rule is "up iff u < p".  |y| >= 6 saturates to 6. */
+int or_e2m1_code_sr(float y, uint32_t h) {
+  int sign = signbit(y) ? 8 : 0;
+  float a = fabsf(y);
+  if (a >= 6.0f) return sign | 7;
+  int lo = 0;
+  while (lo < 6 && E2M1_MAG[lo + 1] <= (double)a) ++lo;
+  float step = (float)(E2M1_MAG[lo + 1] - E2M1_MAG[lo]);
+  float p = (a - (float)E2M1_MAG[lo]) * (1.0f / step); /* exact: step is 2^k */
+  float u = (float)(h >> 8) * 0x1p-24f;                /* exact */
+  return sign | (u < p ? lo + 1 : lo);
+}
+
+/* ------------------------------------------------------------------ */
+/* Block-scale formats.  E4M3 is the OCP E4M3FN byte: bias 7, subnormals
+ * m/8 * 2^-6, largest finite 0x7E = 448, 0x7F = NaN; this gives NVFP4 its
+ * magnitude range 2^-10 .. 2688 = 6 * 448 ([E2E] Low-precision formats).
+ * UE5M3 is unsigned with 5 exponent and 3 mantissa bits ([UE] 数学推导);
+ * its bias, subnormals and NaN code are the reading stated in the header. */
+static int fmt_max_code(int fmt) { return fmt == OR_FMT_E4M3 ? 0x7E : 0xFE; }
+int or_scale_nan_code(int fmt) { return fmt == OR_FMT_E4M3 ? 0x7F : 0xFF; }
+
+double or_scale_decode(int fmt, int code) {
+  code &= 0xFF;
+  if (fmt == OR_FMT_E4M3) {
+    double sign = (code & 0x80) ? -1.0 : 1.0;
+    int c = code & 0x7F;
+    if (c == 0x7F) return NAN;
+    int e = c >> 3, m = c & 7;
+    return sign * (e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10));
+  }
+  if (code == 0xFF) return NAN;
+  int e = code >> 3, m = code & 7;
+  return e == 0 ? ldexp((double)m, -17) : ldexp((double)(8 + m), e - 18);
+}
+
+/* Table of the non-negative finite code values of a format. */
+static void scale_table(int fmt, double *dec) {
+  for (int c = 0; c <= fmt_max_code(fmt); ++c) dec[c] = or_scale_decode(fmt, c);
+}
+
+/* Encode s >= 0 to the nearest finite non-negative code value; an exact
+ * midpoint goes to the even code; values above the largest finite code are
+ * nearest to it (saturation).  Brute force over every code. */
+static int scale_encode_tab(const double *dec, int maxc, float s) {
+  double v = (double)s;
+  if (v >= dec[maxc]) return maxc; /* saturation, said outright */
+  int best = 0;
+  double best_d = fabs(v - dec[0]);
+  for (int c = 1; c <= maxc; ++c) {
+    double d = fabs(v - dec[c]);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return best;
+}
+
+int or_scale_encode(int fmt, float s) {
+  double dec[256];
+  scale_table(fmt, dec);
+  return scale_encode_tab(dec, fmt_max_code(fmt), s);
+}
+
+/* ------------------------------------------------------------------ */
+/* Counter-based hash for stochastic rounding.  fmix32 is the 32-bit
+ * finalizer of MurmurHash3 (A. Appleby, public domain).  The variate for
+ * element index idx under a 64-bit seed is fmix32(lo32(idx) ^ k) with the
+ * key k = fmix32(lo32(seed) ^ fmix32(hi32(seed) ^ hi32(idx) ^ 0x9E3779B9)). */
+uint32_t or_fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+
+uint32_t or_sr_hash(uint64_t seed, uint64_t idx) {
+  uint32_t k = or_fmix32((uint32_t)seed ^
+                         or_fmix32((uint32_t)(seed >> 32) ^ (uint32_t)(idx >> 32) ^ 0x9E3779B9u));
+  return or_fmix32((uint32_t)idx ^ k);
+}
+
+/* ------------------------------------------------------------------ */
+/* Tensor amax: A = max |x| over the tensor ([UE] 数学推导, current-tensor
+ * scaling).  Any NaN makes A NaN; otherwise an infinity makes it +inf. */
+float or_tensor_amax(const float *x, int64_t n) {
+  float m = 0.0f;
+  int nan = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (isnan(x[i])) nan = 1;
+    else if (fabsf(x[i]) > m) m = fabsf(x[i]);
+  }
+  return nan ? NAN : m;
+}
+
+/* FP32 outer scale alpha = A / (6 * S_g): with it the largest block of the
+ * tensor gets block scale S_g, the chosen FP8 maximum (448 for E4M3, 256
+ * under Four-Over-Six so that a max-to-4 scale, 1.5x larger, still fits:
+ * [46a] Implementatiedetails).  A = 0 gives alpha = 1.  A negative or
+ * non-finite A has no scale: NaN. */
+float or_alpha(float amax, float sg) {
+  if (!(amax >= 0.0f) || isinf(amax)) return NAN;
+  if (amax == 0.0f) return 1.0f;
+  return amax / (6.0f * sg);
+}
+
+/* Per-tensor constants shared by every block (binary32, in this order):
+ *   K_Q      = 1 / (Q * alpha), +inf replaced by FLT_MAX      (Q = 6 or 4)
+ *   S_EFF[c] = D[c] * alpha                (effective scale of code c)
+ *   INV_S[c] = 1 / S_EFF[c], or 0 if S_EFF[c] = 0 or the reciprocal is inf */
+typedef struct {
+  int fmt, maxc;
+  double dec[256];
+  float alpha, k6, k4;
+  float seff[256], inv[256];
+} or_consts;
+
+static float recip_or_max(float v) {
+  float r = 1.0f / v;
+  return isinf(r) ? FLT_MAX : r;
+}
+
+static void make_consts(or_consts *c, int fmt, float alpha) {
+  c->fmt = fmt;
+  c->maxc = fmt_max_code(fmt);
+  scale_table(fmt, c->dec);
+  c->alpha = alpha;
+  c->k6 = recip_or_max(6.0f * alpha);
+  c->k4 = recip_or_max(4.0f * alpha);
+  for (int k = 0; k <= c->maxc; ++k) {
+    c->seff[k] = (float)c->dec[k] * alpha;
+    float r = c->seff[k] == 0.0f ? 0.0f : 1.0f / c->seff[k];
+    c->inv[k] = isinf(r) ? 0.0f : r;
+  }
+}
+
+/* One candidate encoding of one 16-element block with max mapped to Q
+ * ([UE] 数学推导: s = quant(amax_b / Q_max); [E2E] Low-precision formats:
+ * value = fp4 * fp8 * fp32):
+ *   s_raw = a_b * K_Q  -> scale code  (nearest, ties to even, saturating)
+ *   y_i   = x_i * INV_S[code]         -> E2M1 code (RNE, or SR)
+ *   d_i   = fmaf(-q_i, S_EFF[code], x_i)
+ *   SSE   = (P0 + P1) + (P2 + P3),  P_k = fmaf(d_i, d_i, P_k) over
+ *           i = 4k .. 4k+3 in order, each P_k starting at +0.
+ * The SSE decides the Four-Over-Six choice, so it is taken in binary32 in
+ * this fixed order. */
+static float encode_block(const or_consts *c, const float *xb, float amax_b, float kq,
+                          int rounding, uint64_t seed, uint64_t idx0, int *scale_code,
+                          uint8_t nib[16]) {
+  float s_raw = amax_b * kq;
+  int code = scale_encode_tab(c->dec, c->maxc, s_raw);
+  float S = c->seff[code], I = c->inv[code];
+  float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < 16; ++i) {
+    float y = xb[i] * I;
+    int n = rounding == OR_ROUND_SR ? or_e2m1_code_sr(y, or_sr_hash(seed, idx0 + (uint64_t)i))
+                                    : or_e2m1_code(y);
+    nib[i] = (uint8_t)n;
+    float q = (float)or_e2m1_value(n);
+    float d = fmaf(-q, S, xb[i]);
+    P[i / 4] = fmaf(d, d, P[i / 4]);
+  }
+  *scale_code = code;
+  return (P[0] + P[1]) + (P[2] + P[3]);
+}
+
+/* Row-wise NVFP4 quantization of x[rows, cols] (cols % 16 == 0): every run of
+ * 16 consecutive elements of a row is one block ([E2E] Low-precision
+ * formats).  Outputs: codes[rows, cols/2] with element 2j in the low nibble
+ * and 2j+1 in the high nibble of byte j; scales[rows, cols/16], one byte per
+ * block.  select = Four-Over-Six encodes every block with max->6 and max->4
+ * and keeps max->4 only if its SSE is strictly lower ([46b] Method; [46a]
+ * Methodologie); *count4 (if given) is increased by the number of such
+ * blocks.  rounding = SR uses the hash of element index (row0 + r) * cols + c,
+ * row0 being the global row of x's first row.  Column-wise quantization is
+ * this function applied to the transpose.  sse_sel / sse6 (optional) receive
+ * each block's SSE for the chosen and for the max->6 encoding.
+ * A negative or non-finite amax writes the NaN scale code to every block and
+ * code 0 to every element. */
+int or_quantize(const float *x, int64_t rows, int64_t cols, int64_t row0, float amax, float sg,
+                int fmt, int select, int rounding, uint64_t seed, uint8_t *codes, uint8_t *scales,
+                uint64_t *count4, float *sse_sel, float *sse6) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  if (fmt != OR_FMT_E4M3 && fmt != OR_FMT_UE5M3) return OR_EINVAL;
+  if (select != OR_SELECT_6 && select != OR_SELECT_4OVER6) return OR_EINVAL;
+  if (rounding != OR_ROUND_RNE && rounding != OR_ROUND_SR) return OR_EINVAL;
+  if (rounding == OR_ROUND_SR && select != OR_SELECT_6) return OR_EINVAL;
+  const int64_t nb = cols / 16;
+  float alpha = or_alpha(amax, sg);
+  if (isnan(alpha)) {
+    memset(codes, 0, (size_t)(rows * cols / 2));
+    memset(scales, or_scale_nan_code(fmt), (size_t)(rows * nb));
+    for (int64_t b = 0; b < rows * nb; ++b) {
+      if (sse_sel) sse_sel[b] = NAN;
+      if (sse6) sse6[b] = NAN;
+    }
+    return OR_OK;
+  }
+  or_consts *c = (or_consts *)malloc(sizeof(or_consts));
+  make_consts(c, fmt, alpha);
+  uint64_t n4 = 0;
+#pragma omp parallel for schedule(static) reduction(+ : n4)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float *xb = x + r * cols + b * 16;
+      float amax_b = 0.0f;
+      for (int i = 0; i < 16; ++i)
+        if (fabsf(xb[i]) > amax_b) amax_b = fabsf(xb[i]);
+      uint64_t idx0 = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(b * 16);
+      uint8_t nib6[16], nib4[16];
+      int code6, code4 = 0;
+      float e6 = encode_block(c, xb, amax_b, c->k6, rounding, seed, idx0, &code6, nib6);
+      float e = e6;
+      const uint8_t *nib = nib6;
+      int code = code6;
+      if (select == OR_SELECT_4OVER6) {
+        float e4 = encode_block(c, xb, amax_b, c->k4, rounding, seed, idx0, &code4, nib4);
+        if (e4 < e6) {
+          e = e4;
+          nib = nib4;
+          code = code4;
+          n4 += 1;
+        }
+      }
+      scales[r * nb + b] = (uint8_t)code;
+      for (int j = 0; j < 8; ++j)
+        codes[r * (cols / 2) + b * 8 + j] = (uint8_t)(nib[2 * j] | (nib[2 * j + 1] << 4));
+      if (sse_sel) sse_sel[r * nb + b] = e;
+      if (sse6) sse6[r * nb + b] = e6;
+    }
+  }
+  free(c);
+  if (count4) *count4 += n4;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantization: x_hat = q * D[scale code] * alpha ([E2E] Low-precision
+ * formats: fp4 value x fp8 block scale x fp32 outer scale), the product taken
+ * exactly in binary64 and rounded once to binary32; a NaN scale code gives
+ * NaN.  out_bf16 (optional) is that binary32 value rounded to bfloat16 with
+ * round-to-nearest-even.  block_scale (optional, [rows, cols/16]) receives
+ * the binary32 effective scale D * alpha of each block. */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+uint16_t or_f32_to_bf16(float f) { return f32_to_bf16_rne(f); }
+
+int or_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                  float amax, float sg, int fmt, float *out_f32, uint16_t *out_bf16,
+                  float *block_scale) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  if (fmt != OR_FMT_E4M3 && fmt != OR_FMT_UE5M3) return OR_EINVAL;
+  const int64_t nb = cols / 16;
+  const double alpha = (double)or_alpha(amax, sg);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      double D = or_scale_decode(fmt, scales[r * nb + b]);
+      if (block_scale) block_scale[r * nb + b] = (float)(D * alpha);
+      for (int i = 0; i < 16; ++i) {
+        int64_t c = b * 16 + i;
+        uint8_t byte = codes[r * (cols / 2) + c / 2];
+        int nib = (c & 1) ? (byte >> 4) : (byte & 15);
+        float v = (float)(or_e2m1_value(nib) * D * alpha);
+        if (out_f32) out_f32[r * cols + c] = v;
+        if (out_bf16) out_bf16[r * cols + c] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* Sum of squared errors sum (x_i - x_hat_i)^2 in binary64, in index order
+ * ([UE] 实现 reports the per-tensor MSE = SSE / n). */
+double or_sse(const float *x, const float *xhat, int64_t n) {
+  double s = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double d = (double)x[i] - (double)xhat[i];
+    s += d * d;
+  }
+  return s;
+}
+
+/* ------------------------------------------------------------------ */
+/* Scale-learning fake quantization ([SL] How Scale Learning Works).
+ *   x~ = s_post * clamp(round(x / s_pre), -6, 6),  round = nearest E2M1
+ * per 16-element block with scales s_pre[b], s_post[b] (s_post == NULL:
+ * tied, s_post = s_pre).  x / s_pre is taken as y = x * inv in binary32 with
+ * inv = 1 / s_pre (0 if s_pre = 0; FLT_MAX-saturated if the reciprocal
+ * overflows); y decides the E2M1 code and the clamp.  x~ = q * s_post
+ * rounded once to binary32. */
+static float fq_inv(float s) {
+  if (s == 0.0f) return 0.0f;
+  float r = 1.0f / s;
+  return isinf(r) ? copysignf(FLT_MAX, r) : r;
+}
+
+int or_fakequant_fwd(const float *x, int64_t rows, int64_t cols, const float *s_pre,
+                     const float *s_post, float *xq) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  const int64_t nb = cols / 16;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      int64_t blk = r * nb + b;
+      float inv = fq_inv(s_pre[blk]);
+      double sp = s_post ? (double)s_post[blk] : (double)s_pre[blk];
+      for (int i = 0; i < 16; ++i) {
+        int64_t e = r * cols + b * 16 + i;
+        float y = x[e] * inv;
+        xq[e] = (float)(or_e2m1_value(or_e2m1_code(y)) * sp);
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* Straight-through backward ([SL] How Scale Learning Works), the derivative
+ * of round taken as 1 and that of the FP8 scale quantization too:
+ *   in_i = (-6 <= y_i <= 6)
+ * Single (tied) scale:
+ *   dL/dx_i = in_i ? g_i : 0
+ *   dL/ds   = sum_i g_i * (in_i ? q_i - y_i : (y_i < -6 ? -6 : +6))
+ * Dual scales:
+ *   dL/dx_i      = in_i ? g_i * (s_post / s_pre) : 0      (0 when s_pre = 0)
+ *   dL/ds_post   = sum_i g_i * clamp(q_i)                  (q_i = +-6 outside)
+ *   dL/ds_pre    = sum_i g_i * (in_i ? -s_post x_i / s_pre^2 : 0)
+ *                = -(s_post * T) / (s_pre * s_pre),  T = sum_{in} g_i x_i
+ *                  (0 when s_pre = 0)
+ * Every product and sum is binary64, summed in index order i = 0..15, and
+ * rounded once to binary32.  ds_post is written only for dual scales. */
+int or_fakequant_bwd(const float *x, const float *g, int64_t rows, int64_t cols,
+                     const float *s_pre, const float *s_post, float *dx, float *ds_pre,
+                     float *ds_post) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  const int64_t nb = cols / 16;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      int64_t blk = r * nb + b;
+      float sp_pre = s_pre[blk];
+      float inv = fq_inv(sp_pre);
+      double acc_s = 0.0, acc_post = 0.0, acc_t = 0.0;
+      double ratio = 0.0;
+      if (s_post && sp_pre != 0.0f) ratio = (double)s_post[blk] / (double)sp_pre;
+      for (int i = 0; i < 16; ++i) {
+        int64_t e = r * cols + b * 16 + i;
+        float y = x[e] * inv;
+        int in = (y >= -6.0f && y <= 6.0f);
+        double q = or_e2m1_value(or_e2m1_code(y)); /* already clamped to +-6 */
+        double gi = (double)g[e];
+        if (!s_post) {
+          dx[e] = in ? g[e] : 0.0f;
+          double d = in ? q - (double)y : (y < -6.0f ? -6.0 : 6.0);
+          acc_s += gi * d;
+        } else {
+          dx[e] = in ? (float)(gi * ratio) : 0.0f;
+          acc_post += gi * q;
+          if (in) acc_t += gi * (double)x[e];
+        }
+      }
+      if (!s_post) {
+        ds_pre[blk] = (float)acc_s;
+      } else {
+        ds_post[blk] = (float)acc_post;
+        if (sp_pre == 0.0f) {
+          ds_pre[blk] = 0.0f;
+        } else {
+          double spd = (double)sp_pre;
+          ds_pre[blk] = (float)(-((double)s_post[blk] * acc_t) / (spd * spd));
+        }
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* Number of OpenMP threads the parallel loops above use. */
+int or_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,207 @@
+/*
+ * nvfp4.h -- NVFP4 block-scaled quantization of bfloat16 tensors on AMD
+ * Instinct MI355X (gfx950).  C ABI of libnvfp4.so.
+ *
+ * The method (sources are web pages, cited by title and section):
+ *  - NVFP4: every 16 consecutive values share one 8-bit block scale; each
+ *    value is a 4-bit E2M1 code with magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6};
+ *    a binary32 per-tensor outer scale alpha shifts the range, and a value is
+ *    reconstructed as fp4 x fp8 x fp32 ("End-to-End 4-Bit Training",
+ *    section "Low-precision formats on Blackwell").
+ *  - Block scale = block amax / Q_max encoded to E4M3 (or to UE5M3, "UE5M3:
+ *    给 FP4 训练算一笔更宽容的账", section 数学推导).
+ *  - Four-Over-Six: encode each block with its max mapped to 6 and to 4 and
+ *    keep the lower-squared-error result ("Four Over Six: More Accurate NVFP4
+ *    Quantization with Adaptive Block Scaling", gist.science summary section
+ *    Methodologie and bud-325 notes section "Method"); under it the outer
+ *    scale maps the tensor amax to an FP8 maximum of 256, not 448 (gist.science
+ *    summary, section Implementatiedetails).
+ *  - Stochastic rounding for gradients only ("UE5M3" blog, 数学推导;
+ *    "End-to-End 4-Bit Training", "Re-quantization with stochastic rounding").
+ *  - Column-wise blocks for the transposed operand ("End-to-End 4-Bit
+ *    Training", "Block-scaled backward passes").
+ *  - Scale-learning fake quantization and its straight-through gradients,
+ *    single and dual (pre/post) scales ("Scale Learning: Training NVFP4 Block
+ *    Scales to Recover Accuracy", section "How Scale Learning Works").
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA/HIP
+ *    tensors) unless stated; the caller owns every buffer; the library keeps
+ *    no state between calls and allocates nothing.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronizes.  Arguments are validated on the host
+ *    before anything is launched; a non-zero status means nothing was
+ *    launched (NVFP4_ERR_HIP: a launch was attempted and HIP reported an
+ *    error).
+ *  - bfloat16 values travel as their 16-bit patterns (uint16_t).
+ *  - Tensors are dense row-major [rows, cols].  Data pointers (x, codes,
+ *    out_f32, out_bf16, grad tensors) must be 16-byte aligned; scale and
+ *    per-block arrays need only their natural alignment.
+ *  - Packed codes: byte j of a row holds element 2j in its low nibble and
+ *    element 2j+1 in its high nibble; nibble = sign << 3 | magnitude index.
+ *    Scales: one byte per 16-element block, [rows, cols/16], row-major.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID = 1,     /* bad argument; nothing launched */
+  NVFP4_ERR_UNSUPPORTED = 2, /* valid request this build does not serve */
+  NVFP4_ERR_HIP = 3          /* a HIP launch reported an error */
+};
+
+/* Block-scale formats.  E4M3 = OCP E4M3FN (bias 7, max 448, 0x7F = NaN).
+ * UE5M3 = unsigned, 5 exponent / 3 mantissa bits, read as bias 15 with
+ * subnormals, max 0xFE = 114688, 0xFF = NaN (the pages fix only the field
+ * widths). */
+enum { NVFP4_SCALE_E4M3 = 0, NVFP4_SCALE_UE5M3 = 1 };
+
+/* Block-scale selection: every block max -> 6, or Four-Over-Six (MSE). */
+enum { NVFP4_SELECT_6 = 0, NVFP4_SELECT_4OVER6 = 1 };
+
+/* Element rounding: round-to-nearest-even, or stochastic (max->6 only). */
+enum { NVFP4_ROUND_RNE = 0, NVFP4_ROUND_SR = 1 };
+
+/* Blocking axes (bitmask): ROW = 16 consecutive elements of a row; COL = 16
+ * consecutive rows of a column, written as the row-wise layout of X^T. */
+enum { NVFP4_AXIS_ROW = 1, NVFP4_AXIS_COL = 2 };
+
+/* Default FP8 maximum the outer scale maps the tensor amax to. */
+#define NVFP4_GLOBAL_MAX_E4M3 448.0f
+#define NVFP4_GLOBAL_MAX_E4M3_4OVER6 256.0f
+#define NVFP4_GLOBAL_MAX_UE5M3 114688.0f
+
+/*
+ * nvfp4_tensor_amax -- current-tensor scaling: *amax_out = max_i |x_i| over
+ * numel bf16 values ("UE5M3" blog, 数学推导).
+ *   x         device, numel bf16 patterns, 16-byte aligned.
+ *   numel     >= 0; 0 writes 0.
+ *   amax_out  device, one float; overwritten (no need to clear it).
+ * A NaN anywhere gives NaN; otherwise an infinity gives +inf.
+ * Errors: x or amax_out NULL with numel > 0, or numel < 0 -> NVFP4_ERR_INVALID.
+ */
+int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* stream);
+
+/*
+ * nvfp4_quantize -- NVFP4 quantization of a bf16 tensor x[rows, cols].
+ *   amax            device float: the tensor amax A (fresh from
+ *                   nvfp4_tensor_amax, or a stale/periodic value).  The outer
+ *                   scale is alpha = A / (6 * global_fp8_max) in binary32
+ *                   (alpha = 1 if A = 0).
+ *   global_fp8_max  S_g > 0, or 0 for the default: 448 (E4M3, max->6),
+ *                   256 (E4M3, Four-Over-Six), 114688 (UE5M3).
+ *   scale_fmt       NVFP4_SCALE_E4M3 or NVFP4_SCALE_UE5M3.
+ *   select          NVFP4_SELECT_6 or NVFP4_SELECT_4OVER6.
+ *   rounding        NVFP4_ROUND_RNE or NVFP4_ROUND_SR (requires SELECT_6).
+ *   axes            NVFP4_AXIS_ROW, NVFP4_AXIS_COL or both.
+ *   seed            stochastic rounding only: the variate of the element at
+ *                   index i of the OUTPUT orientation (r*cols + c row-wise,
+ *                   c*rows + r column-wise) is the counter hash of (seed, i).
+ *   codes, scales   ROW outputs: [rows, cols/2] and [rows, cols/16] bytes.
+ *   codes_t, scales_t  COL outputs: [cols, rows/2] and [cols, rows/16].
+ *   count4          optional device counter; += number of blocks (all axes)
+ *                   that chose max->4.  The caller clears it.
+ * Per block (binary32, in this order): a = max|x_i|; for Q in {6, 4}:
+ * s_raw = a * K_Q with K_Q = 1/(Q*alpha); code = nearest scale code (ties to
+ * even, saturating); y_i = x_i * (1/(D[code]*alpha)); E2M1 code of y_i (RNE,
+ * or SR); SSE over the block in a fixed 4x4 fmaf tree; max->4 is kept only if
+ * its SSE is strictly lower.
+ * A negative or non-finite *amax: every scale byte = the NaN code (0x7F E4M3,
+ * 0xFF UE5M3), every element code 0.  A NaN element with a usable amax: same
+ * for its block.
+ * Errors (NVFP4_ERR_INVALID): x/amax NULL; rows or cols < 0; ROW with
+ * cols % 16 != 0 or codes/scales NULL; COL with rows % 16 != 0 or
+ * codes_t/scales_t NULL; unknown enum; axes == 0; SR with Four-Over-Six;
+ * global_fp8_max negative or non-finite; misaligned pointers.
+ * rows == 0 or cols == 0: nothing to do, NVFP4_OK.
+ */
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                   float global_fp8_max, int scale_fmt, int select, int rounding, int axes,
+                   uint64_t seed, uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                   uint8_t* scales_t, unsigned long long* count4, void* stream);
+
+/*
+ * nvfp4_dequantize -- x_hat = q * D[scale code] * alpha, correctly rounded
+ * to binary32 ("End-to-End 4-Bit Training", "Low-precision formats on
+ * Blackwell"); a NaN scale code gives NaN.
+ *   codes, scales   [rows, cols/2], [rows, cols/16] as nvfp4_quantize writes.
+ *   amax, global_fp8_max, scale_fmt   as given to nvfp4_quantize (here
+ *                   global_fp8_max must be > 0: the value actually used).
+ *   out_f32         optional [rows, cols] float.
+ *   out_bf16        optional [rows, cols] bf16: round-to-nearest-even of the
+ *                   binary32 value.
+ *   block_scale_out optional [rows, cols/16] float: D * alpha per block (the
+ *                   binary32 effective scale; the scale-learning init).
+ *   x_ref, sse_out  optional pair: x_ref [rows, cols] bf16 input; *sse_out
+ *                   (device double) += sum (x - x_hat)^2 in binary64.  The
+ *                   caller clears *sse_out.  Per-tensor MSE = SSE / numel.
+ * Errors (NVFP4_ERR_INVALID): codes/scales/amax NULL; rows or cols < 0;
+ * cols % 16 != 0; unknown format; global_fp8_max <= 0 or non-finite; exactly
+ * one of x_ref / sse_out given; misaligned pointers.
+ */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     const float* amax, float global_fp8_max, int scale_fmt, float* out_f32,
+                     uint16_t* out_bf16, float* block_scale_out, const uint16_t* x_ref,
+                     double* sse_out, void* stream);
+
+/*
+ * nvfp4_fakequant_fwd -- scale-learning fake quantization ("Scale Learning",
+ * "How Scale Learning Works"):
+ *   x~ = s_post * clamp(round_E2M1(x / s_pre), -6, 6)
+ * per 16-element row block b with scales s_pre[b], s_post[b] ([rows, cols/16]
+ * floats).  s_post == NULL: tied single scale (s_post = s_pre).
+ * x / s_pre is y = x * inv in binary32, inv = 1/s_pre (0 if s_pre = 0,
+ * +-FLT_MAX if the reciprocal overflows); x~ = q * s_post rounded once.
+ *   xq_out  [rows, cols] float.
+ * Errors: NULL x/s_pre/xq_out, rows or cols < 0, cols % 16 != 0, misaligned
+ * pointers -> NVFP4_ERR_INVALID.
+ */
+int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
+                        const float* s_post, float* xq_out, void* stream);
+
+/*
+ * nvfp4_fakequant_bwd -- straight-through backward of nvfp4_fakequant_fwd
+ * (derivative of round and of the FP8 scale quantization taken as 1).  With
+ * in_i = (-6 <= y_i <= 6):
+ *  single (s_post == NULL):
+ *   grad_x_i   = in_i ? g_i : 0
+ *   grad_s_pre = sum_i g_i * (in_i ? q_i - y_i : (y_i < -6 ? -6 : 6))
+ *  dual:
+ *   grad_x_i    = in_i ? g_i * (s_post / s_pre) : 0   (0 when s_pre = 0)
+ *   grad_s_post = sum_i g_i * clamp(q_i)
+ *   grad_s_pre  = -(s_post * sum_{in} g_i x_i) / (s_pre * s_pre)  (0 when s_pre = 0)
+ * Products and block sums are binary64 (sum in element order) rounded once to
+ * binary32, so results do not depend on the launch configuration.
+ *   grad_xq      [rows, cols] float, upstream dL/dx~.
+ *   grad_x       [rows, cols] float.
+ *   grad_s_pre   [rows, cols/16] float (the single-scale gradient when tied).
+ *   grad_s_post  [rows, cols/16] float; required for dual, must be NULL when
+ *                tied.
+ * Errors: as nvfp4_fakequant_fwd, plus grad_s_post presence not matching
+ * s_post -> NVFP4_ERR_INVALID.
+ */
+int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
+                        const float* s_pre, const float* s_post, float* grad_x,
+                        float* grad_s_pre, float* grad_s_post, void* stream);
+
+/* Static description of a status code. */
+const char* nvfp4_status_string(int status);
+
+/* NVFP4_ABI_VERSION of the loaded library. */
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,11 @@
+"""NVFP4 block-scaled quantization for AMD Instinct MI355X (gfx950).
+
+The computation lives in libnvfp4.so (hand-written HIP kernels behind the C
+ABI of include/nvfp4.h); this package is its Python binding.  Importing it
+does not load the library; the first call does, and raises if it is not built.
+"""
+from .api import (Quantized, default_global_max, dequantize, fakequant_bwd, fakequant_fwd,
+                  quantize, tensor_amax)
+
+__all__ = ["Quantized", "default_global_max", "dequantize", "fakequant_bwd", "fakequant_fwd",
+           "quantize", "tensor_amax"]

@@ -1,0 +1,71 @@
+"""ctypes loader for libnvfp4.so (the C ABI of include/nvfp4.h).
+
+The library is built in-tree by ``nvfp4_block_scaled_02_amd.build`` (or
+``__graft_entry__.build()``).  There is no fallback: if the library is
+missing or cannot be loaded, every call raises.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+SCALE_E4M3, SCALE_UE5M3 = 0, 1
+SELECT_6, SELECT_4OVER6 = 0, 1
+ROUND_RNE, ROUND_SR = 0, 1
+AXIS_ROW, AXIS_COL = 1, 2
+
+# name -> (restype, argtypes); the exported surface of include/nvfp4.h and
+# include/nvfp4_testing.h
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_u64 = ctypes.c_uint64
+_u32 = ctypes.c_uint32
+_f32 = ctypes.c_float
+SIGNATURES = {
+    "nvfp4_abi_version": (_int, []),
+    "nvfp4_status_string": (ctypes.c_char_p, [_int]),
+    "nvfp4_tensor_amax": (_int, [_vp, _i64, _vp, _vp]),
+    "nvfp4_quantize": (_int, [_vp, _i64, _i64, _vp, _f32, _int, _int, _int, _int, _u64,
+                              _vp, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_dequantize": (_int, [_vp, _vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp, _vp, _vp,
+                                _vp]),
+    "nvfp4_fakequant_fwd": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_fakequant_bwd": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_test_e2m1_rne_range": (_int, [_u32, _i64, _vp, _vp]),
+    "nvfp4_test_e2m1_sr": (_int, [_vp, _vp, _i64, _vp, _vp]),
+    "nvfp4_test_scale_encode_range": (_int, [_int, _u32, _i64, _vp, _vp]),
+    "nvfp4_test_sr_hash": (_int, [_u64, _u64, _i64, _vp, _vp]),
+}
+
+_lib = None
+
+
+class NativeError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise NativeError(
+            f"{LIB_PATH} is not built; run `python -m nvfp4_block_scaled_02_amd.build` "
+            "(hipcc, gfx950) first. There is no non-native fallback.")
+    l = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(l, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = l
+    return l
+
+
+def check(status, what):
+    if status != OK:
+        msg = lib().nvfp4_status_string(status).decode()
+        raise NativeError(f"{what} failed with status {status} ({msg})")

@@ -1,0 +1,200 @@
+"""Torch-facing wrappers over the C ABI of libnvfp4.so (include/nvfp4.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  Torch supplies device memory and the current stream.  Inputs must
+be contiguous tensors on a GPU device; bf16 inputs are passed as their 16-bit
+patterns.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _native as N
+
+_FMT = {"e4m3": N.SCALE_E4M3, "ue5m3": N.SCALE_UE5M3}
+_SELECT = {"6": N.SELECT_6, "4over6": N.SELECT_4OVER6}
+_ROUND = {"rne": N.ROUND_RNE, "sr": N.ROUND_SR}
+_AXES = {"row": N.AXIS_ROW, "col": N.AXIS_COL, "both": N.AXIS_ROW | N.AXIS_COL}
+
+
+def default_global_max(fmt: str = "e4m3", select: str = "4over6") -> float:
+    """FP8 maximum S_g the outer scale maps the tensor amax to."""
+    if fmt == "ue5m3":
+        return 114688.0
+    return 256.0 if select == "4over6" else 448.0
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def tensor_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """max |x| over a bf16 tensor, as a 1-element float32 device tensor."""
+    _need(x, torch.bfloat16, "x")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, "out")
+    N.check(N.lib().nvfp4_tensor_amax(_ptr(x), x.numel(), _ptr(out), _stream(x.device)),
+            "nvfp4_tensor_amax")
+    return out
+
+
+@dataclass
+class Quantized:
+    """NVFP4 tensor: packed codes [rows, cols/2] (uint8, low nibble = even
+    element), scale bytes [rows, cols/16], and the outer-scale inputs."""
+    codes: Optional[torch.Tensor]
+    scales: Optional[torch.Tensor]
+    codes_t: Optional[torch.Tensor]
+    scales_t: Optional[torch.Tensor]
+    amax: torch.Tensor
+    global_max: float
+    fmt: str
+    count4: Optional[torch.Tensor]
+
+
+def quantize(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: str = "e4m3",
+             select: str = "4over6", rounding: str = "rne", axes: str = "row", seed: int = 0,
+             global_max: float = 0.0, count4: bool = False,
+             out: Optional[dict] = None) -> Quantized:
+    """NVFP4-quantize a 2-D bf16 tensor.  amax: 1-element float32 device
+    tensor (default: the fresh tensor amax).  axes: "row", "col" or "both".
+    out: optional preallocated {"codes", "scales", "codes_t", "scales_t",
+    "count4"} tensors (count4 is added to, not cleared)."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if amax is None:
+        amax = tensor_amax(x)
+    _need(amax, torch.float32, "amax")
+    ax = _AXES[axes]
+    out = dict(out or {})
+    dev = x.device
+    if ax & N.AXIS_ROW:
+        out.setdefault("codes", torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev))
+        out.setdefault("scales", torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev))
+    if ax & N.AXIS_COL:
+        out.setdefault("codes_t", torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev))
+        out.setdefault("scales_t", torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev))
+    if count4 and "count4" not in out:
+        out["count4"] = torch.zeros(1, dtype=torch.int64, device=dev)
+    for k in ("codes", "scales", "codes_t", "scales_t"):
+        if k in out:
+            _need(out[k], torch.uint8, k)
+    if "count4" in out:
+        _need(out["count4"], torch.int64, "count4")
+    st = N.lib().nvfp4_quantize(
+        _ptr(x), rows, cols, _ptr(amax), float(global_max), _FMT[fmt], _SELECT[select],
+        _ROUND[rounding], ax, int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out.get("codes")),
+        _ptr(out.get("scales")), _ptr(out.get("codes_t")), _ptr(out.get("scales_t")),
+        _ptr(out.get("count4")), _stream(dev))
+    N.check(st, "nvfp4_quantize")
+    gm = float(global_max) if global_max else default_global_max(fmt, select)
+    return Quantized(out.get("codes"), out.get("scales"), out.get("codes_t"),
+                     out.get("scales_t"), amax, gm, fmt, out.get("count4"))
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
+               global_max: float, fmt: str = "e4m3", out_dtype=torch.float32,
+               want_block_scale: bool = False, x_ref: Optional[torch.Tensor] = None,
+               sse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """x_hat = q * D[scale] * alpha.  Returns x_hat (or None if out_dtype is
+    None), plus the per-block effective scales if asked, plus the binary64
+    SSE tensor if x_ref is given (sse is added to if passed)."""
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    _need(amax, torch.float32, "amax")
+    rows, half = codes.shape
+    cols = 2 * half
+    dev = codes.device
+    of32 = ob16 = None
+    if out_dtype is not None:
+        if out is None:
+            out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+        _need(out, out_dtype, "out")
+        if out_dtype == torch.float32:
+            of32 = out
+        elif out_dtype == torch.bfloat16:
+            ob16 = out
+        else:
+            raise TypeError("out_dtype must be float32, bfloat16 or None")
+    bs = torch.empty((rows, cols // 16), dtype=torch.float32, device=dev) if want_block_scale else None
+    if x_ref is not None:
+        _need(x_ref, torch.bfloat16, "x_ref")
+        if sse is None:
+            sse = torch.zeros(1, dtype=torch.float64, device=dev)
+        _need(sse, torch.float64, "sse")
+    st = N.lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(amax),
+                                  float(global_max), _FMT[fmt], _ptr(of32), _ptr(ob16), _ptr(bs),
+                                  _ptr(x_ref), _ptr(sse) if x_ref is not None else None,
+                                  _stream(dev))
+    N.check(st, "nvfp4_dequantize")
+    res = [out]
+    if want_block_scale:
+        res.append(bs)
+    if x_ref is not None:
+        res.append(sse)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def fakequant_fwd(x: torch.Tensor, s_pre: torch.Tensor, s_post: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x~ = s_post * clamp(round_E2M1(x / s_pre), -6, 6) per 16-element block."""
+    _need(x, torch.bfloat16, "x")
+    _need(s_pre, torch.float32, "s_pre")
+    if s_post is not None:
+        _need(s_post, torch.float32, "s_post")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, "out")
+    st = N.lib().nvfp4_fakequant_fwd(_ptr(x), rows, cols, _ptr(s_pre), _ptr(s_post), _ptr(out),
+                                     _stream(x.device))
+    N.check(st, "nvfp4_fakequant_fwd")
+    return out
+
+
+def fakequant_bwd(x: torch.Tensor, grad: torch.Tensor, s_pre: torch.Tensor,
+                  s_post: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+    """Straight-through backward.  Returns (dx, ds) for tied scales and
+    (dx, ds_pre, ds_post) for dual scales."""
+    _need(x, torch.bfloat16, "x")
+    _need(grad, torch.float32, "grad")
+    _need(s_pre, torch.float32, "s_pre")
+    if s_post is not None:
+        _need(s_post, torch.float32, "s_post")
+    rows, cols = x.shape
+    dev = x.device
+    out = dict(out or {})
+    dx = out.get("dx")
+    if dx is None:
+        dx = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    dpre = out.get("ds_pre")
+    if dpre is None:
+        dpre = torch.empty(s_pre.shape, dtype=torch.float32, device=dev)
+    dpost = None
+    if s_post is not None:
+        dpost = out.get("ds_post")
+        if dpost is None:
+            dpost = torch.empty(s_post.shape, dtype=torch.float32, device=dev)
+    st = N.lib().nvfp4_fakequant_bwd(_ptr(x), _ptr(grad), rows, cols, _ptr(s_pre), _ptr(s_post),
+                                     _ptr(dx), _ptr(dpre), _ptr(dpost), _stream(dev))
+    N.check(st, "nvfp4_fakequant_bwd")
+    return (dx, dpre) if s_post is None else (dx, dpre, dpost)

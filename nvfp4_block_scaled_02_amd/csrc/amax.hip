@@ -1,0 +1,83 @@
+// amax.hip -- tensor amax for current-tensor scaling ("UE5M3: 给 FP4 训练算
+// 一笔更宽容的账", section 数学推导): A = max |x| over a bf16 tensor.
+//
+// HBM-bound (2 bytes read per element).  Each lane streams 16-byte chunks,
+// folds them with packed 16-bit integer max on the sign-cleared patterns
+// (integer order = magnitude order; NaN > inf > finite), the wavefront
+// reduces with DPP moves, and one integer atomicMax per workgroup lands the
+// result as the float whose bits are (pattern << 16).
+#include "common.hpp"
+#include "device.hpp"
+
+namespace nvfp4 {
+
+__global__ void __launch_bounds__(64) amax_init_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[0] = 0u;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  // butterfly over the 64 lanes with ds_swizzle-free cross-lane moves
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+constexpr int kAmaxUnroll = 4;
+
+__global__ void __launch_bounds__(kThreads) amax_kernel(const uint4* __restrict__ x, int64_t nchunks,
+                                                        const uint16_t* __restrict__ tail,
+                                                        int ntail, uint32_t* out) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // unrolled body: kAmaxUnroll independent 16-byte loads in flight per lane
+  for (; i + (kAmaxUnroll - 1) * stride < nchunks; i += kAmaxUnroll * stride) {
+    uint4 w[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) w[u] = ld_nt(x + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      uint32_t v = chunk_abs_max_bits(w[u]);
+      m = m > v ? m : v;
+    }
+  }
+  for (; i < nchunks; i += stride) {
+    uint32_t v = chunk_abs_max_bits(ld_nt(x + i));
+    m = m > v ? m : v;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < ntail) {
+    uint32_t v = tail[threadIdx.x] & 0x7FFFu;
+    m = m > v ? m : v;
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[kThreads / 64];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int w2 = 1; w2 < kThreads / 64; ++w2) r = r > red[w2] ? r : red[w2];
+    atomicMax(out, r << 16);
+  }
+}
+
+hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipStream_t s) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(64), 0, s, o);
+  if (numel == 0) return hipGetLastError();
+  const int64_t nchunks = numel / kChunk;
+  const int ntail = (int)(numel - nchunks * kChunk);
+  // enough workgroups to fill every CU several times over, each lane doing
+  // at least a few unrolled iterations
+  const int64_t want = (nchunks + (int64_t)kThreads * kAmaxUnroll - 1) / ((int64_t)kThreads * kAmaxUnroll);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  int64_t grid = want < cap ? want : cap;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint4*>(x), nchunks, x + nchunks * kChunk, ntail, o);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,237 @@
+// api.hip -- the extern "C" entry points of libnvfp4.so (include/nvfp4.h):
+// host-side validation, resolution of defaults, and dispatch to the kernels.
+// Nothing here allocates device memory or synchronizes.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/nvfp4.h"
+#include "../../include/nvfp4_testing.h"
+#include "common.hpp"
+#include "device.hpp"
+
+namespace nvfp4 {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static bool size_ok(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return false;
+  if (cols != 0 && rows > (INT64_C(1) << 62) / cols) return false;
+  return true;
+}
+
+static int status_of(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// ---------------------------------------------------------------- test hooks
+__global__ void test_e2m1_range_kernel(uint32_t first, int64_t n, uint8_t* codes) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float y = __uint_as_float(first + (uint32_t)i);
+    codes[i] = (uint8_t)(NVFP4_CVT_PK_FP4(0u, y, 0.0f, 0) & 0xFu);
+  }
+}
+
+__global__ void test_e2m1_sr_kernel(const float* y, const uint32_t* h, int64_t n, uint8_t* codes) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    codes[i] = (uint8_t)e2m1_sr_code(y[i], h[i]);
+}
+
+template <int FMT>
+__global__ void test_scale_range_kernel(uint32_t first, int64_t n, uint8_t* codes) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float s = __uint_as_float(first + (uint32_t)i);
+    codes[i] = (uint8_t)(encode_pair(FMT, s, 0.0f) & 0xFFu);
+  }
+}
+
+__global__ void test_sr_hash_kernel(uint64_t seed, uint64_t idx0, int64_t n, uint32_t key0,
+                                    uint32_t* out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint64_t idx = idx0 + (uint64_t)i;
+    const uint32_t hi = (uint32_t)(idx >> 32);
+    const uint32_t key = hi == 0 ? key0 : sr_key(seed, hi);
+    out[i] = fmix32((uint32_t)idx ^ key);
+  }
+}
+
+static unsigned test_grid(int64_t n) {
+  int64_t g = (n + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  return (unsigned)(g < 1 ? 1 : (g < cap ? g : cap));
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID: return "invalid argument";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported request";
+    case NVFP4_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* stream) {
+  if (numel < 0 || !amax_out) return NVFP4_ERR_INVALID;
+  if (numel > 0 && (!x || !aligned16(x))) return NVFP4_ERR_INVALID;
+  if (((uintptr_t)amax_out & 3u) != 0) return NVFP4_ERR_INVALID;
+  return status_of(launch_tensor_amax(x, numel, amax_out, (hipStream_t)stream));
+}
+
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                   float global_fp8_max, int scale_fmt, int select, int rounding, int axes,
+                   uint64_t seed, uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                   uint8_t* scales_t, unsigned long long* count4, void* stream) {
+  if (!x || !amax || !size_ok(rows, cols)) return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (select != NVFP4_SELECT_6 && select != NVFP4_SELECT_4OVER6) return NVFP4_ERR_INVALID;
+  if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
+  if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
+  if (axes != NVFP4_AXIS_ROW && axes != NVFP4_AXIS_COL && axes != (NVFP4_AXIS_ROW | NVFP4_AXIS_COL))
+    return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (axes & NVFP4_AXIS_ROW) {
+    if (cols % 16 != 0 || !codes || !scales || !aligned16(codes)) return NVFP4_ERR_INVALID;
+  }
+  if (axes & NVFP4_AXIS_COL) {
+    if (rows % 16 != 0 || cols % 8 != 0 || !codes_t || !scales_t || !aligned16(codes_t))
+      return NVFP4_ERR_INVALID;
+  }
+  if (!aligned16(x) || ((uintptr_t)amax & 3u) || ((uintptr_t)count4 & 7u)) return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  float sg = global_fp8_max;
+  if (sg == 0.0f) {
+    if (scale_fmt == NVFP4_SCALE_UE5M3) sg = NVFP4_GLOBAL_MAX_UE5M3;
+    else sg = select == NVFP4_SELECT_4OVER6 ? NVFP4_GLOBAL_MAX_E4M3_4OVER6 : NVFP4_GLOBAL_MAX_E4M3;
+  }
+  QuantizeArgs a;
+  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax; a.sg = sg;
+  a.fmt = scale_fmt; a.select = select; a.rounding = rounding; a.axes = axes; a.seed = seed;
+  a.codes = codes; a.scales = scales; a.codes_t = codes_t; a.scales_t = scales_t;
+  a.count4 = count4;
+  return status_of(launch_quantize(a, (hipStream_t)stream));
+}
+
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     const float* amax, float global_fp8_max, int scale_fmt, float* out_f32,
+                     uint16_t* out_bf16, float* block_scale_out, const uint16_t* x_ref,
+                     double* sse_out, void* stream) {
+  if (!codes || !scales || !amax || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if ((x_ref == nullptr) != (sse_out == nullptr)) return NVFP4_ERR_INVALID;
+  if (!aligned16(codes) || !aligned16(out_f32) || !aligned16(out_bf16) || !aligned16(x_ref))
+    return NVFP4_ERR_INVALID;
+  if (((uintptr_t)amax & 3u) || ((uintptr_t)block_scale_out & 3u) || ((uintptr_t)sse_out & 7u))
+    return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  DequantizeArgs a;
+  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = amax;
+  a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32; a.out_bf16 = out_bf16;
+  a.block_scale = block_scale_out; a.x_ref = x_ref; a.sse = sse_out;
+  return status_of(launch_dequantize(a, (hipStream_t)stream));
+}
+
+static int fq_common(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre) {
+  if (!x || !s_pre || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
+  if (!aligned16(x) || ((uintptr_t)s_pre & 3u)) return NVFP4_ERR_INVALID;
+  return NVFP4_OK;
+}
+
+int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
+                        const float* s_post, float* xq_out, void* stream) {
+  int st = fq_common(x, rows, cols, s_pre);
+  if (st != NVFP4_OK) return st;
+  if (!xq_out || !aligned16(xq_out) || ((uintptr_t)s_post & 3u)) return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  FakeQuantArgs a = {};
+  a.x = x; a.rows = rows; a.cols = cols; a.s_pre = s_pre; a.s_post = s_post; a.xq = xq_out;
+  return status_of(launch_fakequant_fwd(a, (hipStream_t)stream));
+}
+
+int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
+                        const float* s_pre, const float* s_post, float* grad_x,
+                        float* grad_s_pre, float* grad_s_post, void* stream) {
+  int st = fq_common(x, rows, cols, s_pre);
+  if (st != NVFP4_OK) return st;
+  if (!grad_xq || !grad_x || !grad_s_pre) return NVFP4_ERR_INVALID;
+  if ((s_post == nullptr) != (grad_s_post == nullptr)) return NVFP4_ERR_INVALID;
+  if (!aligned16(grad_xq) || !aligned16(grad_x) || ((uintptr_t)grad_s_pre & 3u) ||
+      ((uintptr_t)s_post & 3u) || ((uintptr_t)grad_s_post & 3u))
+    return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  FakeQuantArgs a = {};
+  a.x = x; a.g = grad_xq; a.rows = rows; a.cols = cols; a.s_pre = s_pre; a.s_post = s_post;
+  a.dx = grad_x; a.ds_pre = grad_s_pre; a.ds_post = grad_s_post;
+  return status_of(launch_fakequant_bwd(a, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- test hooks
+int nvfp4_test_e2m1_rne_range(uint32_t first, int64_t n, uint8_t* codes, void* stream) {
+  if (n < 0 || n > (INT64_C(1) << 32) || (uint64_t)first + (uint64_t)n > (UINT64_C(1) << 32) ||
+      (n > 0 && !codes))
+    return NVFP4_ERR_INVALID;
+  if (n == 0) return NVFP4_OK;
+  hipLaunchKernelGGL(test_e2m1_range_kernel, dim3(test_grid(n)), dim3(256), 0,
+                     (hipStream_t)stream, first, n, codes);
+  return status_of(hipGetLastError());
+}
+
+int nvfp4_test_e2m1_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, void* stream) {
+  if (n < 0 || (n > 0 && (!y || !h || !codes))) return NVFP4_ERR_INVALID;
+  if (n == 0) return NVFP4_OK;
+  hipLaunchKernelGGL(test_e2m1_sr_kernel, dim3(test_grid(n)), dim3(256), 0, (hipStream_t)stream,
+                     y, h, n, codes);
+  return status_of(hipGetLastError());
+}
+
+int nvfp4_test_scale_encode_range(int fmt, uint32_t first, int64_t n, uint8_t* codes,
+                                  void* stream) {
+  if (fmt != NVFP4_SCALE_E4M3 && fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (n < 0 || (uint64_t)first + (uint64_t)n > (UINT64_C(1) << 31) || (n > 0 && !codes))
+    return NVFP4_ERR_INVALID;
+  if (n == 0) return NVFP4_OK;
+  if (fmt == NVFP4_SCALE_E4M3)
+    hipLaunchKernelGGL(test_scale_range_kernel<FMT_E4M3>, dim3(test_grid(n)), dim3(256), 0,
+                       (hipStream_t)stream, first, n, codes);
+  else
+    hipLaunchKernelGGL(test_scale_range_kernel<FMT_UE5M3>, dim3(test_grid(n)), dim3(256), 0,
+                       (hipStream_t)stream, first, n, codes);
+  return status_of(hipGetLastError());
+}
+
+int nvfp4_test_sr_hash(uint64_t seed, uint64_t idx0, int64_t n, uint32_t* out, void* stream) {
+  if (n < 0 || (n > 0 && !out)) return NVFP4_ERR_INVALID;
+  if (n == 0) return NVFP4_OK;
+  hipLaunchKernelGGL(test_sr_hash_kernel, dim3(test_grid(n)), dim3(256), 0, (hipStream_t)stream,
+                     seed, idx0, n, sr_key(seed, 0u), out);
+  return status_of(hipGetLastError());
+}
+
+}  // extern "C"

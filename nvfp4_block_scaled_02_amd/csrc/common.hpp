@@ -1,0 +1,63 @@
+// common.hpp -- definitions shared by the host entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+enum { FMT_E4M3 = 0, FMT_UE5M3 = 1 };
+enum { SELECT_6 = 0, SELECT_4OVER6 = 1 };
+enum { ROUND_RNE = 0, ROUND_SR = 1 };
+enum { AXIS_ROW = 1, AXIS_COL = 2 };
+
+// Launch shape of the streaming kernels: 256 threads = 4 wave64s per
+// workgroup; each lane owns 8 consecutive elements (one 16-byte bf16 chunk)
+// and two neighbouring lanes own one 16-element block.
+constexpr int kThreads = 256;
+constexpr int kChunk = 8;
+
+struct QuantizeArgs {
+  const uint16_t* x;
+  int64_t rows, cols;
+  const float* amax;
+  float sg;  // resolved S_g (> 0)
+  int fmt, select, rounding, axes;
+  uint64_t seed;
+  uint8_t *codes, *scales, *codes_t, *scales_t;
+  unsigned long long* count4;
+};
+
+struct DequantizeArgs {
+  const uint8_t *codes, *scales;
+  int64_t rows, cols;
+  const float* amax;
+  float sg;
+  int fmt;
+  float* out_f32;
+  uint16_t* out_bf16;
+  float* block_scale;
+  const uint16_t* x_ref;
+  double* sse;
+};
+
+struct FakeQuantArgs {
+  const uint16_t* x;
+  const float* g;
+  int64_t rows, cols;
+  const float *s_pre, *s_post;
+  float* xq;
+  float *dx, *ds_pre, *ds_post;
+};
+
+// Launchers (one translation unit each); return the hipError_t of the launch.
+hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipStream_t s);
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
+hipError_t launch_dequantize(const DequantizeArgs& a, hipStream_t s);
+hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s);
+hipError_t launch_fakequant_bwd(const FakeQuantArgs& a, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace nvfp4

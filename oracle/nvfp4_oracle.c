@@ -274,7 +274,9 @@ static float encode_block(const or_consts *c, const float *xb, float amax_b, flo
  * this function applied to the transpose.  sse_sel / sse6 (optional) receive
  * each block's SSE for the chosen and for the max->6 encoding.
  * A negative or non-finite amax writes the NaN scale code to every block and
- * code 0 to every element. */
+ * code 0 to every element; with a usable amax, a block holding a NaN element
+ * gets the NaN scale code and code 0 for its elements.  Infinite elements
+ * saturate (scale at the largest code, the infinite element at +-6). */
 int or_quantize(const float *x, int64_t rows, int64_t cols, int64_t row0, float amax, float sg,
                 int fmt, int select, int rounding, uint64_t seed, uint8_t *codes, uint8_t *scales,
                 uint64_t *count4, float *sse_sel, float *sse6) {
@@ -302,8 +304,18 @@ int or_quantize(const float *x, int64_t rows, int64_t cols, int64_t row0, float 
     for (int64_t b = 0; b < nb; ++b) {
       const float *xb = x + r * cols + b * 16;
       float amax_b = 0.0f;
-      for (int i = 0; i < 16; ++i)
-        if (fabsf(xb[i]) > amax_b) amax_b = fabsf(xb[i]);
+      int nan_b = 0;
+      for (int i = 0; i < 16; ++i) {
+        if (isnan(xb[i])) nan_b = 1;
+        else if (fabsf(xb[i]) > amax_b) amax_b = fabsf(xb[i]);
+      }
+      if (nan_b) { /* a NaN element: the block has no scale */
+        scales[r * nb + b] = (uint8_t)or_scale_nan_code(fmt);
+        memset(codes + r * (cols / 2) + b * 8, 0, 8);
+        if (sse_sel) sse_sel[r * nb + b] = NAN;
+        if (sse6) sse6[r * nb + b] = NAN;
+        continue;
+      }
       uint64_t idx0 = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(b * 16);
       uint8_t nib6[16], nib4[16];
       int code6, code4 = 0;

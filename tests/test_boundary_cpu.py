@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every symbol its headers declare, and
+rejects bad arguments on the host before any launch.  No GPU needed: every
+call here either fails validation or has nothing to do (an empty tensor)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_block_scaled_02_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("nvfp4.h", "nvfp4_testing.h")]
+
+FAKE = 0x100000  # aligned non-null address that is never dereferenced
+FAKE_ODD = 0x100004
+
+
+def _declared():
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nvfp4_\w+)\s*\(", src, flags=re.M)
+    return names
+
+
+def test_library_loads_and_version():
+    lib = N.lib()
+    assert lib.nvfp4_abi_version() == 1
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = _declared()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(N.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+        assert n in N.SIGNATURES, f"{n} has no Python binding"
+    assert set(N.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    lib = N.lib()
+    for s, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported request"),
+                    (3, b"HIP launch error"), (99, b"unknown status")]:
+        assert lib.nvfp4_status_string(s) == text
+
+
+def _q(**kw):
+    a = dict(x=FAKE, rows=16, cols=32, amax=FAKE, gmax=0.0, fmt=0, select=1, rnd=0, axes=1,
+             seed=0, codes=FAKE, scales=FAKE, codes_t=FAKE, scales_t=FAKE, count4=None)
+    a.update(kw)
+    return N.lib().nvfp4_quantize(a["x"], a["rows"], a["cols"], a["amax"], a["gmax"], a["fmt"],
+                                  a["select"], a["rnd"], a["axes"], a["seed"], a["codes"],
+                                  a["scales"], a["codes_t"], a["scales_t"], a["count4"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(amax=None), dict(rows=-1), dict(cols=-16), dict(cols=24),
+    dict(fmt=2), dict(select=2), dict(rnd=2), dict(axes=0), dict(axes=4),
+    dict(rnd=1, select=1), dict(gmax=-1.0), dict(gmax=float("inf")), dict(gmax=float("nan")),
+    dict(codes=None), dict(scales=None), dict(axes=2, rows=24), dict(axes=2, codes_t=None),
+    dict(axes=3, scales_t=None), dict(axes=2, cols=20, rows=16), dict(x=FAKE_ODD),
+    dict(codes=FAKE_ODD), dict(count4=FAKE_ODD), dict(rows=1 << 40, cols=1 << 40),
+])
+def test_quantize_rejects(kw):
+    assert _q(**kw) == N.ERR_INVALID
+
+
+def test_quantize_empty_is_ok_without_launch():
+    assert _q(rows=0) == N.OK
+    assert _q(cols=0) == N.OK
+    assert _q(rows=0, axes=3) == N.OK
+
+
+def _dq(**kw):
+    a = dict(codes=FAKE, scales=FAKE, rows=16, cols=32, amax=FAKE, gmax=448.0, fmt=0,
+             f32=FAKE, b16=None, bs=None, xref=None, sse=None)
+    a.update(kw)
+    return N.lib().nvfp4_dequantize(a["codes"], a["scales"], a["rows"], a["cols"], a["amax"],
+                                    a["gmax"], a["fmt"], a["f32"], a["b16"], a["bs"], a["xref"],
+                                    a["sse"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(codes=None), dict(scales=None), dict(amax=None), dict(cols=8), dict(rows=-2),
+    dict(fmt=5), dict(gmax=0.0), dict(gmax=-3.0), dict(xref=FAKE), dict(sse=FAKE),
+    dict(f32=FAKE_ODD), dict(sse=FAKE_ODD, xref=FAKE),
+])
+def test_dequantize_rejects(kw):
+    assert _dq(**kw) == N.ERR_INVALID
+
+
+def test_dequantize_empty_ok():
+    assert _dq(rows=0) == N.OK
+
+
+def test_amax_rejects():
+    lib = N.lib()
+    assert lib.nvfp4_tensor_amax(FAKE, -1, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(None, 16, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE, 16, None, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE_ODD, 16, FAKE, None) == N.ERR_INVALID
+
+
+def test_fakequant_rejects():
+    lib = N.lib()
+    f = lib.nvfp4_fakequant_fwd
+    assert f(None, 16, 16, FAKE, None, FAKE, None) == N.ERR_INVALID
+    assert f(FAKE, 16, 8, FAKE, None, FAKE, None) == N.ERR_INVALID
+    assert f(FAKE, 16, 16, None, None, FAKE, None) == N.ERR_INVALID
+    assert f(FAKE, 16, 16, FAKE, None, None, None) == N.ERR_INVALID
+    assert f(FAKE, 0, 16, FAKE, None, FAKE, None) == N.OK
+    b = lib.nvfp4_fakequant_bwd
+    # dual scales need grad_s_post and tied scales must not get one
+    assert b(FAKE, FAKE, 16, 16, FAKE, FAKE, FAKE, FAKE, None, None) == N.ERR_INVALID
+    assert b(FAKE, FAKE, 16, 16, FAKE, None, FAKE, FAKE, FAKE, None) == N.ERR_INVALID
+    assert b(FAKE, None, 16, 16, FAKE, None, FAKE, FAKE, None, None) == N.ERR_INVALID
+    assert b(FAKE, FAKE, 16, 16, FAKE, None, FAKE, None, None, None) == N.ERR_INVALID
+    assert b(FAKE, FAKE, 0, 16, FAKE, None, FAKE, FAKE, None, None) == N.OK
+
+
+def test_test_hooks_reject():
+    lib = N.lib()
+    assert lib.nvfp4_test_e2m1_rne_range(1, (1 << 32), FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_test_scale_encode_range(0, 0x7FFFFFFF, 2, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_test_scale_encode_range(7, 0, 2, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_test_e2m1_sr(None, FAKE, 4, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_test_sr_hash(0, 0, -1, FAKE, None) == N.ERR_INVALID
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(N, "_lib", None)
+    monkeypatch.setattr(N, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(N.NativeError):
+        N.lib()

@@ -357,3 +357,15 @@ def test_sr_index_orientation():
         S = np.float32(np.float32(D) * np.float32(alpha))
         y = np.float32(x[r, c] * np.float32(np.float32(1.0) / S))
         assert nibt[c, r] == O.e2m1_code_sr(float(y), O.sr_hash(1234, c * 32 + r))
+
+
+def test_nan_and_inf_elements_with_finite_amax():
+    x = np.ones((1, 48), np.float32)
+    x[0, 3] = np.nan
+    x[0, 20] = np.inf
+    x[0, 40] = -np.inf
+    codes, sc, n4 = O.quantize(x, 10.0, select=O.SELECT_4OVER6)
+    nib = O.unpack_codes(codes)
+    assert sc[0, 0] == 0x7F and np.all(nib[0, :16] == 0)
+    assert sc[0, 1] == 0x7E and nib[0, 20] == 7 and n4 == 0
+    assert sc[0, 2] == 0x7E and nib[0, 40] == 15

@@ -1,5 +1,5 @@
 """Benchmark: NVFP4 Four-Over-Six quantization of an 8192 x 4096 bf16
-activation tensor on one MI355X.
+activation tensor on one MI355X (default workload).
 
 One step is the whole hot path of that workload: tensor amax (current
 scaling) -> Four-Over-Six quantize along the hidden dimension (E4M3 scales,
@@ -11,6 +11,14 @@ Infinity Cache) are used in rotation so each launch streams from HBM.
 Prints one JSON line.  `value` is the step's algorithmic bytes per second
 (GB/s); per-kernel figures sit under "kernels", the dominant kernel's under
 "roofline", and the CPU oracle timed on a sample under "cpu_baseline".
+
+Other workloads (--workload) time the remaining paths of the method on their
+own shapes; their lines carry the same fields under their own metric names:
+  weight-1k  256x1024: amax + max->6 quantize + 4/6 quantize + dequantize
+  weight     4096x4096: amax + 4/6 quantize with the 4/6 choice count
+  qat        14336x4096: fake-quant forward + backward, tied and dual scales
+  gradient   16384x8192: stale-amax UE5M3 SR quantize, row- and column-wise
+             in one fused pass
 """
 import argparse
 import hashlib
@@ -24,18 +32,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-WORKLOAD = "activation"
-N_SETS = 8
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILE_DIR, "quantize_4over6_activation_8192x4096_traffic.json")
 KERNEL_SOURCES = ["quantize.hip", "device.hpp", "common.hpp"]
+METRIC = "NVFP4 4/6 quantize GB/s (Gelem/s) at 8192x4096 bf16; % of HBM peak"
 
 # algorithmic bytes per element (read + written, each byte counted once)
-BYTES = {
-    "tensor_amax": 2.0,                      # bf16 read
-    "quantize_4over6": 2.0 + 0.5 + 1 / 16,   # bf16 read, 4-bit codes + 1 scale byte per 16
-    "dequantize_f32_mse": 0.5 + 1 / 16 + 2.0 + 4.0,  # codes+scales+bf16 read, f32 written
-}
+B_AMAX = 2.0                    # bf16 read
+B_QUANT = 2.0 + 0.5 + 1 / 16    # bf16 read, 4-bit codes + 1 scale byte per 16
+B_DEQ_MSE = 0.5 + 1 / 16 + 2.0 + 4.0  # codes + scales + bf16 read, f32 written
+B_DEQ = 0.5 + 1 / 16 + 4.0
+B_FQ_FWD = {"tied": 2.0 + 0.25 + 4.0, "dual": 2.0 + 0.5 + 4.0}
+B_FQ_BWD = {"tied": 2.0 + 4.0 + 0.25 + 4.0 + 0.25, "dual": 2.0 + 4.0 + 0.5 + 4.0 + 0.5}
+B_FUSED = 2.0 + 2 * (0.5 + 1 / 16)
 
 
 def log(msg):
@@ -63,16 +72,60 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+class Timer:
+    """HIP events on the stream the kernels are launched on (torch's current
+    stream, which the binding passes to every call)."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream(dev)
+
+    def avg_us(self, fn, reps, nsets):
+        torch = self.torch
+        for i in range(nsets):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+
+def kernel_entry(us, n, bpe):
+    gbps = n * bpe / (us * 1e-6) / 1e9
+    return {"us": round(us, 3), "bytes_per_elem": round(bpe, 4), "gbps": round(gbps, 1),
+            "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+            "gelem_per_s": round(n / (us * 1e-6) / 1e9, 1)}
+
+
+def finish(line, kernels, args, traffic_for=None, traffic=None):
+    dominant = max(kernels, key=lambda k: kernels[k]["us"])
+    d = kernels[dominant]
+    line["kernels"] = kernels
+    line["roofline"] = {"kernel": dominant, "bound": "hbm", "achieved": d["gbps"],
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d["frac_hbm"],
+                        "traffic": traffic if dominant == traffic_for else None}
+    return line
+
+
+def base_line(metric, value, unit, args, ms_step, workload, extra_cfg, n):
+    return {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": dict({"workload": workload}, **extra_cfg),
+            "gelem_per_s": round(n / (ms_step * 1e-3) / 1e9, 2)}
+
+
 def cpu_baseline(xb, target_cpu_s=12.0):
     """The oracle, untuned, on the host: the same step on a bounded sample of
     whole rows of the same tensor, repeated until ~target_cpu_s of CPU time."""
-    import numpy as np
     import oracle as O
 
     threads = O.num_threads()
-    rows = xb.shape[0]
-    sample_rows = rows  # the whole tensor is a bounded sample here (seconds)
-    x = xb[:sample_rows]
+    x = xb
     n = x.size
     reps, t_wall, t_cpu0 = 0, 0.0, time.process_time()
     while True:
@@ -86,17 +139,237 @@ def cpu_baseline(xb, target_cpu_s=12.0):
         if time.process_time() - t_cpu0 >= target_cpu_s or reps >= 20:
             break
     per_step = t_wall / reps
-    step_bytes = n * sum(BYTES.values())
+    step_bytes = n * (B_AMAX + B_QUANT + B_DEQ_MSE)
     return {
         "value": round(step_bytes / per_step / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{sample_rows}x{x.shape[1]} rows of the same tensor, full step "
-                  f"(amax, 4/6 quantize, dequantize, SSE), {reps} reps, "
-                  f"{per_step * 1e3:.1f} ms/step wall, {threads} OpenMP threads",
+        "sample": f"the whole {x.shape[0]}x{x.shape[1]} tensor, full step (amax, 4/6 "
+                  f"quantize, dequantize, SSE), {reps} reps, {per_step * 1e3:.1f} ms/step "
+                  f"wall, {threads} OpenMP threads",
         "gelem_per_s": round(n / per_step / 1e9, 4),
     }
+
+
+def to_dev(torch, np, bits, dev):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+# ---------------------------------------------------------------- workloads
+def run_activation(args, torch, np, nv, synth, dev, timer):
+    nsets = 8
+    log("generating the 8192x4096 activation tensor")
+    xb = synth.make("activation")["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    x0 = to_dev(torch, np, xb, dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    amaxs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    outs = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)}
+            for _ in range(nsets)]
+    xh = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    gm = nv.default_global_max("e4m3", "4over6")
+    if args.profile_once:
+        big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(big)
+        dst.copy_(big)
+        for i in range(4):
+            nv.quantize(xs[i], amaxs[i], select="4over6", out=outs[i])
+        torch.cuda.synchronize()
+        log("profile-once done: one 256 MiB copy, 4 quantize launches")
+        return None
+    total = args.warmup + args.steps
+    sse = torch.zeros(total, dtype=torch.float64, device=dev)
+
+    def step(i):
+        k = i % nsets
+        nv.tensor_amax(xs[k], out=amaxs[k])
+        nv.quantize(xs[k], amaxs[k], select="4over6", out=outs[k])
+        nv.dequantize(outs[k]["codes"], outs[k]["scales"], amaxs[k], global_max=gm,
+                      x_ref=xs[k], sse=sse[i:i + 1], out=xh[k])
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(timer.stream)
+    for i in range(args.warmup, total):
+        step(i)
+    e1.record(timer.stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step")
+    reps = max(args.steps, 40)
+    sse_k = torch.zeros(1, dtype=torch.float64, device=dev)
+    us = {
+        "tensor_amax": timer.avg_us(lambda i: nv.tensor_amax(xs[i % nsets], out=amaxs[i % nsets]),
+                                    reps, nsets),
+        "quantize_4over6": timer.avg_us(lambda i: nv.quantize(
+            xs[i % nsets], amaxs[i % nsets], select="4over6", out=outs[i % nsets]), reps, nsets),
+        "dequantize_f32_mse": timer.avg_us(lambda i: nv.dequantize(
+            outs[i % nsets]["codes"], outs[i % nsets]["scales"], amaxs[i % nsets], global_max=gm,
+            x_ref=xs[i % nsets], sse=sse_k, out=xh[i % nsets]), reps, nsets),
+    }
+    kernels = {"tensor_amax": kernel_entry(us["tensor_amax"], n, B_AMAX),
+               "quantize_4over6": kernel_entry(us["quantize_4over6"], n, B_QUANT),
+               "dequantize_f32_mse": kernel_entry(us["dequantize_f32_mse"], n, B_DEQ_MSE)}
+    log(f"kernels: {json.dumps(kernels)}")
+    step_bytes = n * (B_AMAX + B_QUANT + B_DEQ_MSE)
+    line = base_line(METRIC, step_bytes / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     "activation 8192x4096 bf16 (Student-t(3) x 0.5, 8 channels x 50, seed 2): "
+                     "tensor amax -> Four-Over-Six quantize along hidden (E4M3 scales, FP8 max "
+                     "256, RNE) -> dequantize to f32 with binary64 MSE report",
+                     {"rows": rows, "cols": cols, "elements": n, "step_bytes": int(step_bytes),
+                      "buffer_sets": nsets}, n)
+    finish(line, kernels, args, "quantize_4over6", measured_traffic())
+    q = kernels["quantize_4over6"]
+    line["quantize_roofline"] = {"achieved": q["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                 "frac": q["frac_hbm"], "gelem_per_s": q["gelem_per_s"],
+                                 "traffic": measured_traffic()}
+    line["mse"] = float(sse[total - 1].item()) / n
+    line["amax"] = float(amaxs[(total - 1) % nsets].item())
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(xb)
+    else:
+        line["cpu_baseline"] = None
+    return line
+
+
+def run_weight(args, torch, np, nv, synth, dev, timer, small):
+    name = "weight-1k" if small else "weight"
+    xb = synth.make(name)["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    nsets = 8
+    x0 = to_dev(torch, np, xb, dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    amaxs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    outs = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+             "count4": torch.zeros(1, dtype=torch.int64, device=dev)} for _ in range(nsets)]
+    xh = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    gm = 448.0 if small else 256.0
+    reps = max(args.steps, 40)
+    us = {"tensor_amax": timer.avg_us(lambda i: nv.tensor_amax(xs[i % nsets], out=amaxs[i % nsets]),
+                                      reps, nsets)}
+    if small:
+        o6 = [{"codes": o["codes"], "scales": o["scales"]} for o in outs]
+        us["quantize_6"] = timer.avg_us(lambda i: nv.quantize(
+            xs[i % nsets], amaxs[i % nsets], select="6", global_max=gm, out=o6[i % nsets]), reps, nsets)
+        us["quantize_4over6"] = timer.avg_us(lambda i: nv.quantize(
+            xs[i % nsets], amaxs[i % nsets], select="4over6", global_max=gm, out=o6[i % nsets]),
+            reps, nsets)
+        us["dequantize_f32"] = timer.avg_us(lambda i: nv.dequantize(
+            outs[i % nsets]["codes"], outs[i % nsets]["scales"], amaxs[i % nsets], global_max=gm,
+            out=xh[i % nsets]), reps, nsets)
+        step_keys = ["tensor_amax", "quantize_6", "quantize_4over6", "dequantize_f32"]
+        bpe = {"tensor_amax": B_AMAX, "quantize_6": B_QUANT, "quantize_4over6": B_QUANT,
+               "dequantize_f32": B_DEQ}
+        metric = "NVFP4 quantize latency at 256x1024 bf16 (launch-bound; us per step)"
+    else:
+        us["quantize_4over6_count"] = timer.avg_us(lambda i: nv.quantize(
+            xs[i % nsets], amaxs[i % nsets], select="4over6", out=outs[i % nsets]), reps, nsets)
+        step_keys = ["tensor_amax", "quantize_4over6_count"]
+        bpe = {"tensor_amax": B_AMAX, "quantize_4over6_count": B_QUANT}
+        metric = "NVFP4 4/6 quantize GB/s at 4096x4096 bf16 weight (with 4/6 count)"
+    kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in step_keys}
+    ms_step = sum(us[k] for k in step_keys) / 1e3
+    step_bytes = n * sum(bpe[k] for k in step_keys)
+    line = base_line(metric, step_bytes / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     f"{name} {rows}x{cols} bf16 (synthetic, seed {synth.SEEDS[name]})",
+                     {"rows": rows, "cols": cols, "elements": n,
+                      "timing": "sum of per-kernel event averages"}, n)
+    line["us_per_step"] = round(ms_step * 1e3, 2)
+    return finish(line, kernels, args)
+
+
+def run_qat(args, torch, np, nv, synth, dev, timer):
+    log("generating the 14336x4096 weight and gradient")
+    d = synth.make("qat")
+    xb, g = d["x"], d["g"]
+    rows, cols = xb.shape
+    n = rows * cols
+    nsets = 2  # 2 x (117 MiB weight + 235 MiB gradient) > the Infinity Cache
+    x0 = to_dev(torch, np, xb, dev)
+    g0 = torch.from_numpy(g).to(dev)
+    xs = [x0, x0.clone()]
+    gs = [g0, g0.clone()]
+    amax = nv.tensor_amax(x0)
+    q = nv.quantize(x0, amax, select="6", global_max=448.0)
+    _, s = nv.dequantize(q.codes, q.scales, amax, global_max=448.0, want_block_scale=True)
+    ss = [s, s.clone()]
+    sp = [(s * 1.125).contiguous(), (s * 1.125).contiguous()]
+    xq = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    outs = [{"dx": torch.empty((rows, cols), dtype=torch.float32, device=dev),
+             "ds_pre": torch.empty_like(s), "ds_post": torch.empty_like(s)} for _ in range(nsets)]
+    reps = max(args.steps, 20)
+    us = {
+        "fakequant_fwd_tied": timer.avg_us(lambda i: nv.fakequant_fwd(
+            xs[i % 2], ss[i % 2], out=xq[i % 2]), reps, nsets),
+        "fakequant_bwd_tied": timer.avg_us(lambda i: nv.fakequant_bwd(
+            xs[i % 2], gs[i % 2], ss[i % 2], out={"dx": outs[i % 2]["dx"], "ds_pre": outs[i % 2]["ds_pre"]}),
+            reps, nsets),
+        "fakequant_fwd_dual": timer.avg_us(lambda i: nv.fakequant_fwd(
+            xs[i % 2], ss[i % 2], sp[i % 2], out=xq[i % 2]), reps, nsets),
+        "fakequant_bwd_dual": timer.avg_us(lambda i: nv.fakequant_bwd(
+            xs[i % 2], gs[i % 2], ss[i % 2], sp[i % 2], out=outs[i % 2]), reps, nsets),
+    }
+    bpe = {"fakequant_fwd_tied": B_FQ_FWD["tied"], "fakequant_bwd_tied": B_FQ_BWD["tied"],
+           "fakequant_fwd_dual": B_FQ_FWD["dual"], "fakequant_bwd_dual": B_FQ_BWD["dual"]}
+    kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
+    ms_step = (us["fakequant_fwd_dual"] + us["fakequant_bwd_dual"]) / 1e3
+    step_bytes = n * (bpe["fakequant_fwd_dual"] + bpe["fakequant_bwd_dual"])
+    line = base_line("NVFP4 scale-learning fake-quant fwd+bwd GB/s at 14336x4096 (dual scales)",
+                     step_bytes / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     "qat 14336x4096 bf16 weight N(0,0.02), f32 gradient N(0,1e-3), seed 3; "
+                     "scales initialised from amax/6 in E4M3; step = dual-scale fwd + bwd",
+                     {"rows": rows, "cols": cols, "elements": n,
+                      "timing": "sum of per-kernel event averages"}, n)
+    return finish(line, kernels, args)
+
+
+def run_gradient(args, torch, np, nv, synth, dev, timer):
+    log("generating the 16384x8192 gradient")
+    xb = synth.make("gradient")["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    nsets = 2  # 2 x 256 MiB > the Infinity Cache
+    x0 = to_dev(torch, np, xb, dev)
+    xs = [x0, x0.clone()]
+    a = nv.tensor_amax(x0)
+    stale = (a * 0.8).contiguous()
+    outs = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+             "codes_t": torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev),
+             "scales_t": torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev)}
+            for _ in range(nsets)]
+    reps = max(args.steps, 20)
+    us = {
+        "quantize_fused_row_col_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
+            xs[i % 2], stale, fmt="ue5m3", select="6", rounding="sr", axes="both", seed=1234,
+            out=outs[i % 2]), reps, nsets),
+        "quantize_row_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
+            xs[i % 2], stale, fmt="ue5m3", select="6", rounding="sr", axes="row", seed=1234,
+            out={"codes": outs[i % 2]["codes"], "scales": outs[i % 2]["scales"]}), reps, nsets),
+        "quantize_col_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
+            xs[i % 2], stale, fmt="ue5m3", select="6", rounding="sr", axes="col", seed=1234,
+            out={"codes_t": outs[i % 2]["codes_t"], "scales_t": outs[i % 2]["scales_t"]}),
+            reps, nsets),
+    }
+    bpe = {"quantize_fused_row_col_sr_ue5m3": B_FUSED, "quantize_row_sr_ue5m3": B_QUANT,
+           "quantize_col_sr_ue5m3": B_QUANT}
+    kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
+    ms_step = us["quantize_fused_row_col_sr_ue5m3"] / 1e3
+    line = base_line("NVFP4 fused row+column SR quantize GB/s at 16384x8192 bf16 (UE5M3, stale amax)",
+                     n * B_FUSED / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     "gradient 16384x8192 bf16 N(0,1) x 10^U(-3,0) per row, seed 4; stale amax "
+                     "0.8 A; UE5M3 scales; SR seed 1234; row- and column-wise in one pass",
+                     {"rows": rows, "cols": cols, "elements": n}, n)
+    return finish(line, kernels, args)
 
 
 def main():
@@ -104,6 +377,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="activation",
+                    choices=["activation", "weight-1k", "weight", "qat", "gradient"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 256 MiB copy and a few quantize launches for PMC counters")
@@ -122,140 +397,17 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log("generating the 8192x4096 activation tensor")
-    xb = synth.make(WORKLOAD)["x"]
-    rows, cols = xb.shape
-    n = rows * cols
-    x0 = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
-    xs = [x0] + [x0.clone() for _ in range(N_SETS - 1)]
-    amaxs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(N_SETS)]
-    outs = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
-             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)}
-            for _ in range(N_SETS)]
-    xh = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(N_SETS)]
-    gm = nv.default_global_max("e4m3", "4over6")
-
-    if args.profile_once:
-        big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(big)
-        dst.copy_(big)
-        for i in range(4):
-            nv.quantize(xs[i], amaxs[i], select="4over6", out=outs[i])
-        torch.cuda.synchronize()
-        log("profile-once done: one 256 MiB copy, 4 quantize launches")
-        return
-
-    total = args.warmup + args.steps
-    sse = torch.zeros(total, dtype=torch.float64, device=dev)
-
-    def step(i):
-        k = i % N_SETS
-        nv.tensor_amax(xs[k], out=amaxs[k])
-        nv.quantize(xs[k], amaxs[k], select="4over6", out=outs[k])
-        nv.dequantize(outs[k]["codes"], outs[k]["scales"], amaxs[k], global_max=gm,
-                      x_ref=xs[k], sse=sse[i:i + 1], out=xh[k])
-
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_host0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.warmup, total):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step (host clock {t_host * 1e3 / args.steps:.2f} us/step)")
-
-    # per-kernel average duration: back-to-back launches of one kernel over
-    # the rotating buffer sets, bracketed by events on the same stream
-    def per_kernel(fn, reps):
-        for i in range(N_SETS):
-            fn(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3  # us
-
-    reps = max(args.steps, 40)
-    sse_k = torch.zeros(1, dtype=torch.float64, device=dev)
-    us = {
-        "tensor_amax": per_kernel(lambda i: nv.tensor_amax(xs[i % N_SETS], out=amaxs[i % N_SETS]), reps),
-        "quantize_4over6": per_kernel(lambda i: nv.quantize(xs[i % N_SETS], amaxs[i % N_SETS],
-                                                            select="4over6", out=outs[i % N_SETS]), reps),
-        "dequantize_f32_mse": per_kernel(lambda i: nv.dequantize(
-            outs[i % N_SETS]["codes"], outs[i % N_SETS]["scales"], amaxs[i % N_SETS], global_max=gm,
-            x_ref=xs[i % N_SETS], sse=sse_k, out=xh[i % N_SETS]), reps),
-    }
-    kernels = {}
-    for k, t in us.items():
-        gbps = n * BYTES[k] / (t * 1e-6) / 1e9
-        kernels[k] = {"us": round(t, 3), "bytes_per_elem": round(BYTES[k], 4),
-                      "gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                      "gelem_per_s": round(n / (t * 1e-6) / 1e9, 1)}
-    dominant = max(us, key=us.get)
-    log(f"kernels: {json.dumps(kernels)}")
-
-    # results of the last timed step (report only)
-    last = (total - 1) % N_SETS
-    mse = float(sse[total - 1].item()) / n
-    step_bytes = n * sum(BYTES.values())
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    d = kernels[dominant]
-    traffic = measured_traffic() if dominant == "quantize_4over6" else None
-    line = {
-        "metric": "NVFP4 4/6 quantize GB/s (Gelem/s) at 8192x4096 bf16; % of HBM peak",
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": "activation 8192x4096 bf16 (Student-t(3) x 0.5, 8 channels x 50, seed 2): "
-                        "tensor amax -> Four-Over-Six quantize along hidden (E4M3 scales, FP8 max "
-                        "256, RNE) -> dequantize to f32 with binary64 MSE report",
-            "rows": rows, "cols": cols, "elements": n, "step_bytes": int(step_bytes),
-            "buffer_sets": N_SETS,
-        },
-        "gelem_per_s": round(n / (ms_step * 1e-3) / 1e9, 2),
-        "kernels": kernels,
-        "roofline": {
-            "kernel": dominant,
-            "bound": "hbm",
-            "achieved": d["gbps"],
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": d["frac_hbm"],
-            "traffic": traffic,
-        },
-        "quantize_roofline": {
-            "achieved": kernels["quantize_4over6"]["gbps"], "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": kernels["quantize_4over6"]["frac_hbm"],
-            "gelem_per_s": kernels["quantize_4over6"]["gelem_per_s"],
-        },
-        "mse": mse,
-        "amax": float(amaxs[last].item()),
-    }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on the host")
-        line["cpu_baseline"] = cpu_baseline(xb)
+    timer = Timer(torch, dev)
+    if args.workload == "activation":
+        line = run_activation(args, torch, np, nv, synth, dev, timer)
+    elif args.workload in ("weight-1k", "weight"):
+        line = run_weight(args, torch, np, nv, synth, dev, timer, args.workload == "weight-1k")
+    elif args.workload == "qat":
+        line = run_qat(args, torch, np, nv, synth, dev, timer)
     else:
-        line["cpu_baseline"] = None
-    print(json.dumps(line), flush=True)
+        line = run_gradient(args, torch, np, nv, synth, dev, timer)
+    if line is not None:
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -35,8 +35,9 @@
  *    error).
  *  - bfloat16 values travel as their 16-bit patterns (uint16_t).
  *  - Tensors are dense row-major [rows, cols].  Data pointers (x, codes,
- *    out_f32, out_bf16, grad tensors) must be 16-byte aligned; scale and
- *    per-block arrays need only their natural alignment.
+ *    out_f32, out_bf16, grad tensors) must be 16-byte aligned; the row-wise
+ *    scale array of nvfp4_quantize 4-byte aligned; other per-block arrays
+ *    need only their natural alignment.
  *  - Packed codes: byte j of a row holds element 2j in its low nibble and
  *    element 2j+1 in its high nibble; nibble = sign << 3 | magnitude index.
  *    Scales: one byte per 16-element block, [rows, cols/16], row-major.

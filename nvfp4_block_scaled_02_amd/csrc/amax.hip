@@ -1,11 +1,14 @@
 // amax.hip -- tensor amax for current-tensor scaling ("UE5M3: 给 FP4 训练算
 // 一笔更宽容的账", section 数学推导): A = max |x| over a bf16 tensor.
 //
-// HBM-bound (2 bytes read per element).  Each lane streams 16-byte chunks,
-// folds them with packed 16-bit integer max on the sign-cleared patterns
-// (integer order = magnitude order; NaN > inf > finite), the wavefront
-// reduces with DPP moves, and one integer atomicMax per workgroup lands the
-// result as the float whose bits are (pattern << 16).
+// HBM-bound (2 bytes read per element).  One 1024-thread workgroup per CU;
+// each lane streams 16-byte chunks with non-temporal loads, four in flight,
+// folding them with packed 16-bit integer max on the sign-cleared patterns
+// (integer order = magnitude order; NaN > inf > finite).  The workgroup
+// reduces through cross-lane shuffles and LDS, and one integer atomicMax per
+// workgroup lands the result as the float whose bits are (pattern << 16):
+// same-address atomics serialize, so the grid is kept to one workgroup per
+// CU.  A one-lane kernel clears the result first.
 #include "common.hpp"
 #include "device.hpp"
 
@@ -25,13 +28,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 constexpr int kAmaxUnroll = 4;
+constexpr int kAmaxThreads = 1024;
 
-__global__ void __launch_bounds__(kThreads) amax_kernel(const uint4* __restrict__ x, int64_t nchunks,
+__global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const uint4* __restrict__ x, int64_t nchunks,
                                                         const uint16_t* __restrict__ tail,
                                                         int ntail, uint32_t* out) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
   // unrolled body: kAmaxUnroll independent 16-byte loads in flight per lane
   for (; i + (kAmaxUnroll - 1) * stride < nchunks; i += kAmaxUnroll * stride) {
     uint4 w[kAmaxUnroll];
@@ -52,13 +56,13 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const uint4* __restrict_
     m = m > v ? m : v;
   }
   m = wave_max_u32(m);
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t red[kAmaxThreads / 64];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
-    for (int w2 = 1; w2 < kThreads / 64; ++w2) r = r > red[w2] ? r : red[w2];
+    for (int w2 = 1; w2 < kAmaxThreads / 64; ++w2) r = r > red[w2] ? r : red[w2];
     atomicMax(out, r << 16);
   }
 }
@@ -69,13 +73,12 @@ hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipS
   if (numel == 0) return hipGetLastError();
   const int64_t nchunks = numel / kChunk;
   const int ntail = (int)(numel - nchunks * kChunk);
-  // enough workgroups to fill every CU several times over, each lane doing
-  // at least a few unrolled iterations
-  const int64_t want = (nchunks + (int64_t)kThreads * kAmaxUnroll - 1) / ((int64_t)kThreads * kAmaxUnroll);
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  // one workgroup per CU (fewer if the tensor is small)
+  const int64_t want = (nchunks + (int64_t)kAmaxThreads * kAmaxUnroll - 1) / ((int64_t)kAmaxThreads * kAmaxUnroll);
+  const int64_t cap = (int64_t)device_cu_count();
   int64_t grid = want < cap ? want : cap;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(kAmaxThreads), 0, s,
                      reinterpret_cast<const uint4*>(x), nchunks, x + nchunks * kChunk, ntail, o);
   return hipGetLastError();
 }

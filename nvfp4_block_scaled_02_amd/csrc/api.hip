@@ -117,7 +117,8 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* a
     return NVFP4_ERR_INVALID;
   if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
   if (axes & NVFP4_AXIS_ROW) {
-    if (cols % 16 != 0 || !codes || !scales || !aligned16(codes)) return NVFP4_ERR_INVALID;
+    if (cols % 16 != 0 || !codes || !scales || !aligned16(codes) || ((uintptr_t)scales & 3u))
+      return NVFP4_ERR_INVALID;
   }
   if (axes & NVFP4_AXIS_COL) {
     if (rows % 16 != 0 || cols % 8 != 0 || !codes_t || !scales_t || !aligned16(codes_t))

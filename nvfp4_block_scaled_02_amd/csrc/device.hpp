@@ -40,6 +40,10 @@ __device__ __forceinline__ void st_nt(uint4 v, uint4* p) {
   u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
+__device__ __forceinline__ void st_nt(uint2 v, uint2* p) {
+  u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
 __device__ __forceinline__ void st_nt(uint32_t v, uint32_t* p) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void st_nt(uint8_t v, uint8_t* p) { __builtin_nontemporal_store(v, p); }
 
@@ -94,7 +98,7 @@ __device__ __forceinline__ double shift1_in_quad_f64(double v) {
 
 // 8 binary32 values -> one dword of 8 nibbles, element i in nibble i.
 __device__ __forceinline__ uint32_t e2m1_rne_pack8(const float (&y)[8]) {
-  uint32_t w = 0;
+  uint32_t w = __float_as_uint(y[7]);  // placeholder: all four bytes are written
   w = NVFP4_CVT_PK_FP4(w, y[0], y[1], 0);
   w = NVFP4_CVT_PK_FP4(w, y[2], y[3], 1);
   w = NVFP4_CVT_PK_FP4(w, y[4], y[5], 2);
@@ -161,7 +165,7 @@ __device__ __forceinline__ uint32_t e2m1_sr_code(float y, uint32_t h) {
 // negative input (only from an unusable amax, whose output is replaced by the
 // NaN code) must still index inside the 127-entry code table.
 __device__ __forceinline__ uint32_t e4m3_encode_pair(float a, float b) {
-  i16x2 old = {0, 0};
+  i16x2 old = __builtin_bit_cast(i16x2, __float_as_uint(a));  // low word is replaced
   i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, __builtin_fminf(a, 448.0f),
                                                      __builtin_fminf(b, 448.0f), 1.0f, false);
   return (uint32_t)(uint16_t)r[0] & 0x7F7Fu;

@@ -23,38 +23,36 @@ __device__ __forceinline__ float fq_inv(float s) {
 }
 
 // ---------------------------------------------------------------- forward
-constexpr int kFqUnroll = 2;
+// A lane owns 4 consecutive elements (one contiguous float4 store per lane);
+// 4 lanes share a block's scales.
+constexpr int kFqUnroll = 4;
 
 template <bool DUAL>
 __global__ void __launch_bounds__(kThreads)
-fakequant_fwd_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* __restrict__ s_pre,
+fakequant_fwd_kernel(const uint2* __restrict__ x, int64_t nquads, const float* __restrict__ s_pre,
                      const float* __restrict__ s_post, float4* __restrict__ xq) {
   const int64_t per_iter = (int64_t)gridDim.x * kThreads * kFqUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * kFqUnroll; base < nchunks; base += per_iter) {
-    uint4 w[kFqUnroll];
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kFqUnroll; base < nquads; base += per_iter) {
+    uint2 w[kFqUnroll];
     float sp[kFqUnroll], so[kFqUnroll];
 #pragma unroll
     for (int u = 0; u < kFqUnroll; ++u) {
-      const int64_t ch = base + u * kThreads + threadIdx.x;
-      const bool ok = ch < nchunks;
-      w[u] = ok ? ld_nt(x + ch) : make_uint4(0, 0, 0, 0);
-      sp[u] = ok ? s_pre[ch >> 1] : 0.0f;
-      so[u] = DUAL ? (ok ? s_post[ch >> 1] : 0.0f) : sp[u];
+      const int64_t qd = base + u * kThreads + threadIdx.x;
+      const bool ok = qd < nquads;
+      w[u] = ok ? ld_nt(x + qd) : make_uint2(0, 0);
+      sp[u] = ok ? s_pre[qd >> 2] : 0.0f;
+      so[u] = DUAL ? (ok ? s_post[qd >> 2] : 0.0f) : sp[u];
     }
 #pragma unroll
     for (int u = 0; u < kFqUnroll; ++u) {
-      const int64_t ch = base + u * kThreads + threadIdx.x;
-      if (ch >= nchunks) continue;
+      const int64_t qd = base + u * kThreads + threadIdx.x;
+      if (qd >= nquads) continue;
       const float inv = fq_inv(sp[u]);
-      const float y[8] = {bf16_lo(w[u].x) * inv, bf16_hi(w[u].x) * inv, bf16_lo(w[u].y) * inv,
-                          bf16_hi(w[u].y) * inv, bf16_lo(w[u].z) * inv, bf16_hi(w[u].z) * inv,
-                          bf16_lo(w[u].w) * inv, bf16_hi(w[u].w) * inv};
-      float q[8];
-      e2m1_unpack8(e2m1_rne_pack8(y), q);
-      st_nt(make_float4(q[0] * so[u], q[1] * so[u], q[2] * so[u], q[3] * so[u]),
-                                  xq + 2 * ch);
-      st_nt(make_float4(q[4] * so[u], q[5] * so[u], q[6] * so[u], q[7] * so[u]),
-                                  xq + 2 * ch + 1);
+      uint32_t cw = 0;
+      cw = NVFP4_CVT_PK_FP4(cw, bf16_lo(w[u].x) * inv, bf16_hi(w[u].x) * inv, 0);
+      cw = NVFP4_CVT_PK_FP4(cw, bf16_lo(w[u].y) * inv, bf16_hi(w[u].y) * inv, 1);
+      const f32x2 q01 = NVFP4_DEC_PK_FP4(cw, 0), q23 = NVFP4_DEC_PK_FP4(cw, 1);
+      st_nt(make_float4(q01[0] * so[u], q01[1] * so[u], q23[0] * so[u], q23[1] * so[u]), xq + qd);
     }
   }
 }
@@ -161,15 +159,15 @@ static int64_t grid_for(int64_t units, int64_t per_wg) {
 }
 
 hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s) {
-  const int64_t nchunks = a.rows * a.cols / kChunk;
-  const int64_t grid = grid_for(nchunks, (int64_t)kThreads * kFqUnroll);
+  const int64_t nquads = a.rows * a.cols / 4;
+  const int64_t grid = grid_for(nquads, (int64_t)kThreads * kFqUnroll);
   if (a.s_post)
     hipLaunchKernelGGL(fakequant_fwd_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       reinterpret_cast<const uint4*>(a.x), nchunks, a.s_pre, a.s_post,
+                       reinterpret_cast<const uint2*>(a.x), nquads, a.s_pre, a.s_post,
                        reinterpret_cast<float4*>(a.xq));
   else
     hipLaunchKernelGGL(fakequant_fwd_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       reinterpret_cast<const uint4*>(a.x), nchunks, a.s_pre, a.s_post,
+                       reinterpret_cast<const uint2*>(a.x), nquads, a.s_pre, a.s_post,
                        reinterpret_cast<float4*>(a.xq));
   return hipGetLastError();
 }

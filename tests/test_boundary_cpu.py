@@ -62,7 +62,8 @@ def _q(**kw):
     dict(rnd=1, select=1), dict(gmax=-1.0), dict(gmax=float("inf")), dict(gmax=float("nan")),
     dict(codes=None), dict(scales=None), dict(axes=2, rows=24), dict(axes=2, codes_t=None),
     dict(axes=3, scales_t=None), dict(axes=2, cols=20, rows=16), dict(x=FAKE_ODD),
-    dict(codes=FAKE_ODD), dict(count4=FAKE_ODD), dict(rows=1 << 40, cols=1 << 40),
+    dict(codes=FAKE_ODD), dict(scales=FAKE + 2), dict(count4=FAKE_ODD),
+    dict(rows=1 << 40, cols=1 << 40),
 ])
 def test_quantize_rejects(kw):
     assert _q(**kw) == N.ERR_INVALID

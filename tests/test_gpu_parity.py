@@ -22,6 +22,11 @@ from nvfp4_block_scaled_02_amd import synth  # noqa: E402
 FMTS = {"e4m3": O.FMT_E4M3, "ue5m3": O.FMT_UE5M3}
 SELS = {"6": O.SELECT_6, "4over6": O.SELECT_4OVER6}
 RNDS = {"rne": O.ROUND_RNE, "sr": O.ROUND_SR}
+# The device error report takes x - x_hat in binary32 (one rounding at most,
+# 2^-24 relative, and none when x_hat is within a factor 2 of x), then squares
+# and sums in binary64 in another order than the oracle: relative error below
+# 2 * 2^-24 + n * 2^-53, bounded here by 1e-6.
+SSE_REL = 1e-6
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -125,7 +130,7 @@ def test_config1_weight_1k_both_selections_and_dequantize():
         assert np.array_equal(gb16.view(torch.int16).cpu().numpy().view(np.uint16), xb16)
         assert np.array_equal(gbs.cpu().numpy(), bs)
         sse = O.sse(xb, xh)
-        assert abs(gsse.item() - sse) <= 1e-9 * sse
+        assert abs(gsse.item() - sse) <= SSE_REL * sse
         log(f"weight-1k select={sel}: count4={got['count4']} MSE={sse / xb.size:.6g}")
 
 
@@ -154,7 +159,7 @@ def test_config3_activation_8192x4096_with_mse():
     rx = O.dequantize(ref["codes"], ref["scales"], A)
     assert np.array_equal(xh.cpu().numpy(), rx)
     r_sse = O.sse(xb, rx)
-    assert abs(sse.item() - r_sse) <= 1e-9 * r_sse
+    assert abs(sse.item() - r_sse) <= SSE_REL * r_sse
     log(f"activation: MSE {r_sse / xb.size:.6g}, count4 {got['count4']}")
 
 

@@ -91,19 +91,24 @@ int or_e2m1_code(float y) {
 
 /* Stochastic rounding of y onto E2M1 ([E2E] Re-quantization with stochastic
  * rounding; [UE] 实现): |y| goes to the grid point above it with probability
- * (|y| - lo) / (hi - lo) and to the one below otherwise, so the expectation
- * is |y|.  The uniform variate is u = (h >> 8) * 2^-24 from the 32-bit hash
- * h; the rule is "up iff u < p".  |y| >= 6 saturates to 6. */
+ * (|y| - lo) / (hi - lo) and to the one below otherwise.  Read as dithered
+ * truncation: the fraction p = (|y| - lo) / (hi - lo), truncated to 22 bits
+ * (F = floor(p * 2^22)), is added to the 22-bit variate u = h >> 10 taken from
+ * the top of the 32-bit hash h; a carry out of 22 bits rounds up:
+ *   up iff u + F >= 2^22,
+ * so P(up) = F / 2^22, which is p exactly when p has at most 22 fractional
+ * bits (every |y| >= 1) and below p by less than 2^-22 otherwise.  |y| >= 6
+ * saturates to 6; the sign is kept. */
 int or_e2m1_code_sr(float y, uint32_t h) {
   int sign = signbit(y) ? 8 : 0;
-  float a = fabsf(y);
-  if (a >= 6.0f) return sign | 7;
+  double a = fabs((double)y);
+  if (a >= 6.0) return sign | 7;
   int lo = 0;
-  while (lo < 6 && E2M1_MAG[lo + 1] <= (double)a) ++lo;
-  float step = (float)(E2M1_MAG[lo + 1] - E2M1_MAG[lo]);
-  float p = (a - (float)E2M1_MAG[lo]) * (1.0f / step); /* exact: step is 2^k */
-  float u = (float)(h >> 8) * 0x1p-24f;                /* exact */
-  return sign | (u < p ? lo + 1 : lo);
+  while (lo < 6 && E2M1_MAG[lo + 1] <= a) ++lo;
+  double step = E2M1_MAG[lo + 1] - E2M1_MAG[lo];
+  uint32_t F = (uint32_t)floor((a - E2M1_MAG[lo]) / step * 4194304.0); /* exact */
+  uint32_t u = h >> 10;
+  return sign | ((u + F >= (1u << 22)) ? lo + 1 : lo);
 }
 
 /* ------------------------------------------------------------------ */

@@ -84,14 +84,14 @@ def test_sr_decision_matches_oracle():
                         np.nextafter(grid, np.float32(9)), [5.999999, 6.0000005, 1e-40, -1e-40],
                         rng.standard_normal(10000) * 1e-30]).astype(np.float32)
     h = rng.integers(0, 1 << 32, y.size, dtype=np.uint64).astype(np.uint32)
-    # variates right at the decision threshold: h >> 8 = ceil(p 2^24) and one below
+    # variates right at the decision threshold: h >> 10 = 2^22 - F and one below
     a = np.abs(y[:2000]).astype(np.float64)
     lo = grid[np.searchsorted(grid, a, side="right") - 1].astype(np.float64)
     hi = grid[np.minimum(np.searchsorted(grid, a, side="right"), 7)].astype(np.float64)
-    p = np.where(hi > lo, (a - lo) / np.where(hi > lo, hi - lo, 1), 0)
-    k = np.ceil(p * 2 ** 24).astype(np.int64)
-    h[:2000] = (np.clip(k, 0, 2 ** 24 - 1) << 8).astype(np.uint32)
-    h[2000:4000] = (np.clip(k[:2000] - 1, 0, 2 ** 24 - 1) << 8).astype(np.uint32)
+    F = np.where(hi > lo, np.floor((a - lo) / np.where(hi > lo, hi - lo, 1) * 2.0 ** 22), 0)
+    T = (2 ** 22 - F).astype(np.int64)
+    h[:2000] = (np.clip(T, 0, 2 ** 22 - 1) << 10).astype(np.uint32)
+    h[2000:4000] = ((np.clip(T - 1, 0, 2 ** 22 - 1) << 10) | 0x3FF).astype(np.uint32)
     y[2000:4000] = y[:2000]
     yd = dev_f32(y)
     hd = torch.from_numpy(h.view(np.int32)).cuda()

@@ -83,26 +83,34 @@ def test_sr_example(pages):
 
 
 def test_sr_threshold_makes_it_unbiased():
-    """Up iff u < p with u on the 2^-24 grid: exactly ceil(p 2^24) of the 2^24
-    variates round up, so for p with <= 24 fractional bits E[q] = |y|."""
+    """Up iff u + F >= 2^22 with u = h >> 10 uniform on 22 bits and F the
+    fraction truncated to 22 bits: exactly F of the 2^22 variates round up, so
+    E[q] = |y| whenever p has at most 22 fractional bits (every |y| >= 1) and
+    falls short by less than 2^-22 of a step otherwise."""
     rng = np.random.default_rng(5)
     ys = np.concatenate([rng.uniform(0.25, 6.0, 300).astype(np.float32),
-                         np.array([0.25, 0.3, 1.1, 2.25, 4.5, 5.999999], np.float32)])
+                         rng.uniform(1e-6, 0.25, 100).astype(np.float32),
+                         np.array([0.25, 0.3, 1.1, 2.25, 4.5, 5.999999, 1e-30], np.float32)])
     grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
     for y in ys:
         a = Fraction(float(y))
         lo = max(g for g in grid if g <= a)
-        hi = min(g for g in grid if g > a) if a < 6 else 6.0
-        p = (a - Fraction(lo)) / (Fraction(hi) - Fraction(lo))
-        k = p * 2 ** 24
-        assert k.denominator == 1  # p has <= 24 fractional bits here
-        k = int(k)
-        if 0 < k:
-            assert O.e2m1_value(O.e2m1_code_sr(float(y), (k - 1) << 8)) == hi
-        if k < 2 ** 24:
-            assert O.e2m1_value(O.e2m1_code_sr(float(y), k << 8)) == lo
-        # expectation over the 2^24 variates equals |y| exactly
-        assert Fraction(lo) + (Fraction(hi) - Fraction(lo)) * Fraction(k, 2 ** 24) == a
+        hi = min(g for g in grid if g > a)
+        step = Fraction(hi) - Fraction(lo)
+        p = (a - Fraction(lo)) / step
+        F = int(p * 2 ** 22)  # floor
+        T = 2 ** 22 - F        # smallest u that rounds up
+        if T <= 2 ** 22 - 1:
+            assert O.e2m1_value(O.e2m1_code_sr(float(y), T << 10)) == hi
+            assert O.e2m1_value(O.e2m1_code_sr(float(y), (T << 10) | 0x3FF)) == hi
+        if T >= 1:
+            assert O.e2m1_value(O.e2m1_code_sr(float(y), (T - 1) << 10)) == lo
+            assert O.e2m1_value(O.e2m1_code_sr(float(y), ((T - 1) << 10) | 0x3FF)) == lo
+        # expectation over the 2^22 variates
+        e = Fraction(lo) + step * Fraction(F, 2 ** 22)
+        assert e <= a and a - e < step * Fraction(1, 2 ** 22)
+        if a >= 1:
+            assert e == a
     # on-grid values never move, and the sign is kept
     for g in grid:
         for h in (0, 0xFFFFFFFF, 0x12345678):

@@ -18,7 +18,8 @@ extern "C" {
  * binary32 value whose bit pattern is first + i, for i < n (n <= 2^32). */
 int nvfp4_test_e2m1_rne_range(uint32_t first, int64_t n, uint8_t* codes, void* stream);
 
-/* codes[i] = stochastic-rounding E2M1 code of y[i] with 32-bit variate h[i]. */
+/* codes[i] = stochastic-rounding E2M1 code of y[i] with 32-bit hash h[i], in
+ * groups of eight through the quantizer's packing routine; n % 8 == 0. */
 int nvfp4_test_e2m1_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, void* stream);
 
 /* codes[i] = block-scale code (format fmt) of the non-negative binary32

@@ -47,10 +47,20 @@ __global__ void test_e2m1_range_kernel(uint32_t first, int64_t n, uint8_t* codes
   }
 }
 
+// Eight values per thread through the quantizer's own packing routine (so
+// both nibble positions of the instruction are exercised); n % 8 == 0.
 __global__ void test_e2m1_sr_kernel(const float* y, const uint32_t* h, int64_t n, uint8_t* codes) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    codes[i] = (uint8_t)e2m1_sr_code(y[i], h[i]);
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n / 8;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    float yy[8];
+    uint32_t hh[8];
+    for (int i = 0; i < 8; ++i) {
+      yy[i] = y[8 * g + i];
+      hh[i] = h[8 * g + i];
+    }
+    const uint32_t w = e2m1_sr_pack8(yy, hh);
+    for (int i = 0; i < 8; ++i) codes[8 * g + i] = (uint8_t)((w >> (4 * i)) & 0xFu);
+  }
 }
 
 template <int FMT>
@@ -205,10 +215,10 @@ int nvfp4_test_e2m1_rne_range(uint32_t first, int64_t n, uint8_t* codes, void* s
 }
 
 int nvfp4_test_e2m1_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, void* stream) {
-  if (n < 0 || (n > 0 && (!y || !h || !codes))) return NVFP4_ERR_INVALID;
+  if (n < 0 || n % 8 != 0 || (n > 0 && (!y || !h || !codes))) return NVFP4_ERR_INVALID;
   if (n == 0) return NVFP4_OK;
-  hipLaunchKernelGGL(test_e2m1_sr_kernel, dim3(test_grid(n)), dim3(256), 0, (hipStream_t)stream,
-                     y, h, n, codes);
+  hipLaunchKernelGGL(test_e2m1_sr_kernel, dim3(test_grid(n / 8)), dim3(256), 0,
+                     (hipStream_t)stream, y, h, n, codes);
   return status_of(hipGetLastError());
 }
 

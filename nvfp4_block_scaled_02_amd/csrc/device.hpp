@@ -134,22 +134,44 @@ __host__ __device__ inline uint32_t sr_key(uint64_t seed, uint32_t idx_hi) {
   return h;
 }
 
-// Stochastic rounding of y onto E2M1 with the 32-bit variate h: |y| goes up
-// to the next grid point iff u = (h >> 8) * 2^-24 < p, p = (|y| - lo)/step.
-// Within a binade of the grid (step 0.5 below 2, 1 below 4, 2 below 6) the
-// scaled value t = |y| / step is exact, so p = t - floor(t) is exact.
-__device__ __forceinline__ uint32_t e2m1_sr_code(float y, uint32_t h) {
-  const float a = fabsf(y);
-  const bool b2 = a < 2.0f, b4 = a < 4.0f;
-  const float inv_step = b2 ? 2.0f : (b4 ? 1.0f : 0.5f);
-  const uint32_t off = b2 ? 0u : (b4 ? 2u : 4u);
-  const float t = a * inv_step;
-  const float fl = __builtin_floorf(t);
-  const float p = t - fl;
-  const float u = (float)(h >> 8) * 0x1p-24f;
-  uint32_t k = (uint32_t)fl + (u < p ? 1u : 0u) + off;
-  k = a >= 6.0f ? 7u : k;
-  return ((__float_as_uint(y) >> 28) & 8u) | k;
+// Stochastic rounding onto E2M1 with gfx950 v_cvt_scalef32_sr_pk_fp4_f32
+// (unit scale).  Measured rule: the element in the low nibble goes up iff
+// (r >> 10) + floor(p * 2^22) >= 2^22, p = (|y| - lo) / (hi - lo), r the
+// random word; |y| >= 6 saturates; the sign is kept.  The high-nibble element
+// uses bits [9, 31) of r instead.  So that every element sees only its own
+// hash h (variate h >> 10), each element gets its own instruction: even
+// elements as the low-nibble source with r = h, odd elements as the
+// high-nibble source with r = h >> 1, and one bitfield select merges them.
+//
+// The instruction writes only the selected byte of its destination and keeps
+// the other three (checked on the hardware), but the compiler's builtin for
+// it does not tie the destination to the `old` operand; it is therefore
+// issued here as inline assembly with a read-write destination.
+template <int SEL>
+__device__ __forceinline__ uint32_t sr_fp4_into(uint32_t old, float v, uint32_t r) {
+  const uint64_t src = ((uint64_t)__float_as_uint(v) << 32) | __float_as_uint(v);
+  if constexpr (SEL == 0)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(old) : "v"(src), "v"(r));
+  else if constexpr (SEL == 1)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(old) : "v"(src), "v"(r));
+  else if constexpr (SEL == 2)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(old) : "v"(src), "v"(r));
+  else
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(old) : "v"(src), "v"(r));
+  return old;
+}
+
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float (&y)[8], const uint32_t (&h)[8]) {
+  uint32_t we = h[0], wo = h[1];  // placeholders: all bytes are written
+  we = sr_fp4_into<0>(we, y[0], h[0]);
+  wo = sr_fp4_into<0>(wo, y[1], h[1] >> 1);
+  we = sr_fp4_into<1>(we, y[2], h[2]);
+  wo = sr_fp4_into<1>(wo, y[3], h[3] >> 1);
+  we = sr_fp4_into<2>(we, y[4], h[4]);
+  wo = sr_fp4_into<2>(wo, y[5], h[5] >> 1);
+  we = sr_fp4_into<3>(we, y[6], h[6]);
+  wo = sr_fp4_into<3>(wo, y[7], h[7] >> 1);
+  return (we & 0x0F0F0F0Fu) | (wo & 0xF0F0F0F0u);
 }
 
 // ---------------------------------------------------------------- scales

@@ -94,10 +94,10 @@ __device__ __forceinline__ HalfOut quantize_half(uint4 w, const f32x2* tab, cons
     if constexpr (ROUND == ROUND_RNE) {
       o.codes = e2m1_rne_pack8(y);
     } else {
-      uint32_t cw = 0;
+      uint32_t h[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) cw |= e2m1_sr_code(y[i], fmix32((idx0_lo + i) ^ key)) << (4 * i);
-      o.codes = cw;
+      for (int i = 0; i < 8; ++i) h[i] = fmix32((idx0_lo + i) ^ key);
+      o.codes = e2m1_sr_pack8(y, h);
     }
     o.scale = c6;
     o.four = 0;
@@ -136,14 +136,17 @@ __device__ __forceinline__ uint32_t key_for(uint64_t seed, uint64_t idx, uint32_
 }
 
 // Adds the per-lane 4/6 counts of the workgroup to *count4 (one atomic).
+// Same-address device atomics serialize (about 8 ns each on MI355X), so the
+// launchers keep the grid of a counting launch to about one workgroup per CU.
+template <int BLOCK>
 __device__ __forceinline__ void flush_count(unsigned long long* count4, uint32_t n4) {
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t red[BLOCK / 64];
   for (int off = 32; off >= 1; off >>= 1) n4 += (uint32_t)__shfl_xor((int)n4, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = n4;
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned long long t = 0;
-    for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+    for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
     if (t) atomicAdd(count4, t);
   }
 }
@@ -156,10 +159,9 @@ __device__ __forceinline__ void flush_count(unsigned long long* count4, uint32_t
 // instructions per 8 elements for Four-Over-Six), so nothing is spent on
 // gathering scale bytes into wider stores.
 constexpr int kRowUnroll = 4;
-constexpr int64_t kRowTile = (int64_t)kThreads * kRowUnroll;
 
-template <int FMT, int SELECT, int ROUND>
-__global__ void __launch_bounds__(kThreads)
+template <int FMT, int SELECT, int ROUND, int BLOCK>
+__global__ void __launch_bounds__(BLOCK)
 quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* __restrict__ amax,
                      float sg, uint64_t seed, uint32_t key0, uint32_t* __restrict__ codes,
                      uint8_t* __restrict__ scales, unsigned long long* count4) {
@@ -167,18 +169,19 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
   const TensorScale ts = tensor_scale(*amax, sg);
   build_table<FMT>(tab, ts.alpha);
   __syncthreads();
+  constexpr int64_t kTileChunks = (int64_t)BLOCK * kRowUnroll;
   const bool even = (threadIdx.x & 1) == 0;
   uint32_t n4 = 0;
-  const int64_t per_iter = (int64_t)gridDim.x * kRowTile;
-  const int64_t nfull = (nchunks / kRowTile) * kRowTile;
-  int64_t base = (int64_t)blockIdx.x * kRowTile;
+  const int64_t per_iter = (int64_t)gridDim.x * kTileChunks;
+  const int64_t nfull = (nchunks / kTileChunks) * kTileChunks;
+  int64_t base = (int64_t)blockIdx.x * kTileChunks;
   for (; base < nfull; base += per_iter) {
     uint4 w[kRowUnroll];
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) w[u] = ld_nt(x + base + u * kThreads + threadIdx.x);
+    for (int u = 0; u < kRowUnroll; ++u) w[u] = ld_nt(x + base + u * BLOCK + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
-      const int64_t ch = base + u * kThreads + threadIdx.x;
+      const int64_t ch = base + u * BLOCK + threadIdx.x;
       const uint64_t idx0 = (uint64_t)ch * kChunk;
       const uint32_t key = ROUND == ROUND_SR ? key_for(seed, idx0, key0) : 0u;
       const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, key, (uint32_t)idx0);
@@ -191,12 +194,12 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
     uint4 w[kRowUnroll];
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
-      const int64_t ch = base + u * kThreads + threadIdx.x;
+      const int64_t ch = base + u * BLOCK + threadIdx.x;
       w[u] = ch < nchunks ? ld_nt(x + ch) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
-      const int64_t ch = base + u * kThreads + threadIdx.x;
+      const int64_t ch = base + u * BLOCK + threadIdx.x;
       const uint64_t idx0 = (uint64_t)ch * kChunk;
       const uint32_t key = ROUND == ROUND_SR ? key_for(seed, idx0, key0) : 0u;
       const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, key, (uint32_t)idx0);
@@ -207,7 +210,7 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
       }
     }
   }
-  if (SELECT == SELECT_4OVER6 && count4) flush_count(count4, n4);
+  if (SELECT == SELECT_4OVER6 && count4) flush_count<BLOCK>(count4, n4);
 }
 
 // ---------------------------------------------------------------- column-wise
@@ -293,7 +296,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
     }
     __syncthreads();  // the tile is rewritten by the next iteration
   }
-  if (SELECT == SELECT_4OVER6 && count4) flush_count(count4, n4);
+  if (SELECT == SELECT_4OVER6 && count4) flush_count<kThreads>(count4, n4);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -301,19 +304,31 @@ template <int FMT, int SELECT, int ROUND>
 static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int cus = device_cu_count();
+  const bool counting = a.select == SELECT_4OVER6 && a.count4 != nullptr;
   if (a.axes == AXIS_ROW) {
     const int64_t nchunks = a.rows * a.cols / kChunk;
-    int64_t grid = (nchunks + kRowTile - 1) / kRowTile;
-    const int64_t cap = (int64_t)cus * 8;
-    grid = grid < cap ? grid : cap;
-    hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), nchunks, a.amax,
-                       a.sg, a.seed, key0, reinterpret_cast<uint32_t*>(a.codes), a.scales,
-                       a.count4);
+    if (counting) {
+      // one 1024-thread workgroup per CU: at most one atomic per CU
+      constexpr int B = 1024;
+      int64_t grid = (nchunks + (int64_t)B * kRowUnroll - 1) / ((int64_t)B * kRowUnroll);
+      grid = grid < cus ? grid : cus;
+      hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, B>), dim3((unsigned)grid),
+                         dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nchunks, a.amax,
+                         a.sg, a.seed, key0, reinterpret_cast<uint32_t*>(a.codes), a.scales,
+                         a.count4);
+    } else {
+      int64_t grid = (nchunks + (int64_t)kThreads * kRowUnroll - 1) / ((int64_t)kThreads * kRowUnroll);
+      const int64_t cap = (int64_t)cus * 8;
+      grid = grid < cap ? grid : cap;
+      hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, kThreads>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), nchunks,
+                         a.amax, a.sg, a.seed, key0, reinterpret_cast<uint32_t*>(a.codes),
+                         a.scales, a.count4);
+    }
     return hipGetLastError();
   }
   const int64_t ntiles = ((a.rows + kTile - 1) / kTile) * ((a.cols + kTile - 1) / kTile);
-  const int64_t cap = (int64_t)cus * 8;
+  const int64_t cap = (int64_t)cus * (counting ? 2 : 8);
   const int64_t grid = ntiles < cap ? ntiles : cap;
   if (a.axes == (AXIS_ROW | AXIS_COL)) {
     hipLaunchKernelGGL((quantize_tiles_kernel<FMT, SELECT, ROUND, true>), dim3((unsigned)grid),

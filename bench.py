@@ -94,6 +94,18 @@ class Timer:
         return e0.elapsed_time(e1) / reps * 1e3
 
 
+def profile_once(torch, dev, launches, nsets):
+    """One 256 MiB copy (the reference for the PMC byte counters), then each
+    launch of the step on two buffer sets, in step order."""
+    big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    torch.empty_like(big).copy_(big)
+    for i in range(2):
+        for f in launches:
+            f(i % nsets)
+    torch.cuda.synchronize()
+    log(f"profile-once done: one 256 MiB copy, {len(launches)} launches x 2")
+
+
 def kernel_entry(us, n, bpe):
     gbps = n * bpe / (us * 1e-6) / 1e9
     return {"us": round(us, 3), "bytes_per_elem": round(bpe, 4), "gbps": round(gbps, 1),
@@ -172,13 +184,12 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
     xh = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(nsets)]
     gm = nv.default_global_max("e4m3", "4over6")
     if args.profile_once:
-        big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(big)
-        dst.copy_(big)
-        for i in range(4):
-            nv.quantize(xs[i], amaxs[i], select="4over6", out=outs[i])
-        torch.cuda.synchronize()
-        log("profile-once done: one 256 MiB copy, 4 quantize launches")
+        sse1 = torch.zeros(1, dtype=torch.float64, device=dev)
+        profile_once(torch, dev, [
+            lambda i: nv.tensor_amax(xs[i], out=amaxs[i]),
+            lambda i: nv.quantize(xs[i], amaxs[i], select="4over6", out=outs[i]),
+            lambda i: nv.dequantize(outs[i]["codes"], outs[i]["scales"], amaxs[i], global_max=gm,
+                                    x_ref=xs[i], sse=sse1, out=xh[i])], nsets)
         return None
     total = args.warmup + args.steps
     sse = torch.zeros(total, dtype=torch.float64, device=dev)
@@ -347,6 +358,16 @@ def run_gradient(args, torch, np, nv, synth, dev, timer):
              "codes_t": torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev),
              "scales_t": torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev)}
             for _ in range(nsets)]
+    if args.profile_once:
+        profile_once(torch, dev, [
+            lambda i: nv.quantize(xs[i], stale, fmt="ue5m3", select="6", rounding="sr",
+                                  axes="both", seed=1234, out=outs[i]),
+            lambda i: nv.quantize(xs[i], stale, fmt="ue5m3", select="6", rounding="sr", axes="row",
+                                  seed=1234, out={"codes": outs[i]["codes"], "scales": outs[i]["scales"]}),
+            lambda i: nv.quantize(xs[i], stale, fmt="ue5m3", select="6", rounding="sr", axes="col",
+                                  seed=1234, out={"codes_t": outs[i]["codes_t"],
+                                                  "scales_t": outs[i]["scales_t"]})], nsets)
+        return None
     reps = max(args.steps, 20)
     us = {
         "quantize_fused_row_col_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
@@ -381,7 +402,7 @@ def main():
                     choices=["activation", "weight-1k", "weight", "qat", "gradient"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
-                    help="run a 256 MiB copy and a few quantize launches for PMC counters")
+                    help="run a 256 MiB copy and each kernel of the workload twice (for PMC counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -5,10 +5,11 @@
 // each lane streams 16-byte chunks with non-temporal loads, four in flight,
 // folding them with packed 16-bit integer max on the sign-cleared patterns
 // (integer order = magnitude order; NaN > inf > finite).  The workgroup
-// reduces through cross-lane shuffles and LDS, and one integer atomicMax per
-// workgroup lands the result as the float whose bits are (pattern << 16):
-// same-address atomics serialize, so the grid is kept to one workgroup per
-// CU.  A one-lane kernel clears the result first.
+// reduces through cross-lane shuffles and LDS, and at most one integer
+// atomicMax per workgroup lands the result as the float whose bits are
+// (pattern << 16): same-address atomics (and coherent reads) serialize, at
+// several nanoseconds each on MI355X, so the grid is kept to one workgroup
+// per CU.  A one-lane kernel clears the result first.
 #include "common.hpp"
 #include "device.hpp"
 
@@ -63,7 +64,11 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const uint4* __restr
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
     for (int w2 = 1; w2 < kAmaxThreads / 64; ++w2) r = r > red[w2] ? r : red[w2];
-    atomicMax(out, r << 16);
+    // The running maximum only grows, so a workgroup whose maximum it
+    // already covers skips its atomic; the coherent read costs less than a
+    // same-address atomic.  A stale read is smaller and only costs the atomic.
+    const uint32_t cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((r << 16) > cur) atomicMax(out, r << 16);
   }
 }
 

@@ -52,13 +52,11 @@ __global__ void test_e2m1_range_kernel(uint32_t first, int64_t n, uint8_t* codes
 __global__ void test_e2m1_sr_kernel(const float* y, const uint32_t* h, int64_t n, uint8_t* codes) {
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n / 8;
        g += (int64_t)gridDim.x * blockDim.x) {
-    float yy[8];
+    f32x2 yp[4];
     uint32_t hh[8];
-    for (int i = 0; i < 8; ++i) {
-      yy[i] = y[8 * g + i];
-      hh[i] = h[8 * g + i];
-    }
-    const uint32_t w = e2m1_sr_pack8(yy, hh);
+    for (int b = 0; b < 4; ++b) yp[b] = f32x2{y[8 * g + 2 * b], y[8 * g + 2 * b + 1]};
+    for (int i = 0; i < 8; ++i) hh[i] = h[8 * g + i];
+    const uint32_t w = e2m1_sr_pack8(yp, hh, 0u, 0u);
     for (int i = 0; i < 8; ++i) codes[8 * g + i] = (uint8_t)((w >> (4 * i)) & 0xFu);
   }
 }

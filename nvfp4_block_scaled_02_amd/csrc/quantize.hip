@@ -19,6 +19,8 @@
 // 64x64 tile is read once, optionally quantized row-wise from registers,
 // transposed through LDS with a 16-byte-chunk XOR swizzle (conflict-free
 // 16-bit writes, 128-bit reads), and quantized again column-wise.
+#include <atomic>
+
 #include "common.hpp"
 #include "device.hpp"
 
@@ -69,12 +71,13 @@ __device__ __forceinline__ float half_sse(uint32_t packed, const float (&x)[8], 
 }
 
 // Quantize the lane's half block.  Every lane of the wavefront must call it
-// (DPP partner exchange).  idx0 = output-orientation index of element 0 of
-// this half (stochastic rounding only); key = counter-hash key of its high
-// word.
+// (DPP partner exchange).  Stochastic rounding only: hbase = lo32(idx0) ^ key,
+// idx0 being the output-orientation index of element 0 of this half and key
+// the counter-hash key of its high word.  idx0 is a multiple of 8, so element
+// i's hash input lo32(idx0 + i) ^ key equals hbase ^ i.
 template <int FMT, int SELECT, int ROUND>
 __device__ __forceinline__ HalfOut quantize_half(uint4 w, const f32x2* tab, const TensorScale& ts,
-                                                 uint32_t key, uint32_t idx0_lo) {
+                                                 uint32_t hbase) {
   const float x[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                       bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
   // block amax: IEEE 754-2019 maximum (v_maximum3_f32, NaN-propagating) of
@@ -88,16 +91,20 @@ __device__ __forceinline__ HalfOut quantize_half(uint4 w, const f32x2* tab, cons
   if constexpr (SELECT == SELECT_6) {
     const uint32_t c6 = encode_pair(FMT, a * ts.k6, 0.0f) & 0xFFu;
     const f32x2 t = tab[c6];
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
     if constexpr (ROUND == ROUND_RNE) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
       o.codes = e2m1_rne_pack8(y);
     } else {
+      f32x2 yp[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) yp[b] = f32x2{x[2 * b] * t[1], x[2 * b + 1] * t[1]};
+      const uint32_t t = hbase ^ (hbase >> 16);  // shared first step of fmix32
       uint32_t h[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = fmix32((idx0_lo + i) ^ key);
-      o.codes = e2m1_sr_pack8(y, h);
+      for (int i = 0; i < 8; ++i) h[i] = fmix32_tail(t ^ (uint32_t)i);
+      o.codes = e2m1_sr_pack8(yp, h, __float_as_uint(x[0]), __float_as_uint(x[1]));
     }
     o.scale = c6;
     o.four = 0;
@@ -130,9 +137,15 @@ __device__ __forceinline__ HalfOut quantize_half(uint4 w, const f32x2* tab, cons
   return o;
 }
 
-__device__ __forceinline__ uint32_t key_for(uint64_t seed, uint64_t idx, uint32_t key0) {
-  const uint32_t hi = (uint32_t)(idx >> 32);
-  return hi == 0 ? key0 : sr_key(seed, hi);
+// Hash base of the 8 elements from index idx0 (a multiple of 8).  WIDE: the
+// tensor has more than 2^32 elements, so the key depends on the high word;
+// otherwise every index has high word 0 and key0 serves.
+template <int ROUND, bool WIDE>
+__device__ __forceinline__ uint32_t hash_base(uint64_t seed, uint64_t idx0, uint32_t key0) {
+  if constexpr (ROUND != ROUND_SR) return 0u;
+  const uint32_t hi = (uint32_t)(idx0 >> 32);
+  const uint32_t key = WIDE ? (hi == 0 ? key0 : sr_key(seed, hi)) : key0;
+  return (uint32_t)idx0 ^ key;
 }
 
 // Adds the per-lane 4/6 counts of the workgroup to *count4 (one atomic).
@@ -160,7 +173,7 @@ __device__ __forceinline__ void flush_count(unsigned long long* count4, uint32_t
 // gathering scale bytes into wider stores.
 constexpr int kRowUnroll = 4;
 
-template <int FMT, int SELECT, int ROUND, int BLOCK>
+template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
 __global__ void __launch_bounds__(BLOCK)
 quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* __restrict__ amax,
                      float sg, uint64_t seed, uint32_t key0, uint32_t* __restrict__ codes,
@@ -182,9 +195,8 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
       const int64_t ch = base + u * BLOCK + threadIdx.x;
-      const uint64_t idx0 = (uint64_t)ch * kChunk;
-      const uint32_t key = ROUND == ROUND_SR ? key_for(seed, idx0, key0) : 0u;
-      const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, key, (uint32_t)idx0);
+      const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)ch * kChunk, key0);
+      const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, hb);
       codes[ch] = o.codes;
       if (even) scales[ch >> 1] = (uint8_t)o.scale;
       n4 += even ? o.four : 0u;
@@ -200,9 +212,8 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
       const int64_t ch = base + u * BLOCK + threadIdx.x;
-      const uint64_t idx0 = (uint64_t)ch * kChunk;
-      const uint32_t key = ROUND == ROUND_SR ? key_for(seed, idx0, key0) : 0u;
-      const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, key, (uint32_t)idx0);
+      const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)ch * kChunk, key0);
+      const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, hb);
       if (ch < nchunks) {
         codes[ch] = o.codes;
         if (even) scales[ch >> 1] = (uint8_t)o.scale;
@@ -214,93 +225,219 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
 }
 
 // ---------------------------------------------------------------- column-wise
-constexpr int kTile = 64;                  // 64 x 64 bf16 tile
-constexpr int kTileChunks = kTile * kTile / kChunk;  // 512 chunks
-constexpr int kPerThread = kTileChunks / kThreads;   // 2
+// Strip walker.  A workgroup owns a strip of kSW columns and walks down it in
+// tiles of kTR rows.  Each tile is read once (16-byte chunks, 256 bytes per
+// row), optionally quantized row-wise from registers (64 code bytes per row
+// and tile: one full 64-byte piece), transposed through LDS and quantized
+// column-wise.  Column-wise outputs are staged in LDS and written as 64-byte
+// pieces per column: codes every kCtTiles tiles, scale bytes every kStTiles
+// tiles (and at the end of the walk).  Pieces below 64 bytes, or 32-byte
+// pieces written at different times, cost extra DRAM writes and bandwidth on
+// MI355X; 4-byte pieces per tile, as an unstaged 64-row tile would write for
+// its scales, run at a fraction of the write bandwidth.
+constexpr int kSW = 128;                        // strip width (columns)
+constexpr int kTR = 32;                         // tile height (rows)
+constexpr int kPer = kSW * kTR / kChunk / kThreads;  // 2 chunks per lane and pass
+constexpr int kCtTiles = 4;                     // codes_t: 4 tiles = 64 bytes per column
+constexpr int kCtWords = kCtTiles * kTR / 8;    // 16 code words per column per stage
+constexpr int kCtPitch = kCtWords + 1;          // LDS pitch (words), padded
+constexpr int kStTiles = 32;                    // scales_t: 32 tiles = 64 bytes per column
+constexpr int kStBytes = kStTiles * kTR / 16;   // 64 scale bytes per column per stage
+constexpr int kStPitch = kStBytes + 4;          // LDS pitch (bytes), padded
+static_assert(kPer * kThreads * kChunk == kSW * kTR, "tile split");
 
-// LDS address (in bf16 units) of element (col, row) of the transposed tile:
-// column lines of 64 rows, 16-byte row-chunks XOR-swizzled by col / 8.
+// LDS address (bf16 units) of element (col, row) of the transposed tile:
+// column lines of kTR rows, 16-byte row-chunks XOR-swizzled by col / 8.
 __device__ __forceinline__ int tpos(int col, int row) {
-  return col * kTile + ((((row >> 3) ^ (col >> 3)) & 7) << 3) + (row & 7);
+  return col * kTR + ((((row >> 3) ^ (col >> 3)) & 3) << 3) + (row & 7);
 }
 
-template <int FMT, int SELECT, int ROUND, bool DO_ROW>
+// Load-view position of the lane's chunk in pass u: wavefront wv covers cell
+// u * 4 + wv = 8 rows x 8 chunks (cell / 2 picks the 8 rows, cell % 2 the
+// half row); lane l takes row l / 8 and chunk l % 8 of it.  In the
+// transposing 16-bit LDS writes of one wavefront the 8 chunks then fall on 4
+// swizzle slots and 8 rows: at most two lanes per bank.
+__device__ __forceinline__ int cell_row(int u) {
+  const int cell = u * 4 + (threadIdx.x >> 6);
+  return (cell >> 1) * 8 + ((threadIdx.x & 63) >> 3);
+}
+__device__ __forceinline__ int cell_col(int u) {
+  const int cell = u * 4 + (threadIdx.x >> 6);
+  return ((cell & 1) * 8 + (threadIdx.x & 7)) << 3;
+}
+
+// Writes the staged column-wise bytes of tile rows [t_lo, t_hi) (absolute
+// tile indices within one stage of `stage` tiles) of the strip at c0.  Each
+// staged column holds `bytes_per_tile` bytes per tile; only rows < rows and
+// columns < cols are written.  Consecutive lanes write consecutive bytes (or words) of one column, so a
+// wavefront store covers whole 64-byte pieces.
+__device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __restrict__ codes_t,
+                                              int64_t rows, int64_t cols, int64_t c0,
+                                              int64_t t_lo, int64_t t_hi) {
+  const int64_t row0 = (t_lo / kCtTiles) * kCtTiles * kTR;  // stage origin (rows)
+  const int w_lo = (int)(t_lo % kCtTiles) * (kTR / 8);
+  int64_t w_end = (rows - row0) / 8;  // words (8 rows each) inside the tensor
+  int w_hi = (int)((t_hi - 1) % kCtTiles + 1) * (kTR / 8);
+  if (w_end < w_hi) w_hi = (int)w_end;
+  const int64_t stride = rows >> 1;
+  // rolled: the flush runs once per stage, and unrolling lets the compiler
+  // keep every per-lane address live across the whole walk
+#pragma unroll 1
+  for (int u = 0; u < kSW * kCtWords / kThreads; ++u) {
+    const int j = u * kThreads + threadIdx.x;
+    const int col = j / kCtWords, wd = j % kCtWords;
+    if (wd >= w_lo && wd < w_hi && c0 + col < cols)
+      *reinterpret_cast<uint32_t*>(codes_t + (c0 + col) * stride + (row0 >> 1) + wd * 4) =
+          ct[col * kCtPitch + wd];
+  }
+}
+
+__device__ __forceinline__ void flush_scales_t(const uint8_t* st, uint8_t* __restrict__ scales_t,
+                                               int64_t rows, int64_t cols, int64_t c0,
+                                               int64_t t_lo, int64_t t_hi) {
+  const int64_t row0 = (t_lo / kStTiles) * kStTiles * kTR;
+  const int b_lo = (int)(t_lo % kStTiles) * (kTR / 16);
+  int64_t b_end = (rows - row0) / 16;
+  int b_hi = (int)((t_hi - 1) % kStTiles + 1) * (kTR / 16);
+  if (b_end < b_hi) b_hi = (int)b_end;
+  const int64_t stride = rows >> 4;
+#pragma unroll 1
+  for (int u = 0; u < kSW * kStBytes / kThreads; ++u) {
+    const int j = u * kThreads + threadIdx.x;
+    const int col = j / kStBytes, b = j % kStBytes;
+    if (b >= b_lo && b < b_hi && c0 + col < cols)
+      scales_t[(c0 + col) * stride + (row0 >> 4) + b] = st[col * kStPitch + b];
+  }
+}
+
+// Loads the lane's chunks of the tile at rows r0.., strip c0..; chunks outside
+// the tensor read as zeros.
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t rows,
+                                          int64_t cols, int64_t r0, int64_t c0,
+                                          uint4 (&w)[kPer]) {
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t r = r0 + cell_row(u), c = c0 + cell_col(u);
+    w[u] = (r < rows && c < cols) ? ld_nt(reinterpret_cast<const uint4*>(x + r * cols + c))
+                                  : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Work unit = one strip (kSW columns) over `seg` consecutive tiles, units
+// numbered strip-fastest.  Workgroup b takes units v, v + G, ... (G = grid
+// size, sized by the launcher to what the GPU holds at once) with v
+// renumbering b so that the G/8 workgroups the dispatcher places on one XCD
+// (workgroup b on XCD b mod 8) hold consecutive units: neighbouring strips
+// then share their row-wise cache lines inside one XCD's L2.
+template <int FMT, int SELECT, int ROUND, bool WIDE, bool DO_ROW>
 __global__ void __launch_bounds__(kThreads)
 quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                       const float* __restrict__ amax, float sg, uint64_t seed, uint32_t key0,
                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                       uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
-                      unsigned long long* count4) {
+                      unsigned long long* count4, int64_t seg) {
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kSW * kTR];
+  __shared__ uint32_t ct[kSW * kCtPitch];
+  __shared__ uint8_t st[kSW * kStPitch];
   const TensorScale ts = tensor_scale(*amax, sg);
   build_table<FMT>(tab, ts.alpha);
   __syncthreads();
   const bool even = (threadIdx.x & 1) == 0;
   uint32_t n4 = 0;
-  const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
-  const int64_t ntiles = tiles_r * tiles_c;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t r0 = (t / tiles_c) * kTile, c0 = (t % tiles_c) * kTile;
-    // ---- load (and optionally quantize row-wise) chunks of 8 columns
-    uint4 w[kPerThread];
+  const int64_t tiles_r = (rows + kTR - 1) / kTR, tiles_c = (cols + kSW - 1) / kSW;
+  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  const int64_t v = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  for (int64_t unit = v; unit < units; unit += G) {
+    const int64_t g = unit / tiles_c;
+    const int64_t c0 = (unit - g * tiles_c) * kSW;
+    const int64_t tr0 = g * seg;
+    const int64_t tr1 = tr0 + seg < tiles_r ? tr0 + seg : tiles_r;
+    int64_t ct_lo = tr0, st_lo = tr0;  // first tile of the open stages
+    // load: pass u of wavefront wv covers cell u * 4 + wv, 8 rows x 8 chunks
+    // (half a tile row each: whole 128-byte lines); see cell_row/col.  The
+    // next tile's chunks are requested before the current one is processed.
+    uint4 w[kPer];
+    load_tile(x, rows, cols, tr0 * kTR, c0, w);
+    for (int64_t tr = tr0; tr < tr1; ++tr) {
+      const int64_t r0 = tr * kTR;
+      uint4 wn[kPer];
+      if (tr + 1 < tr1) load_tile(x, rows, cols, r0 + kTR, c0, wn);
+      // ---- row-wise, from registers (the lane pair 2m, 2m+1 holds one block)
+      if constexpr (DO_ROW) {
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int k = u * kThreads + threadIdx.x;  // 8 chunks per tile row
-      const int64_t r = r0 + (k >> 3), c = c0 + ((k & 7) << 3);
-      const bool ok = r < rows && c < cols;
-      w[u] = ok ? ld_nt(reinterpret_cast<const uint4*>(x + r * cols + c))
-                : make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (DO_ROW) {
-#pragma unroll
-      for (int u = 0; u < kPerThread; ++u) {
-        const int k = u * kThreads + threadIdx.x;
-        const int64_t r = r0 + (k >> 3), c = c0 + ((k & 7) << 3);
-        const uint64_t idx0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c;
-        const uint32_t key = ROUND == ROUND_SR ? key_for(seed, idx0, key0) : 0u;
-        const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, key, (uint32_t)idx0);
-        if (r < rows && c < cols) {
-          *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + (c >> 1)) = o.codes;
-          if (even) scales[r * (cols >> 4) + (c >> 4)] = (uint8_t)o.scale;
-          n4 += even ? o.four : 0u;
+        for (int u = 0; u < kPer; ++u) {
+          const int64_t r = r0 + cell_row(u), c = c0 + cell_col(u);
+          const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)c, key0);
+          const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, hb);
+          if (r < rows && c < cols) {
+            *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + (c >> 1)) = o.codes;
+            if (even) scales[r * (cols >> 4) + (c >> 4)] = (uint8_t)o.scale;
+            n4 += even ? o.four : 0u;
+          }
         }
       }
-    }
-    // ---- transpose through LDS
+      // ---- transpose through LDS
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int k = u * kThreads + threadIdx.x;
-      const int row = k >> 3, col = (k & 7) << 3;
-      const uint32_t v[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      for (int u = 0; u < kPer; ++u) {
+        const int row = cell_row(u), col = cell_col(u);
+        const uint32_t e[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        tile[tpos(col + j, row)] = (uint16_t)(v[j >> 1] >> ((j & 1) * 16));
-    }
-    __syncthreads();
-    // ---- column-wise: chunk = 8 consecutive rows of one column
+        for (int j = 0; j < 8; ++j)
+          tile[tpos(col + j, row)] = (uint16_t)(e[j >> 1] >> ((j & 1) * 16));
+      }
+      __syncthreads();
+      // ---- column-wise: chunk k = 8 rows (k % 4) * 8 ..+8 of tile column k / 4
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int k = u * kThreads + threadIdx.x;  // 8 chunks per tile column
-      const int col = k >> 3, rch = k & 7;
-      const uint4 wt = *reinterpret_cast<const uint4*>(tile + tpos(col, rch << 3));
-      const int64_t c = c0 + col, r = r0 + (rch << 3);
-      const uint64_t idx0 = (uint64_t)c * (uint64_t)rows + (uint64_t)r;
-      const uint32_t key = ROUND == ROUND_SR ? key_for(seed, idx0, key0) : 0u;
-      const HalfOut o = quantize_half<FMT, SELECT, ROUND>(wt, tab, ts, key, (uint32_t)idx0);
-      if (r < rows && c < cols) {
-        *reinterpret_cast<uint32_t*>(codes_t + c * (rows >> 1) + (r >> 1)) = o.codes;
-        if (even) scales_t[c * (rows >> 4) + (r >> 4)] = (uint8_t)o.scale;
-        n4 += even ? o.four : 0u;
+      for (int u = 0; u < kPer; ++u) {
+        const int k = u * kThreads + threadIdx.x;
+        const int col = k >> 2, rch = k & 3;
+        const uint4 wt = *reinterpret_cast<const uint4*>(tile + tpos(col, rch << 3));
+        const int64_t c = c0 + col, r = r0 + (rch << 3);
+        const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)c * (uint64_t)rows + (uint64_t)r, key0);
+        const HalfOut o = quantize_half<FMT, SELECT, ROUND>(wt, tab, ts, hb);
+        ct[col * kCtPitch + (int)(tr % kCtTiles) * (kTR / 8) + rch] = o.codes;
+        if (even) st[col * kStPitch + (int)(tr % kStTiles) * (kTR / 16) + (rch >> 1)] = (uint8_t)o.scale;
+        if (r < rows && c < cols) n4 += even ? o.four : 0u;
+      }
+      __syncthreads();  // staged outputs complete; the tile may be rewritten
+      // ---- flush closed stages
+      const bool last = tr + 1 == tr1;
+      if (last || (tr + 1) % kCtTiles == 0) {
+        flush_codes_t(ct, codes_t, rows, cols, c0, ct_lo, tr + 1);
+        ct_lo = tr + 1;
+      }
+      if (last || (tr + 1) % kStTiles == 0) {
+        flush_scales_t(st, scales_t, rows, cols, c0, st_lo, tr + 1);
+        st_lo = tr + 1;
+      }
+      // (the next tile writes the staging buffers only after its first barrier)
+      if (tr + 1 < tr1) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) w[u] = wn[u];
       }
     }
-    __syncthreads();  // the tile is rewritten by the next iteration
   }
   if (SELECT == SELECT_4OVER6 && count4) flush_count<kThreads>(count4, n4);
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int FMT, int SELECT, int ROUND>
+// Workgroups of kThreads lanes of kernel KERN one CU holds at once (its
+// register and LDS use), at least 1; looked up once per kernel.
+template <auto KERN>
+static int resident_per_cu() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERN, kThreads, 0) != hipSuccess || n < 1)
+      n = 1;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int FMT, int SELECT, int ROUND, bool WIDE>
 static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int cus = device_cu_count();
@@ -312,7 +449,7 @@ static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
       constexpr int B = 1024;
       int64_t grid = (nchunks + (int64_t)B * kRowUnroll - 1) / ((int64_t)B * kRowUnroll);
       grid = grid < cus ? grid : cus;
-      hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, B>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, WIDE, B>), dim3((unsigned)grid),
                          dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nchunks, a.amax,
                          a.sg, a.seed, key0, reinterpret_cast<uint32_t*>(a.codes), a.scales,
                          a.count4);
@@ -320,33 +457,41 @@ static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
       int64_t grid = (nchunks + (int64_t)kThreads * kRowUnroll - 1) / ((int64_t)kThreads * kRowUnroll);
       const int64_t cap = (int64_t)cus * 8;
       grid = grid < cap ? grid : cap;
-      hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, kThreads>), dim3((unsigned)grid),
-                         dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), nchunks,
-                         a.amax, a.sg, a.seed, key0, reinterpret_cast<uint32_t*>(a.codes),
-                         a.scales, a.count4);
+      hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, WIDE, kThreads>),
+                         dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         reinterpret_cast<const uint4*>(a.x), nchunks, a.amax, a.sg, a.seed, key0,
+                         reinterpret_cast<uint32_t*>(a.codes), a.scales, a.count4);
     }
     return hipGetLastError();
   }
-  const int64_t ntiles = ((a.rows + kTile - 1) / kTile) * ((a.cols + kTile - 1) / kTile);
-  const int64_t cap = (int64_t)cus * (counting ? 2 : 8);
-  const int64_t grid = ntiles < cap ? ntiles : cap;
-  if (a.axes == (AXIS_ROW | AXIS_COL)) {
-    hipLaunchKernelGGL((quantize_tiles_kernel<FMT, SELECT, ROUND, true>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, s, a.x, a.rows, a.cols, a.amax, a.sg, a.seed, key0,
-                       a.codes, a.scales, a.codes_t, a.scales_t, a.count4);
-  } else {
-    hipLaunchKernelGGL((quantize_tiles_kernel<FMT, SELECT, ROUND, false>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, s, a.x, a.rows, a.cols, a.amax, a.sg, a.seed, key0,
-                       a.codes, a.scales, a.codes_t, a.scales_t, a.count4);
-  }
+  constexpr auto kFused = quantize_tiles_kernel<FMT, SELECT, ROUND, WIDE, true>;
+  constexpr auto kCol = quantize_tiles_kernel<FMT, SELECT, ROUND, WIDE, false>;
+  const bool fused = a.axes == (AXIS_ROW | AXIS_COL);
+  const auto kern = fused ? kFused : kCol;
+  // as many workgroups as the GPU holds at once (fewer when counting: one
+  // atomic each), each walking a strip over `seg` tiles
+  const int64_t tiles_r = (a.rows + kTR - 1) / kTR, tiles_c = (a.cols + kSW - 1) / kSW;
+  const int64_t target =
+      (int64_t)cus * (counting ? 2 : (fused ? resident_per_cu<kFused>() : resident_per_cu<kCol>()));
+  int64_t seg = (tiles_r * tiles_c + target - 1) / target;
+  seg = seg < 1 ? 1 : (seg > tiles_r ? tiles_r : seg);
+  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
+  const int64_t grid = units < target ? units : target;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows, a.cols, a.amax,
+                     a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t, a.count4, seg);
   return hipGetLastError();
 }
 
 template <int FMT>
 static hipError_t launch_fmt(const QuantizeArgs& a, hipStream_t s) {
-  if (a.rounding == ROUND_SR) return launch_typed<FMT, SELECT_6, ROUND_SR>(a, s);
-  if (a.select == SELECT_4OVER6) return launch_typed<FMT, SELECT_4OVER6, ROUND_RNE>(a, s);
-  return launch_typed<FMT, SELECT_6, ROUND_RNE>(a, s);
+  if (a.rounding == ROUND_SR) {
+    // indices reach past 2^32 only in tensors of more than 2^32 elements
+    const bool wide = (uint64_t)a.rows * (uint64_t)a.cols > (1ull << 32);
+    return wide ? launch_typed<FMT, SELECT_6, ROUND_SR, true>(a, s)
+                : launch_typed<FMT, SELECT_6, ROUND_SR, false>(a, s);
+  }
+  if (a.select == SELECT_4OVER6) return launch_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
+  return launch_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
 }
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {

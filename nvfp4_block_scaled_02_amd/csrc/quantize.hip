@@ -137,6 +137,111 @@ __device__ __forceinline__ HalfOut quantize_half(uint4 w, const f32x2* tab, cons
   return o;
 }
 
+// ---------------------------------------------------------------- one lane per block
+struct BlockOut {
+  uint32_t c0, c1;  // codes of elements 0-7 and 8-15, element i in nibble i % 8
+  uint32_t scale;
+  uint32_t four;
+};
+
+// SSE of one candidate over a whole block: four fmaf chains over elements
+// 4k..4k+3 (each from +0), summed as (P0 + P1) + (P2 + P3).
+__device__ __forceinline__ float block_sse(uint32_t w0, uint32_t w1, const float (&x)[16], float S) {
+  float qa[8], qb[8];
+  e2m1_unpack8(w0, qa);
+  e2m1_unpack8(w1, qb);
+  float P[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * k + i;
+      const float d = __builtin_fmaf(-(e < 8 ? qa[e] : qb[e - 8]), S, x[e]);
+      p = __builtin_fmaf(d, d, p);
+    }
+    P[k] = p;
+  }
+  return (P[0] + P[1]) + (P[2] + P[3]);
+}
+
+// Quantize a whole block (chunks a, b) in one lane: no partner exchange and
+// no duplicated scale encode, which the lane-pair form pays for.  hbase as
+// in quantize_half, for element 0 of the block (idx0 a multiple of 16).
+template <int FMT, int SELECT, int ROUND>
+__device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2* tab,
+                                                   const TensorScale& ts, uint32_t hbase) {
+  const float x[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
+                       bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
+                       bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
+                       bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+  float m = __builtin_elementwise_maximum(__builtin_fabsf(x[0]), __builtin_fabsf(x[1]));
+#pragma unroll
+  for (int i = 2; i < 16; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(x[i]));
+  const bool nan_blk = ts.nan || (m != m);
+  BlockOut o;
+  if constexpr (SELECT == SELECT_6) {
+    const uint32_t c6 = encode_pair(FMT, m * ts.k6, 0.0f) & 0xFFu;
+    const f32x2 t = tab[c6];
+    if constexpr (ROUND == ROUND_RNE) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
+      o.c0 = e2m1_rne_pack8(y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t[1];
+      o.c1 = e2m1_rne_pack8(y);
+    } else {
+      const uint32_t tt = hbase ^ (hbase >> 16);  // shared first step of fmix32
+      f32x2 yp[4];
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yp[j] = f32x2{x[2 * j] * t[1], x[2 * j + 1] * t[1]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = fmix32_tail(tt ^ (uint32_t)i);
+      o.c0 = e2m1_sr_pack8(yp, h, __float_as_uint(x[0]), __float_as_uint(x[1]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yp[j] = f32x2{x[8 + 2 * j] * t[1], x[9 + 2 * j] * t[1]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = fmix32_tail(tt ^ (uint32_t)(8 + i));
+      o.c1 = e2m1_sr_pack8(yp, h, __float_as_uint(x[8]), __float_as_uint(x[9]));
+    }
+    o.scale = c6;
+    o.four = 0;
+  } else {
+    const uint32_t cc = encode_pair(FMT, m * ts.k6, m * ts.k4);
+    const uint32_t c6 = cc & 0xFFu, c4 = cc >> 8;
+    const f32x2 t6 = tab[c6], t4 = tab[c4];
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[i] * t6[1];
+    const uint32_t a6 = e2m1_rne_pack8(y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t6[1];
+    const uint32_t b6 = e2m1_rne_pack8(y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[i] * t4[1];
+    const uint32_t a4 = e2m1_rne_pack8(y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t4[1];
+    const uint32_t b4 = e2m1_rne_pack8(y);
+    const float e6 = block_sse(a6, b6, x, t6[0]);
+    const float e4 = block_sse(a4, b4, x, t4[0]);
+    const bool four = e4 < e6;
+    o.c0 = four ? a4 : a6;
+    o.c1 = four ? b4 : b6;
+    o.scale = four ? c4 : c6;
+    o.four = four ? 1u : 0u;
+  }
+  if (nan_blk) {
+    o.c0 = 0;
+    o.c1 = 0;
+    o.scale = FmtTraits<FMT>::kNan;
+    o.four = 0;
+  }
+  return o;
+}
+
 // Hash base of the 8 elements from index idx0 (a multiple of 8).  WIDE: the
 // tensor has more than 2^32 elements, so the key depends on the high word;
 // otherwise every index has high word 0 and key0 serves.
@@ -219,6 +324,79 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
         if (even) scales[ch >> 1] = (uint8_t)o.scale;
         n4 += even ? o.four : 0u;
       }
+    }
+  }
+  if (SELECT == SELECT_4OVER6 && count4) flush_count<BLOCK>(count4, n4);
+}
+
+// Writes the wavefront's 128 chunks (lane l: chunks l and 64 + l) to its LDS
+// region so that lane l can read chunks 2l and 2l + 1 back.  The fences
+// and wave barriers keep the compiler from moving LDS accesses across them
+// (the hardware runs one wavefront's LDS operations in order): the previous
+// group's reads happen before the region is overwritten, the writes before
+// the reads that follow.
+__device__ __forceinline__ void bounce_pair(uint4* reg, int l, uint4 a, uint4 b) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  reg[l] = a;
+  reg[64 + l] = b;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Row-wise, one lane per block (Four-Over-Six and stochastic rounding, whose
+// per-block work dominates).  A wavefront handles groups of 64 blocks (128
+// chunks, 2 KiB): it loads them with two fully coalesced 16-byte loads per
+// lane, bounces them through its own 2 KiB of LDS (no workgroup barrier:
+// LDS operations of one wavefront complete in order) and each lane reads
+// back its two adjacent chunks.  Loading a lane's two chunks directly would
+// leave every load instruction half-dense, which costs about 10% of the
+// memory rate on the max->6 path.  Codes are stored 8 bytes per lane, scale
+// bytes 1 per lane: whole 512- and 64-byte pieces per wavefront.  Register
+// use is held to 64 so that 8 wavefronts per SIMD stay resident.
+template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8)))
+quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float* __restrict__ amax,
+                       float sg, uint64_t seed, uint32_t key0, uint2* __restrict__ codes,
+                       uint8_t* __restrict__ scales, unsigned long long* count4) {
+  __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
+  __shared__ __attribute__((aligned(16))) uint4 stage[BLOCK * 2];
+  const TensorScale ts = tensor_scale(*amax, sg);
+  build_table<FMT>(tab, ts.alpha);
+  __syncthreads();
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint4* reg = stage + wv * 128;  // this wavefront's 2 KiB
+  const int64_t nchunks = nblocks * 2;
+  const int64_t nwhole = nblocks / 64;  // groups of 64 blocks
+  const int64_t nwaves = (int64_t)gridDim.x * (BLOCK / 64);
+  uint32_t n4 = 0;
+  int64_t g = (int64_t)blockIdx.x * (BLOCK / 64) + wv;
+  // whole groups, unchecked
+  for (; g < nwhole; g += nwaves) {
+    const uint4 a = ld_nt(x + g * 128 + l), b = ld_nt(x + g * 128 + 64 + l);
+    bounce_pair(reg, l, a, b);
+    const int64_t bk = g * 64 + l;
+    const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
+    const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
+    codes[bk] = make_uint2(o.c0, o.c1);
+    scales[bk] = (uint8_t)o.scale;
+    n4 += o.four;
+  }
+  // the partial last group (nblocks % 64 blocks), if this wavefront owns it
+  if (g == nwhole && nblocks % 64 != 0) {
+    const int64_t c0 = g * 128;
+    const uint4 a = c0 + l < nchunks ? ld_nt(x + c0 + l) : make_uint4(0, 0, 0, 0);
+    const uint4 b = c0 + 64 + l < nchunks ? ld_nt(x + c0 + 64 + l) : make_uint4(0, 0, 0, 0);
+    bounce_pair(reg, l, a, b);
+    const int64_t bk = g * 64 + l;
+    const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
+    const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
+    if (bk < nblocks) {
+      codes[bk] = make_uint2(o.c0, o.c1);
+      scales[bk] = (uint8_t)o.scale;
+      n4 += o.four;
     }
   }
   if (SELECT == SELECT_4OVER6 && count4) flush_count<BLOCK>(count4, n4);
@@ -443,17 +621,30 @@ static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
   const int cus = device_cu_count();
   const bool counting = a.select == SELECT_4OVER6 && a.count4 != nullptr;
   if (a.axes == AXIS_ROW) {
-    const int64_t nchunks = a.rows * a.cols / kChunk;
-    if (counting) {
-      // one 1024-thread workgroup per CU: at most one atomic per CU
-      constexpr int B = 1024;
-      int64_t grid = (nchunks + (int64_t)B * kRowUnroll - 1) / ((int64_t)B * kRowUnroll);
-      grid = grid < cus ? grid : cus;
-      hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, WIDE, B>), dim3((unsigned)grid),
-                         dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nchunks, a.amax,
-                         a.sg, a.seed, key0, reinterpret_cast<uint32_t*>(a.codes), a.scales,
-                         a.count4);
+    if constexpr (SELECT == SELECT_4OVER6 || ROUND == ROUND_SR) {
+      // one lane per block: these paths are bound by per-block arithmetic
+      const int64_t nblocks = a.rows * a.cols / 16;
+      const int64_t ngroups = (nblocks + 63) / 64;
+      if (counting) {
+        // one 1024-thread workgroup per CU: at most one atomic per CU
+        constexpr int B = 1024;
+        int64_t grid = (ngroups + B / 64 - 1) / (B / 64);
+        grid = grid < cus ? grid : cus;
+        hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, B>), dim3((unsigned)grid),
+                           dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg,
+                           a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+      } else {
+        int64_t grid = (ngroups + kThreads / 64 - 1) / (kThreads / 64);
+        const int64_t cap = (int64_t)cus * 8;
+        grid = grid < cap ? grid : cap;
+        hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, kThreads>),
+                           dim3((unsigned)grid), dim3(kThreads), 0, s,
+                           reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg, a.seed, key0,
+                           reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+      }
     } else {
+      // max->6 with round-to-nearest: the lane-pair stream (no count output)
+      const int64_t nchunks = a.rows * a.cols / kChunk;
       int64_t grid = (nchunks + (int64_t)kThreads * kRowUnroll - 1) / ((int64_t)kThreads * kRowUnroll);
       const int64_t cap = (int64_t)cus * 8;
       grid = grid < cap ? grid : cap;

@@ -6,19 +6,22 @@
 // alpha, encoded to E4M3 or UE5M3; elements rounded onto E2M1; under
 // Four-Over-Six both Q = 6 and Q = 4 are encoded and the lower-SSE one kept.
 //
-// Mapping: a lane owns 8 consecutive elements (one 16-byte bf16 chunk), the
-// lane pair (2m, 2m+1) owns one block; the block amax and the two partial
-// SSEs meet through one DPP quad_perm move each.  Both candidates, their
-// E2M1 codes (v_cvt_scalef32_pk_fp4_f32) and their exact decodes (for the
-// SSE) stay in VGPRs.  Per-code {effective scale, reciprocal} tables live in
-// LDS, built once per workgroup from the device amax.
+// Two block mappings.  One lane per block (quantize_block): the lane holds
+// all 16 elements, both 4/6 candidates, their E2M1 codes
+// (v_cvt_scalef32_pk_fp4_f32) and exact decodes (for the SSE) in VGPRs; used
+// by every path whose per-block arithmetic dominates (Four-Over-Six,
+// stochastic rounding, column-wise).  A lane pair per block (quantize_half):
+// 8 elements per lane, block amax and partial SSEs meeting through one DPP
+// move each; used by the memory-bound row-wise max->6 round-to-nearest
+// stream.  Per-code {effective scale, reciprocal} tables live in LDS, built
+// once per workgroup from the device amax.
 //
-// Row-wise blocks: a flat grid-stride stream over 16-byte chunks (blocks
-// never straddle rows because cols % 16 == 0).  Column-wise blocks (16
-// consecutive rows of a column, written as the row-wise layout of X^T): a
-// 64x64 tile is read once, optionally quantized row-wise from registers,
-// transposed through LDS with a 16-byte-chunk XOR swizzle (conflict-free
-// 16-bit writes, 128-bit reads), and quantized again column-wise.
+// Row-wise blocks: grid-stride streams over the tensor (blocks never
+// straddle rows because cols % 16 == 0).  Column-wise blocks (16 consecutive
+// rows of a column, written as the row-wise layout of X^T): a strip walker
+// that reads each 32 x 128 tile once into LDS, quantizes it row-wise and/or
+// column-wise from there, and stages the column-wise outputs so that they
+// leave as 64-byte pieces.
 #include <atomic>
 
 #include "common.hpp"
@@ -169,12 +172,8 @@ __device__ __forceinline__ float block_sse(uint32_t w0, uint32_t w1, const float
 // no duplicated scale encode, which the lane-pair form pays for.  hbase as
 // in quantize_half, for element 0 of the block (idx0 a multiple of 16).
 template <int FMT, int SELECT, int ROUND>
-__device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2* tab,
-                                                   const TensorScale& ts, uint32_t hbase) {
-  const float x[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                       bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
-                       bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                       bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+__device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const f32x2* tab,
+                                                     const TensorScale& ts, uint32_t hbase) {
   float m = __builtin_elementwise_maximum(__builtin_fabsf(x[0]), __builtin_fabsf(x[1]));
 #pragma unroll
   for (int i = 2; i < 16; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(x[i]));
@@ -240,6 +239,17 @@ __device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2
     o.four = 0;
   }
   return o;
+}
+
+// The block as two 16-byte bf16 chunks.
+template <int FMT, int SELECT, int ROUND>
+__device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2* tab,
+                                                   const TensorScale& ts, uint32_t hbase) {
+  const float x[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
+                       bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
+                       bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
+                       bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+  return quantize_block_x<FMT, SELECT, ROUND>(x, tab, ts, hbase);
 }
 
 // Hash base of the 8 elements from index idx0 (a multiple of 8).  WIDE: the
@@ -405,9 +415,8 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
 // ---------------------------------------------------------------- column-wise
 // Strip walker.  A workgroup owns a strip of kSW columns and walks down it in
 // tiles of kTR rows.  Each tile is read once (16-byte chunks, 256 bytes per
-// row), optionally quantized row-wise from registers (64 code bytes per row
-// and tile: one full 64-byte piece), transposed through LDS and quantized
-// column-wise.  Column-wise outputs are staged in LDS and written as 64-byte
+// row) into LDS, optionally quantized row-wise (64 code bytes per row and
+// tile: one full 64-byte piece) and quantized column-wise.  Column-wise outputs are staged in LDS and written as 64-byte
 // pieces per column: codes every kCtTiles tiles, scale bytes every kStTiles
 // tiles (and at the end of the walk).  Pieces below 64 bytes, or 32-byte
 // pieces written at different times, cost extra DRAM writes and bandwidth on
@@ -415,40 +424,18 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
 // its scales, run at a fraction of the write bandwidth.
 constexpr int kSW = 128;                        // strip width (columns)
 constexpr int kTR = 32;                         // tile height (rows)
-constexpr int kPer = kSW * kTR / kChunk / kThreads;  // 2 chunks per lane and pass
+constexpr int kTilePitch = kSW * 2 + 16;         // LDS row pitch (bytes), padded
 constexpr int kCtTiles = 4;                     // codes_t: 4 tiles = 64 bytes per column
 constexpr int kCtWords = kCtTiles * kTR / 8;    // 16 code words per column per stage
 constexpr int kCtPitch = kCtWords + 1;          // LDS pitch (words), padded
 constexpr int kStTiles = 32;                    // scales_t: 32 tiles = 64 bytes per column
 constexpr int kStBytes = kStTiles * kTR / 16;   // 64 scale bytes per column per stage
 constexpr int kStPitch = kStBytes + 4;          // LDS pitch (bytes), padded
-static_assert(kPer * kThreads * kChunk == kSW * kTR, "tile split");
-
-// LDS address (bf16 units) of element (col, row) of the transposed tile:
-// column lines of kTR rows, 16-byte row-chunks XOR-swizzled by col / 8.
-__device__ __forceinline__ int tpos(int col, int row) {
-  return col * kTR + ((((row >> 3) ^ (col >> 3)) & 3) << 3) + (row & 7);
-}
-
-// Load-view position of the lane's chunk in pass u: wavefront wv covers cell
-// u * 4 + wv = 8 rows x 8 chunks (cell / 2 picks the 8 rows, cell % 2 the
-// half row); lane l takes row l / 8 and chunk l % 8 of it.  In the
-// transposing 16-bit LDS writes of one wavefront the 8 chunks then fall on 4
-// swizzle slots and 8 rows: at most two lanes per bank.
-__device__ __forceinline__ int cell_row(int u) {
-  const int cell = u * 4 + (threadIdx.x >> 6);
-  return (cell >> 1) * 8 + ((threadIdx.x & 63) >> 3);
-}
-__device__ __forceinline__ int cell_col(int u) {
-  const int cell = u * 4 + (threadIdx.x >> 6);
-  return ((cell & 1) * 8 + (threadIdx.x & 7)) << 3;
-}
 
 // Writes the staged column-wise bytes of tile rows [t_lo, t_hi) (absolute
-// tile indices within one stage of `stage` tiles) of the strip at c0.  Each
-// staged column holds `bytes_per_tile` bytes per tile; only rows < rows and
-// columns < cols are written.  Consecutive lanes write consecutive bytes (or words) of one column, so a
-// wavefront store covers whole 64-byte pieces.
+// tile indices within one stage) of the strip at c0.  Only rows < rows and
+// columns < cols are written.  Consecutive lanes write consecutive words (or
+// bytes) of one column, so a wavefront store covers whole 64-byte pieces.
 __device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __restrict__ codes_t,
                                               int64_t rows, int64_t cols, int64_t c0,
                                               int64_t t_lo, int64_t t_hi) {
@@ -488,14 +475,17 @@ __device__ __forceinline__ void flush_scales_t(const uint8_t* st, uint8_t* __res
   }
 }
 
-// Loads the lane's chunks of the tile at rows r0.., strip c0..; chunks outside
-// the tensor read as zeros.
+// Loads the lane's chunks of the tile at rows r0.., strip c0.. (chunk
+// k = u * kThreads + lane: tile row k / 16, columns (k % 16) * 8 ..+8);
+// chunks outside the tensor read as zeros.
+constexpr int kLoads = kSW * kTR / kChunk / kThreads;  // 2
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t rows,
                                           int64_t cols, int64_t r0, int64_t c0,
-                                          uint4 (&w)[kPer]) {
+                                          uint4 (&w)[kLoads]) {
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int64_t r = r0 + cell_row(u), c = c0 + cell_col(u);
+  for (int u = 0; u < kLoads; ++u) {
+    const int k = u * kThreads + threadIdx.x;
+    const int64_t r = r0 + (k >> 4), c = c0 + (k & 15) * 8;
     w[u] = (r < rows && c < cols) ? ld_nt(reinterpret_cast<const uint4*>(x + r * cols + c))
                                   : make_uint4(0, 0, 0, 0);
   }
@@ -507,6 +497,14 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
 // renumbering b so that the G/8 workgroups the dispatcher places on one XCD
 // (workgroup b on XCD b mod 8) hold consecutive units: neighbouring strips
 // then share their row-wise cache lines inside one XCD's L2.
+//
+// Per tile: the lanes load it with coalesced 16-byte loads (issued one tile
+// ahead) and store it into LDS, row-major with a padded pitch
+// (conflict-free 16-byte writes and reads); after a barrier,
+// lane b quantizes row block b (tile row b / 8, columns (b % 8) * 16 ..+16)
+// from two 16-byte LDS reads, and column block b (tile column b % 128, rows
+// (b / 128) * 16 ..+16) from sixteen 16-bit reads; both with the
+// one-lane-per-block quantizer.
 template <int FMT, int SELECT, int ROUND, bool WIDE, bool DO_ROW>
 __global__ void __launch_bounds__(kThreads)
 quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
@@ -514,70 +512,70 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                       uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
                       unsigned long long* count4, int64_t seg) {
+  static_assert(kSW * kTR / 16 == kThreads, "one row block and one column block per lane");
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kSW * kTR];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kTilePitch];
   __shared__ uint32_t ct[kSW * kCtPitch];
   __shared__ uint8_t st[kSW * kStPitch];
   const TensorScale ts = tensor_scale(*amax, sg);
   build_table<FMT>(tab, ts.alpha);
   __syncthreads();
-  const bool even = (threadIdx.x & 1) == 0;
   uint32_t n4 = 0;
   const int64_t tiles_r = (rows + kTR - 1) / kTR, tiles_c = (cols + kSW - 1) / kSW;
   const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
   const int64_t G = gridDim.x, b = blockIdx.x;
   const int64_t v = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int lane = threadIdx.x;
+  const int rb_row = lane >> 3, rb_col = (lane & 7) * 16;  // row block of this lane
+  const int cb_col = lane & (kSW - 1), cb_row = (lane / kSW) * 16;  // column block
   for (int64_t unit = v; unit < units; unit += G) {
     const int64_t g = unit / tiles_c;
     const int64_t c0 = (unit - g * tiles_c) * kSW;
     const int64_t tr0 = g * seg;
     const int64_t tr1 = tr0 + seg < tiles_r ? tr0 + seg : tiles_r;
     int64_t ct_lo = tr0, st_lo = tr0;  // first tile of the open stages
-    // load: pass u of wavefront wv covers cell u * 4 + wv, 8 rows x 8 chunks
-    // (half a tile row each: whole 128-byte lines); see cell_row/col.  The
-    // next tile's chunks are requested before the current one is processed.
-    uint4 w[kPer];
+    // the next tile's chunks are requested before the current one is processed
+    uint4 w[kLoads];
     load_tile(x, rows, cols, tr0 * kTR, c0, w);
     for (int64_t tr = tr0; tr < tr1; ++tr) {
       const int64_t r0 = tr * kTR;
-      uint4 wn[kPer];
+      uint4 wn[kLoads];
       if (tr + 1 < tr1) load_tile(x, rows, cols, r0 + kTR, c0, wn);
-      // ---- row-wise, from registers (the lane pair 2m, 2m+1 holds one block)
-      if constexpr (DO_ROW) {
+      // ---- into LDS, row-major
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          const int64_t r = r0 + cell_row(u), c = c0 + cell_col(u);
-          const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)c, key0);
-          const HalfOut o = quantize_half<FMT, SELECT, ROUND>(w[u], tab, ts, hb);
-          if (r < rows && c < cols) {
-            *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + (c >> 1)) = o.codes;
-            if (even) scales[r * (cols >> 4) + (c >> 4)] = (uint8_t)o.scale;
-            n4 += even ? o.four : 0u;
-          }
-        }
-      }
-      // ---- transpose through LDS
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int row = cell_row(u), col = cell_col(u);
-        const uint32_t e[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          tile[tpos(col + j, row)] = (uint16_t)(e[j >> 1] >> ((j & 1) * 16));
+      for (int u = 0; u < kLoads; ++u) {
+        const int k = u * kThreads + lane;
+        *reinterpret_cast<uint4*>(tile + (k >> 4) * kTilePitch + (k & 15) * 16) = w[u];
       }
       __syncthreads();
-      // ---- column-wise: chunk k = 8 rows (k % 4) * 8 ..+8 of tile column k / 4
+      // ---- row-wise block
+      if constexpr (DO_ROW) {
+        const uint4 wa = *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2);
+        const uint4 wb = *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2 + 16);
+        const int64_t r = r0 + rb_row, c = c0 + rb_col;
+        const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)c, key0);
+        const BlockOut o = quantize_block<FMT, SELECT, ROUND>(wa, wb, tab, ts, hb);
+        if (r < rows && c < cols) {
+          *reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c >> 1)) = make_uint2(o.c0, o.c1);
+          scales[r * (cols >> 4) + (c >> 4)] = (uint8_t)o.scale;
+          n4 += o.four;
+        }
+      }
+      // ---- column-wise block
+      {
+        float xc[16];
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int k = u * kThreads + threadIdx.x;
-        const int col = k >> 2, rch = k & 3;
-        const uint4 wt = *reinterpret_cast<const uint4*>(tile + tpos(col, rch << 3));
-        const int64_t c = c0 + col, r = r0 + (rch << 3);
+        for (int i = 0; i < 16; ++i)
+          xc[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(
+                                      tile + (cb_row + i) * kTilePitch + cb_col * 2) << 16);
+        const int64_t c = c0 + cb_col, r = r0 + cb_row;
         const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)c * (uint64_t)rows + (uint64_t)r, key0);
-        const HalfOut o = quantize_half<FMT, SELECT, ROUND>(wt, tab, ts, hb);
-        ct[col * kCtPitch + (int)(tr % kCtTiles) * (kTR / 8) + rch] = o.codes;
-        if (even) st[col * kStPitch + (int)(tr % kStTiles) * (kTR / 16) + (rch >> 1)] = (uint8_t)o.scale;
-        if (r < rows && c < cols) n4 += even ? o.four : 0u;
+        const BlockOut o = quantize_block_x<FMT, SELECT, ROUND>(xc, tab, ts, hb);
+        const int wd = (int)(tr % kCtTiles) * (kTR / 8) + (cb_row >> 3);
+        ct[cb_col * kCtPitch + wd] = o.c0;
+        ct[cb_col * kCtPitch + wd + 1] = o.c1;
+        st[cb_col * kStPitch + (int)(tr % kStTiles) * (kTR / 16) + (cb_row >> 4)] = (uint8_t)o.scale;
+        if (r < rows && c < cols) n4 += o.four;
       }
       __syncthreads();  // staged outputs complete; the tile may be rewritten
       // ---- flush closed stages
@@ -593,7 +591,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
       // (the next tile writes the staging buffers only after its first barrier)
       if (tr + 1 < tr1) {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) w[u] = wn[u];
+        for (int u = 0; u < kLoads; ++u) w[u] = wn[u];
       }
     }
   }

@@ -33,8 +33,13 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILE_DIR, "quantize_4over6_activation_8192x4096_traffic.json")
-KERNEL_SOURCES = ["quantize.hip", "device.hpp", "common.hpp"]
+TRAFFIC_FILE = os.path.join(PROFILE_DIR, "activation_8192x4096_traffic.json")
+# sources each activation-step kernel is built from (a change voids its PMC bytes)
+KERNEL_SOURCES = {
+    "tensor_amax": ["amax.hip", "device.hpp", "common.hpp"],
+    "quantize_4over6": ["quantize.hip", "device.hpp", "common.hpp"],
+    "dequantize_f32_mse": ["dequantize.hip", "device.hpp", "common.hpp"],
+}
 METRIC = "NVFP4 4/6 quantize GB/s (Gelem/s) at 8192x4096 bf16; % of HBM peak"
 
 # algorithmic bytes per element (read + written, each byte counted once)
@@ -51,23 +56,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "nvfp4_block_scaled_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per quantize launch from the committed PMC summary, if it
-    was taken on the current kernel source; else None."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of an activation-step kernel from the committed
+    PMC summary, if it was taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            t = json.load(f)["kernels"][kernel]
+    except (OSError, ValueError, KeyError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    if t.get("source_sha256") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return t.get("bytes_per_launch")
 
@@ -113,13 +118,17 @@ def kernel_entry(us, n, bpe):
             "gelem_per_s": round(n / (us * 1e-6) / 1e9, 1)}
 
 
-def finish(line, kernels, args, traffic_for=None, traffic=None):
+def finish(line, kernels, args, traffic=None):
+    """traffic: kernel -> measured HBM bytes per launch (or None)."""
+    traffic = traffic or {}
+    for k, v in kernels.items():
+        v["traffic_bytes"] = traffic.get(k)
     dominant = max(kernels, key=lambda k: kernels[k]["us"])
     d = kernels[dominant]
     line["kernels"] = kernels
     line["roofline"] = {"kernel": dominant, "bound": "hbm", "achieved": d["gbps"],
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d["frac_hbm"],
-                        "traffic": traffic if dominant == traffic_for else None}
+                        "traffic": traffic.get(dominant)}
     return line
 
 
@@ -235,11 +244,11 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
                      "256, RNE) -> dequantize to f32 with binary64 MSE report",
                      {"rows": rows, "cols": cols, "elements": n, "step_bytes": int(step_bytes),
                       "buffer_sets": nsets}, n)
-    finish(line, kernels, args, "quantize_4over6", measured_traffic())
+    finish(line, kernels, args, {k: measured_traffic(k) for k in kernels})
     q = kernels["quantize_4over6"]
     line["quantize_roofline"] = {"achieved": q["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": q["frac_hbm"], "gelem_per_s": q["gelem_per_s"],
-                                 "traffic": measured_traffic()}
+                                 "traffic": q["traffic_bytes"]}
     line["mse"] = float(sse[total - 1].item()) / n
     line["amax"] = float(amaxs[(total - 1) % nsets].item())
     if not args.no_cpu_baseline:

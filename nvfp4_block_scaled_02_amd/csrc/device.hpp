@@ -96,9 +96,17 @@ __device__ __forceinline__ double shift1_in_quad_f64(double v) {
 // Exact decode of byte `sel` of a packed word into {low nibble, high nibble}.
 #define NVFP4_DEC_PK_FP4(word, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((word), 1.0f, (sel))
 
+// A register with no defined value, for destinations whose every byte is
+// written before use (the empty asm emits nothing, so no copy is made).
+__device__ __forceinline__ uint32_t scratch_vgpr() {
+  uint32_t w;
+  asm volatile("" : "=v"(w));
+  return w;
+}
+
 // 8 binary32 values -> one dword of 8 nibbles, element i in nibble i.
 __device__ __forceinline__ uint32_t e2m1_rne_pack8(const float (&y)[8]) {
-  uint32_t w = __float_as_uint(y[7]);  // placeholder: all four bytes are written
+  uint32_t w = scratch_vgpr();  // placeholder: all four bytes are written
   w = NVFP4_CVT_PK_FP4(w, y[0], y[1], 0);
   w = NVFP4_CVT_PK_FP4(w, y[2], y[3], 1);
   w = NVFP4_CVT_PK_FP4(w, y[4], y[5], 2);

@@ -171,12 +171,22 @@ __device__ __forceinline__ float block_sse(uint32_t w0, uint32_t w1, const float
 // Quantize a whole block (chunks a, b) in one lane: no partner exchange and
 // no duplicated scale encode, which the lane-pair form pays for.  hbase as
 // in quantize_half, for element 0 of the block (idx0 a multiple of 16).
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  return __builtin_elementwise_maximum(
+      __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)), __builtin_fabsf(c));
+}
+
 template <int FMT, int SELECT, int ROUND>
 __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const f32x2* tab,
                                                      const TensorScale& ts, uint32_t hbase) {
-  float m = __builtin_elementwise_maximum(__builtin_fabsf(x[0]), __builtin_fabsf(x[1]));
-#pragma unroll
-  for (int i = 2; i < 16; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(x[i]));
+  // block amax as a depth-3 tree of v_maximum3_f32 (IEEE maximum is
+  // associative and commutative, NaN included, so the order is immaterial)
+  const float m0 = max3_abs(x[0], x[1], x[2]), m1 = max3_abs(x[3], x[4], x[5]);
+  const float m2 = max3_abs(x[6], x[7], x[8]), m3 = max3_abs(x[9], x[10], x[11]);
+  const float m4 = max3_abs(x[12], x[13], x[14]);
+  const float m = __builtin_elementwise_maximum(
+      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, m1), m2),
+      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m3, m4), __builtin_fabsf(x[15])));
   const bool nan_blk = ts.nan || (m != m);
   BlockOut o;
   if constexpr (SELECT == SELECT_6) {

@@ -77,6 +77,18 @@ def _load():
     lib.or_fakequant_fwd.argtypes = [_f32p, _i64, _i64, _f32p, _f32p, _f32p]
     lib.or_fakequant_bwd.restype = ctypes.c_int
     lib.or_fakequant_bwd.argtypes = [_f32p, _f32p, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p]
+    lib.or_row_amax.restype = ctypes.c_int
+    lib.or_row_amax.argtypes = [_f32p, _i64, _i64, _f32p]
+    lib.or_quantize_rowscaled.restype = ctypes.c_int
+    lib.or_quantize_rowscaled.argtypes = [_f32p, _i64, _i64, _i64, _f32p, ctypes.c_float,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_uint64, _u8p, _u8p, _u64p]
+    lib.or_dequantize_rowscaled.restype = ctypes.c_int
+    lib.or_dequantize_rowscaled.argtypes = [_u8p, _u8p, _i64, _i64, _f32p, ctypes.c_float,
+                                            ctypes.c_int, _f32p, _u16p, _f32p]
+    lib.or_quantize_2d.restype = ctypes.c_int
+    lib.or_quantize_2d.argtypes = [_f32p, _i64, _i64, ctypes.c_float, ctypes.c_float,
+                                   ctypes.c_int, _u8p, _u8p, _u8p, _u8p]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_num_threads.argtypes = []
     _lib = lib
@@ -267,3 +279,86 @@ def unpack_codes(codes):
     out[:, 0::2] = codes & 15
     out[:, 1::2] = codes >> 4
     return out
+
+
+# ---------------------------------------------------------------- per-row outer scales
+def row_amax(x):
+    """A_r = max |x| over each row of a 2-D array (float32 per row)."""
+    xf = as_f32(x)
+    assert xf.ndim == 2
+    out = np.empty(xf.shape[0], np.float32)
+    st = _load().or_row_amax(_ptr(xf, _f32p), xf.shape[0], xf.shape[1], _ptr(out, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle row_amax rejected the arguments (status {st})")
+    return out
+
+
+def quantize_rowscaled(x, row_amaxes, *, fmt=FMT_E4M3, select=SELECT_4OVER6,
+                       rounding=ROUND_RNE, seed=0, global_max=None, row0=0):
+    """Row-wise quantization with a per-row outer scale alpha_r from
+    row_amaxes[r].  Returns (codes, scales, count4)."""
+    xf = as_f32(x)
+    assert xf.ndim == 2
+    rows, cols = xf.shape
+    ra = np.ascontiguousarray(np.asarray(row_amaxes, np.float32))
+    assert ra.shape == (rows,)
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, select) if global_max is None else float(global_max)
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    cnt = np.zeros(1, np.uint64)
+    st = _load().or_quantize_rowscaled(_ptr(xf, _f32p), rows, cols, int(row0), _ptr(ra, _f32p),
+                                       sg, fmt, int(select), int(rounding), int(seed),
+                                       _ptr(codes, _u8p), _ptr(scales, _u8p), _ptr(cnt, _u64p))
+    if st != 0:
+        raise ValueError(f"oracle quantize_rowscaled rejected the arguments (status {st})")
+    return codes, scales, int(cnt[0])
+
+
+def dequantize_rowscaled(codes, scales, row_amaxes, *, fmt=FMT_E4M3, select=SELECT_4OVER6,
+                         global_max=None, want_bf16=False, want_block_scale=False):
+    """x_hat under per-row outer scales; returns float32 [rows, cols] (and the
+    bf16 bits and/or block scales when asked)."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, half = codes.shape
+    cols = half * 2
+    ra = np.ascontiguousarray(np.asarray(row_amaxes, np.float32))
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, select) if global_max is None else float(global_max)
+    out = np.empty((rows, cols), np.float32)
+    bf = np.empty((rows, cols), np.uint16) if want_bf16 else None
+    bs = np.empty((rows, cols // 16), np.float32) if want_block_scale else None
+    st = _load().or_dequantize_rowscaled(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols,
+                                         _ptr(ra, _f32p), sg, fmt, _ptr(out, _f32p),
+                                         _ptr(bf, _u16p), _ptr(bs, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle dequantize_rowscaled rejected the arguments (status {st})")
+    res = [out]
+    if want_bf16:
+        res.append(bf)
+    if want_block_scale:
+        res.append(bs)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---------------------------------------------------------------- 16x16 tile scales
+def quantize_2d(x, amax, *, fmt=FMT_E4M3, global_max=None, want_t=True):
+    """16x16-tile-scaled quantization (max->6, RNE).  Returns (codes, scales)
+    in the row-wise layout and, with want_t, also (codes_t, scales_t) in the
+    column-wise layout of X^T."""
+    xf = as_f32(x)
+    assert xf.ndim == 2
+    rows, cols = xf.shape
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, SELECT_6) if global_max is None else float(global_max)
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    codes_t = np.zeros((cols, rows // 2), np.uint8) if want_t else None
+    scales_t = np.empty((cols, rows // 16), np.uint8) if want_t else None
+    st = _load().or_quantize_2d(_ptr(xf, _f32p), rows, cols, float(amax), sg, fmt,
+                                _ptr(codes, _u8p), _ptr(scales, _u8p), _ptr(codes_t, _u8p),
+                                _ptr(scales_t, _u8p))
+    if st != 0:
+        raise ValueError(f"oracle quantize_2d rejected the arguments (status {st})")
+    return (codes, scales, codes_t, scales_t) if want_t else (codes, scales)

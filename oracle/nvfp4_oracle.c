@@ -350,6 +350,91 @@ int or_quantize(const float *x, int64_t rows, int64_t cols, int64_t row0, float 
 }
 
 /* ------------------------------------------------------------------ */
+/* Per-row outer scales ([E2E] Recipe details: per-token outer scales when
+ * quantizing activations, per-expert ones for weights).  Row r has its own
+ * FP32 outer scale alpha_r = A_r / (6 * S_g), A_r = max |x| over row r (NaN
+ * and infinity rules as for the tensor amax).  Everything else is the
+ * per-tensor method with A replaced by A_r, so row r is quantized exactly as
+ * or_quantize quantizes a one-row tensor holding that row (SR indices keep the
+ * row's global position).  A per-expert outer scale is the per-tensor method
+ * applied to each expert's matrix. */
+int or_row_amax(const float *x, int64_t rows, int64_t cols, float *row_amax) {
+  if (rows < 0 || cols < 0) return OR_EINVAL;
+  for (int64_t r = 0; r < rows; ++r) row_amax[r] = or_tensor_amax(x + r * cols, cols);
+  return OR_OK;
+}
+
+int or_quantize_rowscaled(const float *x, int64_t rows, int64_t cols, int64_t row0,
+                          const float *row_amax, float sg, int fmt, int select, int rounding,
+                          uint64_t seed, uint8_t *codes, uint8_t *scales, uint64_t *count4) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  const int64_t nb = cols / 16;
+  int bad = 0;
+  uint64_t n4 = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(+ : n4) reduction(| : bad)
+  for (int64_t r = 0; r < rows; ++r) {
+    uint64_t c4 = 0;
+    bad |= or_quantize(x + r * cols, 1, cols, row0 + r, row_amax[r], sg, fmt, select, rounding,
+                       seed, codes + r * (cols / 2), scales + r * nb, &c4, NULL, NULL);
+    n4 += c4;
+  }
+  if (bad) return OR_EINVAL;
+  if (count4) *count4 += n4;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* 16x16 tile scales ([E2E] Block-scaled backward passes): one block scale per
+ * square 16x16 tile, from the tile's amax, shared by the tile's 16 row-wise
+ * (1x16) blocks and its 16 column-wise (16x1) blocks, so that the column-wise
+ * quantization is exactly the transpose of the row-wise one (w_q equals the
+ * transpose of (w^T)_q, bit for bit).  Max->6, round-to-nearest-even: the
+ * weights path ([E2E] Recipe details forgoes 4/6 for weights).  Requires rows
+ * and cols to be multiples of 16.  Outputs the row-wise layout (codes[rows,
+ * cols/2], scales[rows, cols/16]: every row block carries its tile's code)
+ * and, if codes_t is given, the column-wise layout of X^T (codes_t[cols,
+ * rows/2], scales_t[cols, rows/16]).  NaN rules as or_quantize, per tile. */
+int or_quantize_2d(const float *x, int64_t rows, int64_t cols, float amax, float sg, int fmt,
+                   uint8_t *codes, uint8_t *scales, uint8_t *codes_t, uint8_t *scales_t) {
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return OR_EINVAL;
+  if (fmt != OR_FMT_E4M3 && fmt != OR_FMT_UE5M3) return OR_EINVAL;
+  const int64_t tr_n = rows / 16, tc_n = cols / 16;
+  float alpha = or_alpha(amax, sg);
+  or_consts *c = (or_consts *)malloc(sizeof(or_consts));
+  if (!isnan(alpha)) make_consts(c, fmt, alpha);
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < tr_n * tc_n; ++t) {
+    const int64_t r0 = (t / tc_n) * 16, c0 = (t % tc_n) * 16;
+    float at = 0.0f;
+    int nan_t = isnan(alpha);
+    for (int i = 0; i < 16; ++i)
+      for (int j = 0; j < 16; ++j) {
+        float v = x[(r0 + i) * cols + c0 + j];
+        if (isnan(v)) nan_t = 1;
+        else if (fabsf(v) > at) at = fabsf(v);
+      }
+    int code = nan_t ? or_scale_nan_code(fmt) : scale_encode_tab(c->dec, c->maxc, at * c->k6);
+    float I = nan_t ? 0.0f : c->inv[code];
+    for (int i = 0; i < 16; ++i) {
+      scales[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)code;
+      if (scales_t) scales_t[(c0 + i) * (rows / 16) + r0 / 16] = (uint8_t)code;
+      for (int j = 0; j < 16; ++j) {
+        const int64_t r = r0 + i, cc = c0 + j;
+        int n = nan_t ? 0 : or_e2m1_code(x[r * cols + cc] * I);
+        uint8_t *b = &codes[r * (cols / 2) + cc / 2];
+        *b = (uint8_t)((cc & 1) ? ((*b & 0x0F) | (n << 4)) : ((*b & 0xF0) | n));
+        if (codes_t) {
+          uint8_t *bt = &codes_t[cc * (rows / 2) + r / 2];
+          *bt = (uint8_t)((r & 1) ? ((*bt & 0x0F) | (n << 4)) : ((*bt & 0xF0) | n));
+        }
+      }
+    }
+  }
+  free(c);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* Dequantization: x_hat = q * D[scale code] * alpha ([E2E] Low-precision
  * formats: fp4 value x fp8 block scale x fp32 outer scale), the product taken
  * exactly in binary64 and rounded once to binary32; a NaN scale code gives
@@ -390,6 +475,21 @@ int or_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int
     }
   }
   return OR_OK;
+}
+
+/* Dequantization under per-row outer scales: row r uses alpha_r. */
+int or_dequantize_rowscaled(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int64_t cols, const float *row_amax, float sg, int fmt,
+                            float *out_f32, uint16_t *out_bf16, float *block_scale) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  const int64_t nb = cols / 16;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+  for (int64_t r = 0; r < rows; ++r)
+    bad |= or_dequantize(codes + r * (cols / 2), scales + r * nb, 1, cols, row_amax[r], sg, fmt,
+                         out_f32 ? out_f32 + r * cols : NULL, out_bf16 ? out_bf16 + r * cols : NULL,
+                         block_scale ? block_scale + r * nb : NULL);
+  return bad ? OR_EINVAL : OR_OK;
 }
 
 /* Sum of squared errors sum (x_i - x_hat_i)^2 in binary64, in index order

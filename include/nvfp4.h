@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -194,6 +194,71 @@ int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const flo
 int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
                         const float* s_pre, const float* s_post, float* grad_x,
                         float* grad_s_pre, float* grad_s_post, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Per-row outer scales ("End-to-End 4-Bit Training", Recipe details:
+ * per-token outer scales when quantizing activations).  Row r has its own
+ * FP32 outer scale alpha_r = row_amax[r] / (6 * S_g); every other step is the
+ * per-tensor method with A replaced by row_amax[r], so a row's result does
+ * not depend on any other row (batch invariance).  A per-expert outer scale
+ * is the per-tensor calls applied to each expert's matrix.
+ *
+ * nvfp4_row_amax -- row_amax[r] = max |x[r, c]| over the row, with the rules
+ * of nvfp4_tensor_amax per row (any NaN -> NaN; else an infinity -> +inf; an
+ * empty row -> 0).
+ *   x         [rows, cols] bf16, 16-byte aligned, cols % 16 == 0.
+ *   row_amax  [rows] float, 4-byte aligned; written.
+ * Errors: NULL pointers with rows > 0, misalignment, cols % 16 != 0 ->
+ * NVFP4_ERR_INVALID.
+ */
+int nvfp4_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* row_amax, void* stream);
+
+/*
+ * nvfp4_quantize_rowscaled -- row-wise NVFP4 quantization with per-row
+ * outer scales (as nvfp4_quantize with axes = ROW, A_r in place of A).
+ *   row_amax  [rows] float on the device (from nvfp4_row_amax, or stale).
+ *   Other arguments and errors as nvfp4_quantize; codes / scales / count4 as
+ *   there.  A row whose amax is negative or non-finite gets the NaN scale
+ *   code in every block and element code 0.  SR uses the row-major element
+ *   index r * cols + c.
+ */
+int nvfp4_quantize_rowscaled(const uint16_t* x, int64_t rows, int64_t cols, const float* row_amax,
+                             float global_fp8_max, int scale_fmt, int select, int rounding,
+                             uint64_t seed, uint8_t* codes, uint8_t* scales,
+                             unsigned long long* count4, void* stream);
+
+/*
+ * nvfp4_dequantize_rowscaled -- nvfp4_dequantize with per-row outer scales:
+ * x_hat = q * D * alpha_r.  Arguments, outputs and errors as
+ * nvfp4_dequantize, with row_amax[rows] in place of amax.
+ */
+int nvfp4_dequantize_rowscaled(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                               int64_t cols, const float* row_amax, float global_fp8_max,
+                               int scale_fmt, float* out_f32, uint16_t* out_bf16,
+                               float* block_scale_out, const uint16_t* x_ref, double* sse_out,
+                               void* stream);
+
+/* ---------------------------------------------------------------------
+ * nvfp4_quantize_2d -- 16x16 tile scales ("End-to-End 4-Bit Training",
+ * Block-scaled backward passes): one block scale per square 16x16 tile, from
+ * the tile's amax, shared by the tile's 16 row blocks and 16 column blocks,
+ * so the column-wise codes are bit for bit the transpose of the row-wise ones.
+ * Max->6 and round-to-nearest-even (the weights path).  Per-tensor outer
+ * scale from *amax as in nvfp4_quantize.
+ *   x          [rows, cols] bf16, rows % 16 == 0, cols % 16 == 0.
+ *   codes      [rows, cols/2], scales [rows, cols/16] (every row block holds
+ *              its tile's code); 16- and 4-byte aligned.
+ *   codes_t    [cols, rows/2], scales_t [cols, rows/16]: the layout of X^T;
+ *              both NULL to skip, else codes_t 16-byte aligned.
+ * NaN rules: a non-finite or negative amax -> NaN scale code everywhere and
+ * codes 0; a tile holding a NaN element -> its scale is the NaN code and its
+ * codes 0.
+ * Errors: NULL / misaligned outputs, shape not a multiple of 16, unknown
+ * scale_fmt, only one of codes_t / scales_t -> NVFP4_ERR_INVALID.
+ */
+int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                      float global_fp8_max, int scale_fmt, uint8_t* codes, uint8_t* scales,
+                      uint8_t* codes_t, uint8_t* scales_t, void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(int status);

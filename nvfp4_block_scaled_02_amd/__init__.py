@@ -4,8 +4,10 @@ The computation lives in libnvfp4.so (hand-written HIP kernels behind the C
 ABI of include/nvfp4.h); this package is its Python binding.  Importing it
 does not load the library; the first call does, and raises if it is not built.
 """
-from .api import (Quantized, default_global_max, dequantize, fakequant_bwd, fakequant_fwd,
-                  quantize, tensor_amax)
+from .api import (Quantized, default_global_max, dequantize, dequantize_rowscaled,
+                  fakequant_bwd, fakequant_fwd, quantize, quantize_2d, quantize_rowscaled,
+                  row_amax, tensor_amax)
 
-__all__ = ["Quantized", "default_global_max", "dequantize", "fakequant_bwd", "fakequant_fwd",
-           "quantize", "tensor_amax"]
+__all__ = ["Quantized", "default_global_max", "dequantize", "dequantize_rowscaled",
+           "fakequant_bwd", "fakequant_fwd", "quantize", "quantize_2d", "quantize_rowscaled",
+           "row_amax", "tensor_amax"]

@@ -32,6 +32,12 @@ SIGNATURES = {
                               _vp, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_dequantize": (_int, [_vp, _vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp, _vp, _vp,
                                 _vp]),
+    "nvfp4_row_amax": (_int, [_vp, _i64, _i64, _vp, _vp]),
+    "nvfp4_quantize_rowscaled": (_int, [_vp, _i64, _i64, _vp, _f32, _int, _int, _int, _u64,
+                                        _vp, _vp, _vp, _vp]),
+    "nvfp4_dequantize_rowscaled": (_int, [_vp, _vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp,
+                                          _vp, _vp, _vp]),
+    "nvfp4_quantize_2d": (_int, [_vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_fakequant_fwd": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_fakequant_bwd": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_test_e2m1_rne_range": (_int, [_u32, _i64, _vp, _vp]),

@@ -114,7 +114,8 @@ def quantize(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: str =
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
                global_max: float, fmt: str = "e4m3", out_dtype=torch.float32,
                want_block_scale: bool = False, x_ref: Optional[torch.Tensor] = None,
-               sse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+               sse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               _entry: str = "nvfp4_dequantize"):
     """x_hat = q * D[scale] * alpha.  Returns x_hat (or None if out_dtype is
     None), plus the per-block effective scales if asked, plus the binary64
     SSE tensor if x_ref is given (sse is added to if passed)."""
@@ -141,17 +142,109 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
         if sse is None:
             sse = torch.zeros(1, dtype=torch.float64, device=dev)
         _need(sse, torch.float64, "sse")
-    st = N.lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), rows, cols, _ptr(amax),
+    st = getattr(N.lib(), _entry)(_ptr(codes), _ptr(scales), rows, cols, _ptr(amax),
                                   float(global_max), _FMT[fmt], _ptr(of32), _ptr(ob16), _ptr(bs),
                                   _ptr(x_ref), _ptr(sse) if x_ref is not None else None,
                                   _stream(dev))
-    N.check(st, "nvfp4_dequantize")
+    N.check(st, _entry)
     res = [out]
     if want_block_scale:
         res.append(bs)
     if x_ref is not None:
         res.append(sse)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---------------------------------------------------------------- per-row outer scales
+def row_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """max |x| over each row of a 2-D bf16 tensor, as float32 [rows]."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, "out")
+    N.check(N.lib().nvfp4_row_amax(_ptr(x), rows, cols, _ptr(out), _stream(x.device)),
+            "nvfp4_row_amax")
+    return out
+
+
+def quantize_rowscaled(x: torch.Tensor, row_amaxes: Optional[torch.Tensor] = None, *,
+                       fmt: str = "e4m3", select: str = "4over6", rounding: str = "rne",
+                       seed: int = 0, global_max: float = 0.0, count4: bool = False,
+                       out: Optional[dict] = None) -> Quantized:
+    """Row-wise NVFP4 quantization with a per-row outer scale (per-token
+    scaling); row_amaxes defaults to row_amax(x).  Quantized.amax holds the
+    per-row amaxes."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if row_amaxes is None:
+        row_amaxes = row_amax(x)
+    _need(row_amaxes, torch.float32, "row_amaxes")
+    dev = x.device
+    out = dict(out or {})
+    out.setdefault("codes", torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev))
+    out.setdefault("scales", torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev))
+    if count4 and "count4" not in out:
+        out["count4"] = torch.zeros(1, dtype=torch.int64, device=dev)
+    _need(out["codes"], torch.uint8, "codes")
+    _need(out["scales"], torch.uint8, "scales")
+    if "count4" in out:
+        _need(out["count4"], torch.int64, "count4")
+    st = N.lib().nvfp4_quantize_rowscaled(
+        _ptr(x), rows, cols, _ptr(row_amaxes), float(global_max), _FMT[fmt], _SELECT[select],
+        _ROUND[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out["codes"]), _ptr(out["scales"]),
+        _ptr(out.get("count4")), _stream(dev))
+    N.check(st, "nvfp4_quantize_rowscaled")
+    gm = float(global_max) if global_max else default_global_max(fmt, select)
+    return Quantized(out["codes"], out["scales"], None, None, row_amaxes, gm, fmt,
+                     out.get("count4"))
+
+
+def dequantize_rowscaled(codes: torch.Tensor, scales: torch.Tensor, row_amaxes: torch.Tensor, *,
+                         global_max: float, fmt: str = "e4m3", out_dtype=torch.float32,
+                         want_block_scale: bool = False, x_ref: Optional[torch.Tensor] = None,
+                         sse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """dequantize() with per-row outer scales (row_amaxes [rows])."""
+    return dequantize(codes, scales, row_amaxes, global_max=global_max, fmt=fmt,
+                      out_dtype=out_dtype, want_block_scale=want_block_scale, x_ref=x_ref,
+                      sse=sse, out=out, _entry="nvfp4_dequantize_rowscaled")
+
+
+# ---------------------------------------------------------------- 16x16 tile scales
+def quantize_2d(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: str = "e4m3",
+                global_max: float = 0.0, transpose: bool = True,
+                out: Optional[dict] = None) -> Quantized:
+    """NVFP4 with one block scale per 16x16 tile (max->6, RNE): the row-wise
+    layout and, with transpose, the column-wise layout of X^T, whose codes are
+    the transpose of the row-wise ones."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if amax is None:
+        amax = tensor_amax(x)
+    _need(amax, torch.float32, "amax")
+    dev = x.device
+    out = dict(out or {})
+    out.setdefault("codes", torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev))
+    out.setdefault("scales", torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev))
+    if transpose:
+        out.setdefault("codes_t", torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev))
+        out.setdefault("scales_t", torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev))
+    for k in ("codes", "scales", "codes_t", "scales_t"):
+        if k in out:
+            _need(out[k], torch.uint8, k)
+    st = N.lib().nvfp4_quantize_2d(
+        _ptr(x), rows, cols, _ptr(amax), float(global_max), _FMT[fmt], _ptr(out["codes"]),
+        _ptr(out["scales"]), _ptr(out.get("codes_t")), _ptr(out.get("scales_t")), _stream(dev))
+    N.check(st, "nvfp4_quantize_2d")
+    gm = float(global_max) if global_max else default_global_max(fmt, "6")
+    return Quantized(out["codes"], out["scales"], out.get("codes_t"), out.get("scales_t"), amax,
+                     gm, fmt, None)
 
 
 def fakequant_fwd(x: torch.Tensor, s_pre: torch.Tensor, s_post: Optional[torch.Tensor] = None,

@@ -72,6 +72,50 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const uint4* __restr
   }
 }
 
+// Per-row amax (per-token outer scales, "End-to-End 4-Bit Training", Recipe
+// details).  A wavefront owns whole rows: its lanes stream the row's 16-byte
+// chunks (four in flight), fold them with the same packed 16-bit integer max
+// on sign-cleared patterns, reduce across the wavefront and lane 0 stores the
+// row's float.  No atomics.  cols % 16 == 0, so a row is whole chunks.
+constexpr int kRowAmaxUnroll = 4;
+
+__global__ void __launch_bounds__(kThreads) row_amax_kernel(const uint4* __restrict__ x, int64_t rows,
+                                                           int64_t row_chunks, float* __restrict__ out) {
+  const int l = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows; r += nwaves) {
+    const uint4* xr = x + r * row_chunks;
+    uint32_t m = 0;
+    int64_t i = l;
+    for (; i + (kRowAmaxUnroll - 1) * 64 < row_chunks; i += kRowAmaxUnroll * 64) {
+      uint4 w[kRowAmaxUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowAmaxUnroll; ++u) w[u] = ld_nt(xr + i + u * 64);
+#pragma unroll
+      for (int u = 0; u < kRowAmaxUnroll; ++u) {
+        const uint32_t v = chunk_abs_max_bits(w[u]);
+        m = m > v ? m : v;
+      }
+    }
+    for (; i < row_chunks; i += 64) {
+      const uint32_t v = chunk_abs_max_bits(ld_nt(xr + i));
+      m = m > v ? m : v;
+    }
+    m = wave_max_u32(m);
+    if (l == 0) out[r] = __uint_as_float(m << 16);
+  }
+}
+
+hipError_t launch_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* out, hipStream_t s) {
+  const int64_t per_wg = kThreads / 64;  // rows in flight per workgroup
+  int64_t grid = (rows + per_wg - 1) / per_wg;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  grid = grid < cap ? grid : cap;
+  hipLaunchKernelGGL(row_amax_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     reinterpret_cast<const uint4*>(x), rows, cols / kChunk, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipStream_t s) {
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
   hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(64), 0, s, o);

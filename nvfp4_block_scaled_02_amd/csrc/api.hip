@@ -105,6 +105,12 @@ const char* nvfp4_status_string(int status) {
   }
 }
 
+static float resolve_sg(float global_fp8_max, int scale_fmt, int select) {
+  if (global_fp8_max != 0.0f) return global_fp8_max;
+  if (scale_fmt == NVFP4_SCALE_UE5M3) return NVFP4_GLOBAL_MAX_UE5M3;
+  return select == NVFP4_SELECT_4OVER6 ? NVFP4_GLOBAL_MAX_E4M3_4OVER6 : NVFP4_GLOBAL_MAX_E4M3;
+}
+
 int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* stream) {
   if (numel < 0 || !amax_out) return NVFP4_ERR_INVALID;
   if (numel > 0 && (!x || !aligned16(x))) return NVFP4_ERR_INVALID;
@@ -134,13 +140,9 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* a
   }
   if (!aligned16(x) || ((uintptr_t)amax & 3u) || ((uintptr_t)count4 & 7u)) return NVFP4_ERR_INVALID;
   if (rows == 0 || cols == 0) return NVFP4_OK;
-  float sg = global_fp8_max;
-  if (sg == 0.0f) {
-    if (scale_fmt == NVFP4_SCALE_UE5M3) sg = NVFP4_GLOBAL_MAX_UE5M3;
-    else sg = select == NVFP4_SELECT_4OVER6 ? NVFP4_GLOBAL_MAX_E4M3_4OVER6 : NVFP4_GLOBAL_MAX_E4M3;
-  }
   QuantizeArgs a;
-  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax; a.sg = sg;
+  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax;
+  a.sg = resolve_sg(global_fp8_max, scale_fmt, select);
   a.fmt = scale_fmt; a.select = select; a.rounding = rounding; a.axes = axes; a.seed = seed;
   a.codes = codes; a.scales = scales; a.codes_t = codes_t; a.scales_t = scales_t;
   a.count4 = count4;
@@ -163,8 +165,83 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
   DequantizeArgs a;
   a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = amax;
   a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32; a.out_bf16 = out_bf16;
-  a.block_scale = block_scale_out; a.x_ref = x_ref; a.sse = sse_out;
+  a.block_scale = block_scale_out; a.x_ref = x_ref; a.sse = sse_out; a.row_scaled = false;
   return status_of(launch_dequantize(a, (hipStream_t)stream));
+}
+
+int nvfp4_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* row_amax, void* stream) {
+  if (!size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
+  if (rows > 0 && (!x || !row_amax || !aligned16(x) || ((uintptr_t)row_amax & 3u)))
+    return NVFP4_ERR_INVALID;
+  if (rows == 0) return NVFP4_OK;
+  return status_of(launch_row_amax(x, rows, cols, row_amax, (hipStream_t)stream));
+}
+
+int nvfp4_quantize_rowscaled(const uint16_t* x, int64_t rows, int64_t cols, const float* row_amax,
+                             float global_fp8_max, int scale_fmt, int select, int rounding,
+                             uint64_t seed, uint8_t* codes, uint8_t* scales,
+                             unsigned long long* count4, void* stream) {
+  if (!x || !row_amax || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (select != NVFP4_SELECT_6 && select != NVFP4_SELECT_4OVER6) return NVFP4_ERR_INVALID;
+  if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
+  if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (!codes || !scales || !aligned16(codes) || ((uintptr_t)scales & 3u)) return NVFP4_ERR_INVALID;
+  if (!aligned16(x) || ((uintptr_t)row_amax & 3u) || ((uintptr_t)count4 & 7u))
+    return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  QuantizeArgs a;
+  a.x = x; a.rows = rows; a.cols = cols; a.amax = row_amax;
+  a.sg = resolve_sg(global_fp8_max, scale_fmt, select);
+  a.fmt = scale_fmt; a.select = select; a.rounding = rounding; a.axes = AXIS_ROW; a.seed = seed;
+  a.codes = codes; a.scales = scales; a.codes_t = nullptr; a.scales_t = nullptr;
+  a.count4 = count4;
+  return status_of(launch_quantize_rowscaled(a, (hipStream_t)stream));
+}
+
+int nvfp4_dequantize_rowscaled(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                               int64_t cols, const float* row_amax, float global_fp8_max,
+                               int scale_fmt, float* out_f32, uint16_t* out_bf16,
+                               float* block_scale_out, const uint16_t* x_ref, double* sse_out,
+                               void* stream) {
+  if (!codes || !scales || !row_amax || !size_ok(rows, cols) || cols % 16 != 0)
+    return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if ((x_ref == nullptr) != (sse_out == nullptr)) return NVFP4_ERR_INVALID;
+  if (!aligned16(codes) || !aligned16(out_f32) || !aligned16(out_bf16) || !aligned16(x_ref))
+    return NVFP4_ERR_INVALID;
+  if (((uintptr_t)row_amax & 3u) || ((uintptr_t)block_scale_out & 3u) || ((uintptr_t)sse_out & 7u))
+    return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  DequantizeArgs a;
+  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = row_amax;
+  a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32; a.out_bf16 = out_bf16;
+  a.block_scale = block_scale_out; a.x_ref = x_ref; a.sse = sse_out; a.row_scaled = true;
+  return status_of(launch_dequantize(a, (hipStream_t)stream));
+}
+
+int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                      float global_fp8_max, int scale_fmt, uint8_t* codes, uint8_t* scales,
+                      uint8_t* codes_t, uint8_t* scales_t, void* stream) {
+  if (!x || !amax || !size_ok(rows, cols) || rows % 16 != 0 || cols % 16 != 0)
+    return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (!codes || !scales || !aligned16(codes) || ((uintptr_t)scales & 3u)) return NVFP4_ERR_INVALID;
+  if ((codes_t == nullptr) != (scales_t == nullptr)) return NVFP4_ERR_INVALID;
+  if (codes_t && !aligned16(codes_t)) return NVFP4_ERR_INVALID;
+  if (!aligned16(x) || ((uintptr_t)amax & 3u)) return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  QuantizeArgs a;
+  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax;
+  a.sg = resolve_sg(global_fp8_max, scale_fmt, NVFP4_SELECT_6);
+  a.fmt = scale_fmt; a.select = SELECT_6; a.rounding = ROUND_RNE;
+  a.axes = codes_t ? (AXIS_ROW | AXIS_COL) : AXIS_ROW; a.seed = 0;
+  a.codes = codes; a.scales = scales; a.codes_t = codes_t; a.scales_t = scales_t;
+  a.count4 = nullptr;
+  return status_of(launch_quantize_2d(a, (hipStream_t)stream));
 }
 
 static int fq_common(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre) {

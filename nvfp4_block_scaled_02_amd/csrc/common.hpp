@@ -39,6 +39,7 @@ struct DequantizeArgs {
   float* block_scale;
   const uint16_t* x_ref;
   double* sse;
+  bool row_scaled;  // amax points to one amax per row (per-row outer scales)
 };
 
 struct FakeQuantArgs {
@@ -53,6 +54,11 @@ struct FakeQuantArgs {
 // Launchers (one translation unit each); return the hipError_t of the launch.
 hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipStream_t s);
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
+hipError_t launch_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* out, hipStream_t s);
+// a.amax = one amax per row
+hipError_t launch_quantize_rowscaled(const QuantizeArgs& a, hipStream_t s);
+// 16x16 tile scales (max->6, RNE); a.axes = ROW or ROW | COL
+hipError_t launch_quantize_2d(const QuantizeArgs& a, hipStream_t s);
 hipError_t launch_dequantize(const DequantizeArgs& a, hipStream_t s);
 hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s);
 hipError_t launch_fakequant_bwd(const FakeQuantArgs& a, hipStream_t s);

@@ -1,5 +1,6 @@
 // dequantize.hip -- NVFP4 -> binary32 / bf16 ("End-to-End 4-Bit Training",
-// "Low-precision formats on Blackwell": value = fp4 x fp8 x fp32).
+// "Low-precision formats on Blackwell": value = fp4 x fp8 x fp32; per-row
+// fp32 outer scales: Recipe details).
 //
 // x_hat = (q * D) * alpha: q * D is exact in binary32 (2 + 4 significant
 // bits), so the second product is the correctly rounded q * D * alpha.  q
@@ -35,15 +36,17 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return v != v ? ((b >> 16) | 0x40u) : r;
 }
 
-template <int FMT, bool F32, bool BF16, bool BSC, bool SSE, int BLOCK>
+// ROWSC: amax holds one amax per row (per-row outer scales); each quad lies in
+// one row (cols % 16 == 0) and takes that row's alpha.
+template <int FMT, bool F32, bool BF16, bool BSC, bool SSE, int BLOCK, bool ROWSC>
 __global__ void __launch_bounds__(BLOCK)
 dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                   int64_t nquads, const float* __restrict__ amax, float sg,
                   float4* __restrict__ out_f32, uint2* __restrict__ out_bf16,
                   float* __restrict__ block_scale, const uint2* __restrict__ x_ref,
-                  double* sse) {
-  const TensorScale ts = tensor_scale(*amax, sg);
-  const float alpha = ts.nan ? __builtin_nanf("") : ts.alpha;
+                  double* sse, int64_t quads_per_row) {
+  const float alpha_t = ROWSC ? 0.0f : outer_alpha(*amax, sg);
+  const bool narrow = (nquads >> 32) == 0;  // quad indices fit 32 bits
   const bool lead4 = (threadIdx.x & 3) == 0;
   double acc = 0.0;
   const int64_t per_iter = (int64_t)gridDim.x * BLOCK * kDqUnroll;
@@ -62,6 +65,12 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
     for (int u = 0; u < kDqUnroll; ++u) {
       const int64_t qd = base + u * BLOCK + threadIdx.x;
       if (qd >= nquads) continue;
+      float alpha = alpha_t;
+      if constexpr (ROWSC) {
+        const int64_t r = narrow ? (int64_t)((uint32_t)qd / (uint32_t)quads_per_row)
+                                 : qd / quads_per_row;
+        alpha = outer_alpha(amax[r], sg);
+      }
       const float D = decode_scale(FMT, sc[u]);
       const f32x2 q01 = NVFP4_DEC_PK_FP4(cw[u], 0), q23 = NVFP4_DEC_PK_FP4(cw[u], 1);
       const float v[4] = {(q01[0] * D) * alpha, (q01[1] * D) * alpha, (q23[0] * D) * alpha,
@@ -96,20 +105,26 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
   }
 }
 
-template <int FMT, bool F32, bool BF16, bool BSC, bool SSE>
-static hipError_t launch_dq(const DequantizeArgs& a, hipStream_t s) {
+template <int FMT, bool F32, bool BF16, bool BSC, bool SSE, bool ROWSC>
+static hipError_t launch_dq_rs(const DequantizeArgs& a, hipStream_t s) {
   constexpr int BLOCK = SSE ? 1024 : kThreads;
   const int64_t nquads = a.rows * a.cols / 4;
   const int64_t per_wg = (int64_t)BLOCK * kDqUnroll;
   int64_t grid = (nquads + per_wg - 1) / per_wg;
   const int64_t cap = (int64_t)device_cu_count() * (SSE ? 1 : 8);
   grid = grid < cap ? grid : cap;
-  hipLaunchKernelGGL((dequantize_kernel<FMT, F32, BF16, BSC, SSE, BLOCK>), dim3((unsigned)grid),
-                     dim3(BLOCK), 0, s, reinterpret_cast<const uint16_t*>(a.codes), a.scales,
-                     nquads, a.amax, a.sg, reinterpret_cast<float4*>(a.out_f32),
-                     reinterpret_cast<uint2*>(a.out_bf16), a.block_scale,
-                     reinterpret_cast<const uint2*>(a.x_ref), a.sse);
+  hipLaunchKernelGGL((dequantize_kernel<FMT, F32, BF16, BSC, SSE, BLOCK, ROWSC>),
+                     dim3((unsigned)grid), dim3(BLOCK), 0, s,
+                     reinterpret_cast<const uint16_t*>(a.codes), a.scales, nquads, a.amax, a.sg,
+                     reinterpret_cast<float4*>(a.out_f32), reinterpret_cast<uint2*>(a.out_bf16),
+                     a.block_scale, reinterpret_cast<const uint2*>(a.x_ref), a.sse, a.cols / 4);
   return hipGetLastError();
+}
+
+template <int FMT, bool F32, bool BF16, bool BSC, bool SSE>
+static hipError_t launch_dq(const DequantizeArgs& a, hipStream_t s) {
+  return a.row_scaled ? launch_dq_rs<FMT, F32, BF16, BSC, SSE, true>(a, s)
+                      : launch_dq_rs<FMT, F32, BF16, BSC, SSE, false>(a, s);
 }
 
 template <int FMT, bool F32, bool BF16, bool BSC>

@@ -260,6 +260,13 @@ struct TensorScale {
   bool nan;
 };
 
+// Outer scale alpha = A / (6 S_g) (1 for A = 0); NaN when A is negative or
+// not finite (no usable scale).
+__device__ __forceinline__ float outer_alpha(float amax, float sg) {
+  if (!(amax >= 0.0f) || __builtin_isinf(amax)) return __builtin_nanf("");
+  return amax == 0.0f ? 1.0f : amax / (6.0f * sg);
+}
+
 __device__ __forceinline__ TensorScale tensor_scale(float amax, float sg) {
   TensorScale t;
   t.nan = !(amax >= 0.0f) || __builtin_isinf(amax);

@@ -262,6 +262,50 @@ __device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2
   return quantize_block_x<FMT, SELECT, ROUND>(x, tab, ts, hbase);
 }
 
+// A block (16 values in one lane) quantized with a given block amax instead
+// of its own: 16x16 tile scales, where every row and column block of a tile
+// takes the tile's amax.  Max->6, round-to-nearest-even; a NaN amax (a NaN
+// in the tile) gives the NaN scale code and codes 0.
+template <int FMT>
+__device__ __forceinline__ BlockOut quantize_block_amax(const float (&x)[16], const f32x2* tab,
+                                                        const TensorScale& ts, float amax_t) {
+  BlockOut o;
+  const uint32_t c6 = encode_pair(FMT, amax_t * ts.k6, 0.0f) & 0xFFu;
+  const f32x2 t = tab[c6];
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
+  o.c0 = e2m1_rne_pack8(y);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t[1];
+  o.c1 = e2m1_rne_pack8(y);
+  o.scale = c6;
+  o.four = 0;
+  if (ts.nan || amax_t != amax_t) {
+    o.c0 = 0;
+    o.c1 = 0;
+    o.scale = FmtTraits<FMT>::kNan;
+  }
+  return o;
+}
+
+// NaN-propagating maximum of |x| over a block (a depth-3 tree of maximum3).
+__device__ __forceinline__ float block_absmax(const float (&x)[16]) {
+  const float m0 = max3_abs(x[0], x[1], x[2]), m1 = max3_abs(x[3], x[4], x[5]);
+  const float m2 = max3_abs(x[6], x[7], x[8]), m3 = max3_abs(x[9], x[10], x[11]);
+  const float m4 = max3_abs(x[12], x[13], x[14]);
+  return __builtin_elementwise_maximum(
+      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, m1), m2),
+      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m3, m4), __builtin_fabsf(x[15])));
+}
+
+__device__ __forceinline__ void unpack16(uint4 a, uint4 b, float (&x)[16]) {
+  x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x); x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
+  x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z); x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
+  x[8] = bf16_lo(b.x); x[9] = bf16_hi(b.x); x[10] = bf16_lo(b.y); x[11] = bf16_hi(b.y);
+  x[12] = bf16_lo(b.z); x[13] = bf16_hi(b.z); x[14] = bf16_lo(b.w); x[15] = bf16_hi(b.w);
+}
+
 // Hash base of the 8 elements from index idx0 (a multiple of 8).  WIDE: the
 // tensor has more than 2^32 elements, so the key depends on the high word;
 // otherwise every index has high word 0 and key0 serves.
@@ -422,6 +466,50 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
   if (SELECT == SELECT_4OVER6 && count4) flush_count<BLOCK>(count4, n4);
 }
 
+// ---------------------------------------------------------------- per-row outer scales
+// Row-wise quantization with per-row outer scales ("End-to-End 4-Bit
+// Training", Recipe details: per-token outer scales for activations).  A
+// workgroup owns one row at a time: it forms alpha_r from the row's amax,
+// builds the row's {S_EFF, INV_S} table in LDS, and its wavefronts take the
+// row's groups of 64 blocks through the same LDS bounce and one-lane
+// quantizer as quantize_blocks_kernel.
+template <int FMT, int SELECT, int ROUND, bool WIDE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+quantize_rowscaled_kernel(const uint4* __restrict__ x, int64_t rows, int64_t cols,
+                          const float* __restrict__ row_amax, float sg, uint64_t seed,
+                          uint32_t key0, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                          unsigned long long* count4) {
+  __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
+  __shared__ __attribute__((aligned(16))) uint4 stage[kThreads * 2];
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint4* reg = stage + wv * 128;  // this wavefront's 2 KiB
+  const int64_t nb = cols / 16, nch = cols / kChunk;  // blocks and chunks per row
+  const int64_t ngroups = (nb + 63) / 64;
+  uint32_t n4 = 0;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const TensorScale ts = tensor_scale(row_amax[r], sg);
+    __syncthreads();  // the previous row's table reads are done
+    build_table<FMT>(tab, ts.alpha);
+    __syncthreads();
+    const uint4* xr = x + r * nch;
+    for (int64_t g = wv; g < ngroups; g += kThreads / 64) {
+      const int64_t c0 = g * 128;
+      const uint4 a = c0 + l < nch ? ld_nt(xr + c0 + l) : make_uint4(0, 0, 0, 0);
+      const uint4 b = c0 + 64 + l < nch ? ld_nt(xr + c0 + 64 + l) : make_uint4(0, 0, 0, 0);
+      bounce_pair(reg, l, a, b);
+      const int64_t bk = g * 64 + l;
+      const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)bk * 16, key0);
+      const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
+      if (bk < nb) {
+        codes[r * nb + bk] = make_uint2(o.c0, o.c1);
+        scales[r * nb + bk] = (uint8_t)o.scale;
+        n4 += o.four;
+      }
+    }
+  }
+  if (SELECT == SELECT_4OVER6 && count4) flush_count<kThreads>(count4, n4);
+}
+
 // ---------------------------------------------------------------- column-wise
 // Strip walker.  A workgroup owns a strip of kSW columns and walks down it in
 // tiles of kTR rows.  Each tile is read once (16-byte chunks, 256 bytes per
@@ -501,6 +589,14 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
   }
 }
 
+// Amax of 16x16 tile t from its 16 row-block values in LDS (NaN-propagating).
+__device__ __forceinline__ float tile_amax(const float* am, int t) {
+  const float4* p = reinterpret_cast<const float4*>(am + t * 16);
+  const float4 a = p[0], b = p[1], c = p[2], d = p[3];
+  const float x[16] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+  return block_absmax(x);
+}
+
 // Work unit = one strip (kSW columns) over `seg` consecutive tiles, units
 // numbered strip-fastest.  Workgroup b takes units v, v + G, ... (G = grid
 // size, sized by the launcher to what the GPU holds at once) with v
@@ -515,7 +611,15 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
 // from two 16-byte LDS reads, and column block b (tile column b % 128, rows
 // (b / 128) * 16 ..+16) from sixteen 16-bit reads; both with the
 // one-lane-per-block quantizer.
-template <int FMT, int SELECT, int ROUND, bool WIDE, bool DO_ROW>
+//
+// TILE2D (16x16 tile scales, max->6, RNE): after the tile is in LDS each
+// lane stores its row block's amax in LDS, and after a second barrier every
+// row and column block takes the amax of its 16x16 tile (the 16 row-block
+// values of that tile), so both passes encode with the tile's scale and the
+// column-wise codes are the transpose of the row-wise ones.  DO_COL = false
+// skips the column-wise pass (row-wise layout only).
+template <int FMT, int SELECT, int ROUND, bool WIDE, bool DO_ROW, bool DO_COL = true,
+          bool TILE2D = false>
 __global__ void __launch_bounds__(kThreads)
 quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                       const float* __restrict__ amax, float sg, uint64_t seed, uint32_t key0,
@@ -525,8 +629,10 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
   static_assert(kSW * kTR / 16 == kThreads, "one row block and one column block per lane");
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kTilePitch];
-  __shared__ uint32_t ct[kSW * kCtPitch];
-  __shared__ uint8_t st[kSW * kStPitch];
+  __shared__ uint32_t ct[DO_COL ? kSW * kCtPitch : 1];
+  __shared__ uint8_t st[DO_COL ? kSW * kStPitch : 1];
+  // TILE2D: row-block amaxes, [16x16 tile t = (row / 16) * 8 + col / 16][row % 16]
+  __shared__ __attribute__((aligned(16))) float am[TILE2D ? kThreads : 1];
   const TensorScale ts = tensor_scale(*amax, sg);
   build_table<FMT>(tab, ts.alpha);
   __syncthreads();
@@ -558,13 +664,27 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
         *reinterpret_cast<uint4*>(tile + (k >> 4) * kTilePitch + (k & 15) * 16) = w[u];
       }
       __syncthreads();
+      if constexpr (TILE2D) {
+        float xr[16];
+        unpack16(*reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2),
+                 *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2 + 16), xr);
+        am[((rb_row >> 4) * 8 + (rb_col >> 4)) * 16 + (rb_row & 15)] = block_absmax(xr);
+        __syncthreads();
+      }
       // ---- row-wise block
       if constexpr (DO_ROW) {
         const uint4 wa = *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2);
         const uint4 wb = *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2 + 16);
         const int64_t r = r0 + rb_row, c = c0 + rb_col;
-        const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)c, key0);
-        const BlockOut o = quantize_block<FMT, SELECT, ROUND>(wa, wb, tab, ts, hb);
+        BlockOut o;
+        if constexpr (TILE2D) {
+          float xr[16];
+          unpack16(wa, wb, xr);
+          o = quantize_block_amax<FMT>(xr, tab, ts, tile_amax(am, (rb_row >> 4) * 8 + (rb_col >> 4)));
+        } else {
+          const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)c, key0);
+          o = quantize_block<FMT, SELECT, ROUND>(wa, wb, tab, ts, hb);
+        }
         if (r < rows && c < cols) {
           *reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c >> 1)) = make_uint2(o.c0, o.c1);
           scales[r * (cols >> 4) + (c >> 4)] = (uint8_t)o.scale;
@@ -572,15 +692,20 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
         }
       }
       // ---- column-wise block
-      {
+      if constexpr (DO_COL) {
         float xc[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           xc[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(
                                       tile + (cb_row + i) * kTilePitch + cb_col * 2) << 16);
         const int64_t c = c0 + cb_col, r = r0 + cb_row;
-        const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)c * (uint64_t)rows + (uint64_t)r, key0);
-        const BlockOut o = quantize_block_x<FMT, SELECT, ROUND>(xc, tab, ts, hb);
+        BlockOut o;
+        if constexpr (TILE2D) {
+          o = quantize_block_amax<FMT>(xc, tab, ts, tile_amax(am, (cb_row >> 4) * 8 + (cb_col >> 4)));
+        } else {
+          const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)c * (uint64_t)rows + (uint64_t)r, key0);
+          o = quantize_block_x<FMT, SELECT, ROUND>(xc, tab, ts, hb);
+        }
         const int wd = (int)(tr % kCtTiles) * (kTR / 8) + (cb_row >> 3);
         ct[cb_col * kCtPitch + wd] = o.c0;
         ct[cb_col * kCtPitch + wd + 1] = o.c1;
@@ -589,14 +714,16 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
       }
       __syncthreads();  // staged outputs complete; the tile may be rewritten
       // ---- flush closed stages
-      const bool last = tr + 1 == tr1;
-      if (last || (tr + 1) % kCtTiles == 0) {
-        flush_codes_t(ct, codes_t, rows, cols, c0, ct_lo, tr + 1);
-        ct_lo = tr + 1;
-      }
-      if (last || (tr + 1) % kStTiles == 0) {
-        flush_scales_t(st, scales_t, rows, cols, c0, st_lo, tr + 1);
-        st_lo = tr + 1;
+      if constexpr (DO_COL) {
+        const bool last = tr + 1 == tr1;
+        if (last || (tr + 1) % kCtTiles == 0) {
+          flush_codes_t(ct, codes_t, rows, cols, c0, ct_lo, tr + 1);
+          ct_lo = tr + 1;
+        }
+        if (last || (tr + 1) % kStTiles == 0) {
+          flush_scales_t(st, scales_t, rows, cols, c0, st_lo, tr + 1);
+          st_lo = tr + 1;
+        }
       }
       // (the next tile writes the staging buffers only after its first barrier)
       if (tr + 1 < tr1) {
@@ -691,6 +818,57 @@ static hipError_t launch_fmt(const QuantizeArgs& a, hipStream_t s) {
   }
   if (a.select == SELECT_4OVER6) return launch_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
   return launch_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
+}
+
+template <int FMT, int SELECT, int ROUND, bool WIDE>
+static hipError_t launch_rowscaled_typed(const QuantizeArgs& a, hipStream_t s) {
+  const uint32_t key0 = sr_key(a.seed, 0u);
+  const int64_t cus = device_cu_count();
+  const bool counting = a.select == SELECT_4OVER6 && a.count4 != nullptr;
+  const int64_t cap = counting ? cus : cus * 8;  // counting: one atomic per workgroup
+  const int64_t grid = a.rows < cap ? a.rows : cap;
+  hipLaunchKernelGGL((quantize_rowscaled_kernel<FMT, SELECT, ROUND, WIDE>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), a.rows, a.cols,
+                     a.amax, a.sg, a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales,
+                     a.count4);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_rowscaled_fmt(const QuantizeArgs& a, hipStream_t s) {
+  if (a.rounding == ROUND_SR) {
+    const bool wide = (uint64_t)a.rows * (uint64_t)a.cols > (1ull << 32);
+    return wide ? launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, true>(a, s)
+                : launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, false>(a, s);
+  }
+  if (a.select == SELECT_4OVER6) return launch_rowscaled_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
+  return launch_rowscaled_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
+}
+
+hipError_t launch_quantize_rowscaled(const QuantizeArgs& a, hipStream_t s) {
+  return a.fmt == FMT_E4M3 ? launch_rowscaled_fmt<FMT_E4M3>(a, s) : launch_rowscaled_fmt<FMT_UE5M3>(a, s);
+}
+
+template <int FMT>
+static hipError_t launch_2d_fmt(const QuantizeArgs& a, hipStream_t s) {
+  constexpr auto kBoth = quantize_tiles_kernel<FMT, SELECT_6, ROUND_RNE, false, true, true, true>;
+  constexpr auto kRow = quantize_tiles_kernel<FMT, SELECT_6, ROUND_RNE, false, true, false, true>;
+  const bool both = a.axes == (AXIS_ROW | AXIS_COL);
+  const int64_t tiles_r = (a.rows + kTR - 1) / kTR, tiles_c = (a.cols + kSW - 1) / kSW;
+  const int64_t target =
+      (int64_t)device_cu_count() * (both ? resident_per_cu<kBoth>() : resident_per_cu<kRow>());
+  int64_t seg = (tiles_r * tiles_c + target - 1) / target;
+  seg = seg < 1 ? 1 : (seg > tiles_r ? tiles_r : seg);
+  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
+  const int64_t grid = units < target ? units : target;
+  hipLaunchKernelGGL(both ? kBoth : kRow, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows,
+                     a.cols, a.amax, a.sg, a.seed, 0u, a.codes, a.scales, a.codes_t, a.scales_t,
+                     nullptr, seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_2d(const QuantizeArgs& a, hipStream_t s) {
+  return a.fmt == FMT_E4M3 ? launch_2d_fmt<FMT_E4M3>(a, s) : launch_2d_fmt<FMT_UE5M3>(a, s);
 }
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {

@@ -27,7 +27,7 @@ def _declared():
 
 def test_library_loads_and_version():
     lib = N.lib()
-    assert lib.nvfp4_abi_version() == 1
+    assert lib.nvfp4_abi_version() == 2
 
 
 def test_every_declared_symbol_is_exported_and_bound():
@@ -120,6 +120,80 @@ def test_fakequant_rejects():
     assert b(FAKE, None, 16, 16, FAKE, None, FAKE, FAKE, None, None) == N.ERR_INVALID
     assert b(FAKE, FAKE, 16, 16, FAKE, None, FAKE, None, None, None) == N.ERR_INVALID
     assert b(FAKE, FAKE, 0, 16, FAKE, None, FAKE, FAKE, None, None) == N.OK
+
+
+def test_row_amax_rejects():
+    f = N.lib().nvfp4_row_amax
+    assert f(FAKE, -1, 16, FAKE, None) == N.ERR_INVALID
+    assert f(FAKE, 16, 24, FAKE, None) == N.ERR_INVALID
+    assert f(None, 16, 16, FAKE, None) == N.ERR_INVALID
+    assert f(FAKE, 16, 16, None, None) == N.ERR_INVALID
+    assert f(FAKE_ODD, 16, 16, FAKE, None) == N.ERR_INVALID
+    assert f(FAKE, 16, 16, FAKE + 2, None) == N.ERR_INVALID
+    assert f(None, 0, 16, None, None) == N.OK
+
+
+def _qrs(**kw):
+    a = dict(x=FAKE, rows=16, cols=32, ra=FAKE, gmax=0.0, fmt=0, select=1, rnd=0, seed=0,
+             codes=FAKE, scales=FAKE, count4=None)
+    a.update(kw)
+    return N.lib().nvfp4_quantize_rowscaled(a["x"], a["rows"], a["cols"], a["ra"], a["gmax"],
+                                            a["fmt"], a["select"], a["rnd"], a["seed"],
+                                            a["codes"], a["scales"], a["count4"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(ra=None), dict(rows=-1), dict(cols=24), dict(fmt=2), dict(select=2),
+    dict(rnd=2), dict(rnd=1, select=1), dict(gmax=-1.0), dict(gmax=float("nan")),
+    dict(codes=None), dict(scales=None), dict(codes=FAKE_ODD), dict(scales=FAKE + 2),
+    dict(x=FAKE_ODD), dict(ra=FAKE + 2), dict(count4=FAKE_ODD),
+])
+def test_quantize_rowscaled_rejects(kw):
+    assert _qrs(**kw) == N.ERR_INVALID
+
+
+def test_quantize_rowscaled_empty_ok():
+    assert _qrs(rows=0) == N.OK and _qrs(cols=0) == N.OK
+
+
+def _dqrs(**kw):
+    a = dict(codes=FAKE, scales=FAKE, rows=16, cols=32, ra=FAKE, gmax=448.0, fmt=0,
+             f32=FAKE, b16=None, bs=None, xref=None, sse=None)
+    a.update(kw)
+    return N.lib().nvfp4_dequantize_rowscaled(a["codes"], a["scales"], a["rows"], a["cols"],
+                                              a["ra"], a["gmax"], a["fmt"], a["f32"], a["b16"],
+                                              a["bs"], a["xref"], a["sse"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(codes=None), dict(ra=None), dict(cols=8), dict(fmt=3), dict(gmax=0.0),
+    dict(xref=FAKE), dict(f32=FAKE_ODD), dict(ra=FAKE + 2),
+])
+def test_dequantize_rowscaled_rejects(kw):
+    assert _dqrs(**kw) == N.ERR_INVALID
+
+
+def _q2d(**kw):
+    a = dict(x=FAKE, rows=32, cols=32, amax=FAKE, gmax=0.0, fmt=0, codes=FAKE, scales=FAKE,
+             codes_t=FAKE, scales_t=FAKE)
+    a.update(kw)
+    return N.lib().nvfp4_quantize_2d(a["x"], a["rows"], a["cols"], a["amax"], a["gmax"],
+                                     a["fmt"], a["codes"], a["scales"], a["codes_t"],
+                                     a["scales_t"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(amax=None), dict(rows=24), dict(cols=8), dict(fmt=2), dict(gmax=-2.0),
+    dict(codes=None), dict(scales=None), dict(codes_t=None), dict(scales_t=None),
+    dict(codes_t=FAKE_ODD), dict(codes=FAKE_ODD), dict(x=FAKE_ODD), dict(amax=FAKE + 2),
+])
+def test_quantize_2d_rejects(kw):
+    assert _q2d(**kw) == N.ERR_INVALID
+
+
+def test_quantize_2d_empty_ok():
+    assert _q2d(rows=0) == N.OK
+    assert _q2d(codes_t=None, scales_t=None, rows=0) == N.OK
 
 
 def test_test_hooks_reject():

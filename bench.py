@@ -19,6 +19,9 @@ own shapes; their lines carry the same fields under their own metric names:
   qat        14336x4096: fake-quant forward + backward, tied and dual scales
   gradient   16384x8192: stale-amax UE5M3 SR quantize, row- and column-wise
              in one fused pass
+  activation-pertoken  8192x4096: per-row outer scales (row amax, row-scaled
+             4/6 quantize, row-scaled dequantize + MSE)
+  weight-2d  4096x4096: 16x16 tile scales, row-wise and transposed layouts
 """
 import argparse
 import hashlib
@@ -352,6 +355,86 @@ def run_qat(args, torch, np, nv, synth, dev, timer):
     return finish(line, kernels, args)
 
 
+def run_activation_pertoken(args, torch, np, nv, synth, dev, timer):
+    """Per-token outer scales on the 8192x4096 activation: row amax -> row-
+    scaled 4/6 quantize -> row-scaled dequantize with the MSE report."""
+    nsets = 8
+    xb = synth.make("activation")["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    x0 = to_dev(torch, np, xb, dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    ras = [torch.empty(rows, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    outs = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)}
+            for _ in range(nsets)]
+    xh = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    gm = nv.default_global_max("e4m3", "4over6")
+    sse = torch.zeros(1, dtype=torch.float64, device=dev)
+    reps = max(args.steps, 40)
+    us = {
+        "row_amax": timer.avg_us(lambda i: nv.row_amax(xs[i % nsets], out=ras[i % nsets]),
+                                 reps, nsets),
+        "quantize_rowscaled_4over6": timer.avg_us(lambda i: nv.quantize_rowscaled(
+            xs[i % nsets], ras[i % nsets], select="4over6", out=outs[i % nsets]), reps, nsets),
+        "dequantize_rowscaled_f32_mse": timer.avg_us(lambda i: nv.dequantize_rowscaled(
+            outs[i % nsets]["codes"], outs[i % nsets]["scales"], ras[i % nsets], global_max=gm,
+            x_ref=xs[i % nsets], sse=sse, out=xh[i % nsets]), reps, nsets),
+    }
+    bpe = {"row_amax": B_AMAX, "quantize_rowscaled_4over6": B_QUANT,
+           "dequantize_rowscaled_f32_mse": B_DEQ_MSE}
+    kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
+    ms_step = sum(us.values()) / 1e3
+    step_bytes = n * sum(bpe.values())
+    line = base_line("NVFP4 per-token 4/6 quantize step GB/s at 8192x4096 bf16",
+                     step_bytes / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     "activation 8192x4096 bf16 (seed 2), per-row outer scales: row amax -> "
+                     "row-scaled Four-Over-Six quantize (E4M3, FP8 max 256) -> row-scaled "
+                     "dequantize to f32 with binary64 MSE report",
+                     {"rows": rows, "cols": cols, "elements": n,
+                      "timing": "sum of per-kernel event averages"}, n)
+    return finish(line, kernels, args)
+
+
+def run_weight_2d(args, torch, np, nv, synth, dev, timer):
+    """16x16 tile scales on the 4096x4096 weight: amax -> tile-scaled quantize
+    with both layouts (the transposed codes bit-identical)."""
+    nsets = 8
+    xb = synth.make("weight")["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    x0 = to_dev(torch, np, xb, dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    amaxs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    outs = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+             "codes_t": torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev),
+             "scales_t": torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev)}
+            for _ in range(nsets)]
+    reps = max(args.steps, 40)
+    us = {
+        "tensor_amax": timer.avg_us(lambda i: nv.tensor_amax(xs[i % nsets], out=amaxs[i % nsets]),
+                                    reps, nsets),
+        "quantize_2d_both": timer.avg_us(lambda i: nv.quantize_2d(
+            xs[i % nsets], amaxs[i % nsets], out=outs[i % nsets]), reps, nsets),
+        "quantize_2d_row": timer.avg_us(lambda i: nv.quantize_2d(
+            xs[i % nsets], amaxs[i % nsets], transpose=False,
+            out={"codes": outs[i % nsets]["codes"], "scales": outs[i % nsets]["scales"]}),
+            reps, nsets),
+    }
+    bpe = {"tensor_amax": B_AMAX, "quantize_2d_both": B_FUSED, "quantize_2d_row": B_QUANT}
+    kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
+    ms_step = (us["tensor_amax"] + us["quantize_2d_both"]) / 1e3
+    step_bytes = n * (B_AMAX + B_FUSED)
+    line = base_line("NVFP4 16x16-tile quantize (both layouts) GB/s at 4096x4096 bf16 weight",
+                     step_bytes / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     f"weight 4096x4096 bf16 (seed {synth.SEEDS['weight']}): amax -> 16x16 tile "
+                     "scales, E4M3 (FP8 max 448), RNE, row-wise and transposed layouts",
+                     {"rows": rows, "cols": cols, "elements": n,
+                      "timing": "sum of per-kernel event averages"}, n)
+    return finish(line, kernels, args)
+
+
 def run_gradient(args, torch, np, nv, synth, dev, timer):
     log("generating the 16384x8192 gradient")
     xb = synth.make("gradient")["x"]
@@ -408,7 +491,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="activation",
-                    choices=["activation", "weight-1k", "weight", "qat", "gradient"])
+                    choices=["activation", "weight-1k", "weight", "qat", "gradient",
+                             "activation-pertoken", "weight-2d"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 256 MiB copy and each kernel of the workload twice (for PMC counters)")
@@ -434,6 +518,10 @@ def main():
         line = run_weight(args, torch, np, nv, synth, dev, timer, args.workload == "weight-1k")
     elif args.workload == "qat":
         line = run_qat(args, torch, np, nv, synth, dev, timer)
+    elif args.workload == "activation-pertoken":
+        line = run_activation_pertoken(args, torch, np, nv, synth, dev, timer)
+    elif args.workload == "weight-2d":
+        line = run_weight_2d(args, torch, np, nv, synth, dev, timer)
     else:
         line = run_gradient(args, torch, np, nv, synth, dev, timer)
     if line is not None:

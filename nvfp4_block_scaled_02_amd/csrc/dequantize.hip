@@ -36,17 +36,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return v != v ? ((b >> 16) | 0x40u) : r;
 }
 
-// ROWSC: amax holds one amax per row (per-row outer scales); each quad lies in
-// one row (cols % 16 == 0) and takes that row's alpha.
-template <int FMT, bool F32, bool BF16, bool BSC, bool SSE, int BLOCK, bool ROWSC>
+template <int FMT, bool F32, bool BF16, bool BSC, bool SSE, int BLOCK>
 __global__ void __launch_bounds__(BLOCK)
 dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                   int64_t nquads, const float* __restrict__ amax, float sg,
                   float4* __restrict__ out_f32, uint2* __restrict__ out_bf16,
                   float* __restrict__ block_scale, const uint2* __restrict__ x_ref,
-                  double* sse, int64_t quads_per_row) {
-  const float alpha_t = ROWSC ? 0.0f : outer_alpha(*amax, sg);
-  const bool narrow = (nquads >> 32) == 0;  // quad indices fit 32 bits
+                  double* sse) {
+  const float alpha = outer_alpha(*amax, sg);
   const bool lead4 = (threadIdx.x & 3) == 0;
   double acc = 0.0;
   const int64_t per_iter = (int64_t)gridDim.x * BLOCK * kDqUnroll;
@@ -65,12 +62,6 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
     for (int u = 0; u < kDqUnroll; ++u) {
       const int64_t qd = base + u * BLOCK + threadIdx.x;
       if (qd >= nquads) continue;
-      float alpha = alpha_t;
-      if constexpr (ROWSC) {
-        const int64_t r = narrow ? (int64_t)((uint32_t)qd / (uint32_t)quads_per_row)
-                                 : qd / quads_per_row;
-        alpha = outer_alpha(amax[r], sg);
-      }
       const float D = decode_scale(FMT, sc[u]);
       const f32x2 q01 = NVFP4_DEC_PK_FP4(cw[u], 0), q23 = NVFP4_DEC_PK_FP4(cw[u], 1);
       const float v[4] = {(q01[0] * D) * alpha, (q01[1] * D) * alpha, (q23[0] * D) * alpha,
@@ -105,26 +96,104 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
   }
 }
 
-template <int FMT, bool F32, bool BF16, bool BSC, bool SSE, bool ROWSC>
-static hipError_t launch_dq_rs(const DequantizeArgs& a, hipStream_t s) {
-  constexpr int BLOCK = SSE ? 1024 : kThreads;
-  const int64_t nquads = a.rows * a.cols / 4;
-  const int64_t per_wg = (int64_t)BLOCK * kDqUnroll;
-  int64_t grid = (nquads + per_wg - 1) / per_wg;
-  const int64_t cap = (int64_t)device_cu_count() * (SSE ? 1 : 8);
-  grid = grid < cap ? grid : cap;
-  hipLaunchKernelGGL((dequantize_kernel<FMT, F32, BF16, BSC, SSE, BLOCK, ROWSC>),
-                     dim3((unsigned)grid), dim3(BLOCK), 0, s,
-                     reinterpret_cast<const uint16_t*>(a.codes), a.scales, nquads, a.amax, a.sg,
-                     reinterpret_cast<float4*>(a.out_f32), reinterpret_cast<uint2*>(a.out_bf16),
-                     a.block_scale, reinterpret_cast<const uint2*>(a.x_ref), a.sse, a.cols / 4);
-  return hipGetLastError();
+// Per-row outer scales: a workgroup owns whole rows, kDqUnroll of them at a
+// time (rows r, r + G, r + 2G, ... for G = grid size), forms each row's
+// alpha_r once, and lane t handles quad t (then t + BLOCK, ...) of each of
+// those rows, so every lane keeps kDqUnroll independent loads in flight
+// whatever the row length.
+template <int FMT, bool F32, bool BF16, bool BSC, bool SSE, int BLOCK>
+__global__ void __launch_bounds__(BLOCK)
+dequantize_rows_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                       int64_t rows, int64_t qpr, const float* __restrict__ row_amax, float sg,
+                       float4* __restrict__ out_f32, uint2* __restrict__ out_bf16,
+                       float* __restrict__ block_scale, const uint2* __restrict__ x_ref,
+                       double* sse) {
+  const bool lead4 = (threadIdx.x & 3) == 0;
+  const int64_t G = gridDim.x;
+  double acc = 0.0;
+  for (int64_t r0 = blockIdx.x; r0 < rows; r0 += G * kDqUnroll) {
+    float alpha[kDqUnroll];
+#pragma unroll
+    for (int u = 0; u < kDqUnroll; ++u) {
+      const int64_t r = r0 + u * G;
+      alpha[u] = r < rows ? outer_alpha(row_amax[r], sg) : 0.0f;
+    }
+    for (int64_t q = threadIdx.x; q < qpr; q += BLOCK) {
+      uint32_t cw[kDqUnroll], sc[kDqUnroll];
+      uint2 xr[kDqUnroll];
+#pragma unroll
+      for (int u = 0; u < kDqUnroll; ++u) {
+        const int64_t r = r0 + u * G;
+        const bool ok = r < rows;
+        const int64_t qd = r * qpr + q;
+        cw[u] = ok ? (uint32_t)codes[qd] : 0u;
+        sc[u] = ok ? (uint32_t)scales[qd >> 2] : 0u;
+        if (SSE) xr[u] = ok ? ld_nt(x_ref + qd) : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kDqUnroll; ++u) {
+        const int64_t r = r0 + u * G;
+        if (r >= rows) continue;
+        const int64_t qd = r * qpr + q;
+        const float D = decode_scale(FMT, sc[u]);
+        const f32x2 q01 = NVFP4_DEC_PK_FP4(cw[u], 0), q23 = NVFP4_DEC_PK_FP4(cw[u], 1);
+        const float v[4] = {(q01[0] * D) * alpha[u], (q01[1] * D) * alpha[u],
+                            (q23[0] * D) * alpha[u], (q23[1] * D) * alpha[u]};
+        if (F32) st_nt(make_float4(v[0], v[1], v[2], v[3]), out_f32 + qd);
+        if (BF16) {
+          const uint2 h = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                     bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+          st_nt(h, out_bf16 + qd);
+        }
+        if (BSC && lead4) block_scale[qd >> 2] = D * alpha[u];
+        if (SSE) {
+          const float xs[4] = {bf16_lo(xr[u].x), bf16_hi(xr[u].x), bf16_lo(xr[u].y), bf16_hi(xr[u].y)};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const double d = (double)(xs[i] - v[i]);
+            acc = __builtin_fma(d, d, acc);
+          }
+        }
+      }
+    }
+  }
+  if (SSE) {
+    __shared__ double red[BLOCK / 64];
+    acc = wave_sum_f64(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
+      unsafeAtomicAdd(sse, t);
+    }
+  }
 }
 
 template <int FMT, bool F32, bool BF16, bool BSC, bool SSE>
 static hipError_t launch_dq(const DequantizeArgs& a, hipStream_t s) {
-  return a.row_scaled ? launch_dq_rs<FMT, F32, BF16, BSC, SSE, true>(a, s)
-                      : launch_dq_rs<FMT, F32, BF16, BSC, SSE, false>(a, s);
+  constexpr int BLOCK = SSE ? 1024 : kThreads;
+  const int64_t cap = (int64_t)device_cu_count() * (SSE ? 1 : 8);
+  if (a.row_scaled) {
+    const int64_t grid = a.rows < cap ? a.rows : cap;
+    hipLaunchKernelGGL((dequantize_rows_kernel<FMT, F32, BF16, BSC, SSE, BLOCK>),
+                       dim3((unsigned)grid), dim3(BLOCK), 0, s,
+                       reinterpret_cast<const uint16_t*>(a.codes), a.scales, a.rows, a.cols / 4,
+                       a.amax, a.sg, reinterpret_cast<float4*>(a.out_f32),
+                       reinterpret_cast<uint2*>(a.out_bf16), a.block_scale,
+                       reinterpret_cast<const uint2*>(a.x_ref), a.sse);
+    return hipGetLastError();
+  }
+  const int64_t nquads = a.rows * a.cols / 4;
+  const int64_t per_wg = (int64_t)BLOCK * kDqUnroll;
+  int64_t grid = (nquads + per_wg - 1) / per_wg;
+  grid = grid < cap ? grid : cap;
+  hipLaunchKernelGGL((dequantize_kernel<FMT, F32, BF16, BSC, SSE, BLOCK>), dim3((unsigned)grid),
+                     dim3(BLOCK), 0, s, reinterpret_cast<const uint16_t*>(a.codes), a.scales,
+                     nquads, a.amax, a.sg, reinterpret_cast<float4*>(a.out_f32),
+                     reinterpret_cast<uint2*>(a.out_bf16), a.block_scale,
+                     reinterpret_cast<const uint2*>(a.x_ref), a.sse);
+  return hipGetLastError();
 }
 
 template <int FMT, bool F32, bool BF16, bool BSC>

@@ -176,7 +176,16 @@ __device__ __forceinline__ float max3_abs(float a, float b, float c) {
       __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)), __builtin_fabsf(c));
 }
 
-template <int FMT, int SELECT, int ROUND>
+// DIRECT: {S_EFF, INV_S} of the chosen codes are computed (decode, product,
+// correctly rounded reciprocal: the same formula as the LDS table) instead of
+// looked up -- for per-row outer scales, where no table is shared.
+template <int FMT, bool DIRECT>
+__device__ __forceinline__ f32x2 scale_of(const f32x2* tab, uint32_t code, float alpha) {
+  if constexpr (DIRECT) return scale_entry(FMT, code, alpha);
+  else return tab[code];
+}
+
+template <int FMT, int SELECT, int ROUND, bool DIRECT = false>
 __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const f32x2* tab,
                                                      const TensorScale& ts, uint32_t hbase) {
   // block amax as a depth-3 tree of v_maximum3_f32 (IEEE maximum is
@@ -191,7 +200,7 @@ __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const
   BlockOut o;
   if constexpr (SELECT == SELECT_6) {
     const uint32_t c6 = encode_pair(FMT, m * ts.k6, 0.0f) & 0xFFu;
-    const f32x2 t = tab[c6];
+    const f32x2 t = scale_of<FMT, DIRECT>(tab, c6, ts.alpha);
     if constexpr (ROUND == ROUND_RNE) {
       float y[8];
 #pragma unroll
@@ -220,7 +229,8 @@ __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const
   } else {
     const uint32_t cc = encode_pair(FMT, m * ts.k6, m * ts.k4);
     const uint32_t c6 = cc & 0xFFu, c4 = cc >> 8;
-    const f32x2 t6 = tab[c6], t4 = tab[c4];
+    const f32x2 t6 = scale_of<FMT, DIRECT>(tab, c6, ts.alpha);
+    const f32x2 t4 = scale_of<FMT, DIRECT>(tab, c4, ts.alpha);
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = x[i] * t6[1];
@@ -252,14 +262,14 @@ __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const
 }
 
 // The block as two 16-byte bf16 chunks.
-template <int FMT, int SELECT, int ROUND>
+template <int FMT, int SELECT, int ROUND, bool DIRECT = false>
 __device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2* tab,
                                                    const TensorScale& ts, uint32_t hbase) {
   const float x[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
                        bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
                        bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
                        bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
-  return quantize_block_x<FMT, SELECT, ROUND>(x, tab, ts, hbase);
+  return quantize_block_x<FMT, SELECT, ROUND, DIRECT>(x, tab, ts, hbase);
 }
 
 // A block (16 values in one lane) quantized with a given block amax instead
@@ -468,41 +478,106 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
 
 // ---------------------------------------------------------------- per-row outer scales
 // Row-wise quantization with per-row outer scales ("End-to-End 4-Bit
-// Training", Recipe details: per-token outer scales for activations).  A
-// workgroup owns one row at a time: it forms alpha_r from the row's amax,
-// builds the row's {S_EFF, INV_S} table in LDS, and its wavefronts take the
-// row's groups of 64 blocks through the same LDS bounce and one-lane
-// quantizer as quantize_blocks_kernel.
+// Training", Recipe details: per-token outer scales for activations): the
+// one-lane-per-block stream of quantize_blocks_kernel, where each lane forms
+// its block's row constants (alpha_r, K_6, K_4) and the chosen codes'
+// {S_EFF, INV_S} itself.  A per-row LDS table would need two workgroup
+// barriers per row, which on this stream cost more than the divisions.
 template <int FMT, int SELECT, int ROUND, bool WIDE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
-quantize_rowscaled_kernel(const uint4* __restrict__ x, int64_t rows, int64_t cols,
+quantize_rowscaled_kernel(const uint4* __restrict__ x, int64_t nblocks, int64_t row_blocks,
                           const float* __restrict__ row_amax, float sg, uint64_t seed,
                           uint32_t key0, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
                           unsigned long long* count4) {
-  __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint4 stage[kThreads * 2];
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-  uint4* reg = stage + wv * 128;  // this wavefront's 2 KiB
-  const int64_t nb = cols / 16, nch = cols / kChunk;  // blocks and chunks per row
-  const int64_t ngroups = (nb + 63) / 64;
+  uint4* reg = stage + wv * 128;
+  const int64_t nchunks = nblocks * 2;
+  const int64_t ngroups = (nblocks + 63) / 64;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const bool narrow = (nblocks >> 32) == 0;
   uint32_t n4 = 0;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    const TensorScale ts = tensor_scale(row_amax[r], sg);
-    __syncthreads();  // the previous row's table reads are done
-    build_table<FMT>(tab, ts.alpha);
-    __syncthreads();
+  for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + wv; g < ngroups; g += nwaves) {
+    const int64_t c0 = g * 128;
+    const bool whole = c0 + 128 <= nchunks;
+    const uint4 a = (whole || c0 + l < nchunks) ? ld_nt(x + c0 + l) : make_uint4(0, 0, 0, 0);
+    const uint4 b = (whole || c0 + 64 + l < nchunks) ? ld_nt(x + c0 + 64 + l) : make_uint4(0, 0, 0, 0);
+    bounce_pair(reg, l, a, b);
+    const int64_t bk = g * 64 + l;
+    const bool ok = bk < nblocks;
+    const int64_t r = narrow ? (int64_t)((uint32_t)bk / (uint32_t)row_blocks) : bk / row_blocks;
+    const TensorScale ts = tensor_scale(ok ? row_amax[r] : 0.0f, sg);
+    const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
+    const BlockOut o = quantize_block<FMT, SELECT, ROUND, true>(reg[2 * l], reg[2 * l + 1], nullptr, ts, hb);
+    if (ok) {
+      codes[bk] = make_uint2(o.c0, o.c1);
+      scales[bk] = (uint8_t)o.scale;
+      n4 += o.four;
+    }
+  }
+  if (SELECT == SELECT_4OVER6 && count4) flush_count<kThreads>(count4, n4);
+}
+
+// Long rows (at least 64 blocks): a wavefront owns whole rows.  Per row it
+// builds its own {S_EFF, INV_S} table in its own LDS (no workgroup barrier:
+// only this wavefront reads it, and its LDS operations complete in order),
+// then streams the row's 64-block groups exactly as quantize_blocks_kernel
+// does.  The table's divisions are paid once per row, not once per block.
+template <int FMT, int SELECT, int ROUND, bool WIDE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_blocks,
+                        const float* __restrict__ row_amax, float sg, uint64_t seed,
+                        uint32_t key0, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                        unsigned long long* count4) {
+  constexpr int kTab = (FmtTraits<FMT>::kCodes + 63) / 64 * 64;
+  __shared__ __attribute__((aligned(16))) uint4 stage[kThreads * 2];
+  __shared__ f32x2 tabs[kThreads / 64][kTab];
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint4* reg = stage + wv * 128;
+  f32x2* tab = tabs[wv];
+  const int64_t nch = row_blocks * 2;
+  const int64_t ngroups = (row_blocks + 63) / 64, nwhole = row_blocks / 64;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  uint32_t n4 = 0;
+  for (int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + wv; r < rows; r += nwaves) {
     const uint4* xr = x + r * nch;
-    for (int64_t g = wv; g < ngroups; g += kThreads / 64) {
+    TensorScale ts = tensor_scale(row_amax[r], sg);
+    // the row's constants are uniform over the wavefront: keep them in SGPRs
+    ts.alpha = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ts.alpha)));
+    ts.k6 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ts.k6)));
+    ts.k4 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ts.k4)));
+    // the previous row's lookups are done before its table is overwritten
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c = l; c < kTab; c += 64)
+      if (c < FmtTraits<FMT>::kCodes) tab[c] = scale_entry(FMT, (uint32_t)c, ts.alpha);
+    const uint4* xg = xr + l;
+    const int64_t ob0 = r * row_blocks + l;
+    int64_t g = 0;
+    for (; g < nwhole; ++g) {
+      const uint4 a = ld_nt(xg + g * 128), b = ld_nt(xg + g * 128 + 64);
+      bounce_pair(reg, l, a, b);  // also orders the table's writes before its reads
+      const int64_t ob = ob0 + g * 64;
+      const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)ob * 16, key0);
+      const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
+      codes[ob] = make_uint2(o.c0, o.c1);
+      scales[ob] = (uint8_t)o.scale;
+      n4 += o.four;
+    }
+    if (g < ngroups) {  // the row's partial last group
       const int64_t c0 = g * 128;
       const uint4 a = c0 + l < nch ? ld_nt(xr + c0 + l) : make_uint4(0, 0, 0, 0);
       const uint4 b = c0 + 64 + l < nch ? ld_nt(xr + c0 + 64 + l) : make_uint4(0, 0, 0, 0);
       bounce_pair(reg, l, a, b);
       const int64_t bk = g * 64 + l;
-      const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)bk * 16, key0);
+      const int64_t ob = r * row_blocks + bk;
+      const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)ob * 16, key0);
       const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
-      if (bk < nb) {
-        codes[r * nb + bk] = make_uint2(o.c0, o.c1);
-        scales[r * nb + bk] = (uint8_t)o.scale;
+      if (bk < row_blocks) {
+        codes[ob] = make_uint2(o.c0, o.c1);
+        scales[ob] = (uint8_t)o.scale;
         n4 += o.four;
       }
     }
@@ -825,12 +900,27 @@ static hipError_t launch_rowscaled_typed(const QuantizeArgs& a, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int64_t cus = device_cu_count();
   const bool counting = a.select == SELECT_4OVER6 && a.count4 != nullptr;
+  const int64_t nblocks = a.rows * a.cols / 16;
+  const int64_t row_blocks = a.cols / 16;
   const int64_t cap = counting ? cus : cus * 8;  // counting: one atomic per workgroup
-  const int64_t grid = a.rows < cap ? a.rows : cap;
+  // A wavefront per row when its groups are mostly full (at least 3/4 of
+  // the lanes busy), else one lane per block over the flat block stream.
+  if (row_blocks % 64 == 0 || row_blocks >= 192) {
+    int64_t grid = (a.rows + kThreads / 64 - 1) / (kThreads / 64);
+    grid = grid < cap ? grid : cap;
+    hipLaunchKernelGGL((quantize_rowwave_kernel<FMT, SELECT, ROUND, WIDE>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), a.rows,
+                       row_blocks, a.amax, a.sg, a.seed, key0,
+                       reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+    return hipGetLastError();
+  }
+  const int64_t ngroups = (nblocks + 63) / 64;
+  int64_t grid = (ngroups + kThreads / 64 - 1) / (kThreads / 64);
+  grid = grid < cap ? grid : cap;
   hipLaunchKernelGGL((quantize_rowscaled_kernel<FMT, SELECT, ROUND, WIDE>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), a.rows, a.cols,
-                     a.amax, a.sg, a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales,
-                     a.count4);
+                     dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), nblocks,
+                     a.cols / 16, a.amax, a.sg, a.seed, key0,
+                     reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
   return hipGetLastError();
 }
 

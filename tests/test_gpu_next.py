@@ -107,7 +107,7 @@ def test_rowscaled_sr_ue5m3_gradient_rows():
     _same(s, rs, "scales")
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 16), (5, 48), (19, 1040), (64, 4112), (3, 16384)])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (5, 48), (19, 1040), (64, 4112), (3, 16384), (2, 3088)])
 @pytest.mark.parametrize("select", ["6", "4over6"])
 def test_rowscaled_ragged(rows, cols, select):
     xb = _rows_tensor(rows, cols, 3 * rows + cols)
@@ -119,8 +119,9 @@ def test_rowscaled_ragged(rows, cols, select):
     assert n == rn
 
 
-def test_rowscaled_special_rows():
-    xb = _rows_tensor(8, 64, 5)
+@pytest.mark.parametrize("cols", [64, 1024])  # short rows: a lane per block; long: a wave per row
+def test_rowscaled_special_rows(cols):
+    xb = _rows_tensor(8, cols, 5)
     ra = O.row_amax(xb)
     ra[1] = 0.0          # all-zero outer scale input: alpha = 1
     ra[2] = np.nan       # no usable scale

@@ -22,326 +22,9 @@
 // that reads each 32 x 128 tile once into LDS, quantizes it row-wise and/or
 // column-wise from there, and stages the column-wise outputs so that they
 // leave as 64-byte pieces.
-#include <atomic>
-
-#include "common.hpp"
-#include "device.hpp"
+#include "quantize_core.hpp"
 
 namespace nvfp4 {
-
-template <int FMT>
-struct FmtTraits;
-template <>
-struct FmtTraits<FMT_E4M3> {
-  static constexpr int kCodes = 127;  // finite non-negative codes 0x00..0x7E
-  static constexpr uint32_t kNan = 0x7Fu;
-};
-template <>
-struct FmtTraits<FMT_UE5M3> {
-  static constexpr int kCodes = 255;  // 0x00..0xFE
-  static constexpr uint32_t kNan = 0xFFu;
-};
-
-template <int FMT>
-__device__ __forceinline__ void build_table(f32x2* tab, float alpha) {
-  for (int c = threadIdx.x; c < FmtTraits<FMT>::kCodes; c += blockDim.x)
-    tab[c] = scale_entry(FMT, (uint32_t)c, alpha);
-}
-
-struct HalfOut {
-  uint32_t codes;  // 8 nibbles, element i in nibble i
-  uint32_t scale;  // the block's scale byte (same in both lanes of the pair)
-  uint32_t four;   // 1 if the block chose max->4
-};
-
-// SSE contribution of this lane's 8 elements for one candidate: two fmaf
-// chains over elements 0-3 and 4-7 (each from +0), then their sum.
-__device__ __forceinline__ float half_sse(uint32_t packed, const float (&x)[8], float S) {
-  float q[8];
-  e2m1_unpack8(packed, q);
-  float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float d = __builtin_fmaf(-q[i], S, x[i]);
-    p0 = __builtin_fmaf(d, d, p0);
-  }
-#pragma unroll
-  for (int i = 4; i < 8; ++i) {
-    float d = __builtin_fmaf(-q[i], S, x[i]);
-    p1 = __builtin_fmaf(d, d, p1);
-  }
-  return p0 + p1;
-}
-
-// Quantize the lane's half block.  Every lane of the wavefront must call it
-// (DPP partner exchange).  Stochastic rounding only: hbase = lo32(idx0) ^ key,
-// idx0 being the output-orientation index of element 0 of this half and key
-// the counter-hash key of its high word.  idx0 is a multiple of 8, so element
-// i's hash input lo32(idx0 + i) ^ key equals hbase ^ i.
-template <int FMT, int SELECT, int ROUND>
-__device__ __forceinline__ HalfOut quantize_half(uint4 w, const f32x2* tab, const TensorScale& ts,
-                                                 uint32_t hbase) {
-  const float x[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                      bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-  // block amax: IEEE 754-2019 maximum (v_maximum3_f32, NaN-propagating) of
-  // |x| over the lane's 8 elements, then over the lane pair
-  float m = __builtin_elementwise_maximum(__builtin_fabsf(x[0]), __builtin_fabsf(x[1]));
-#pragma unroll
-  for (int i = 2; i < 8; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(x[i]));
-  const float a = __builtin_elementwise_maximum(m, xor1_f32(m));
-  const bool nan_blk = ts.nan || (a != a);
-  HalfOut o;
-  if constexpr (SELECT == SELECT_6) {
-    const uint32_t c6 = encode_pair(FMT, a * ts.k6, 0.0f) & 0xFFu;
-    const f32x2 t = tab[c6];
-    if constexpr (ROUND == ROUND_RNE) {
-      float y[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
-      o.codes = e2m1_rne_pack8(y);
-    } else {
-      f32x2 yp[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) yp[b] = f32x2{x[2 * b] * t[1], x[2 * b + 1] * t[1]};
-      const uint32_t t = hbase ^ (hbase >> 16);  // shared first step of fmix32
-      uint32_t h[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = fmix32_tail(t ^ (uint32_t)i);
-      o.codes = e2m1_sr_pack8(yp, h, __float_as_uint(x[0]), __float_as_uint(x[1]));
-    }
-    o.scale = c6;
-    o.four = 0;
-  } else {
-    const uint32_t cc = encode_pair(FMT, a * ts.k6, a * ts.k4);
-    const uint32_t c6 = cc & 0xFFu, c4 = cc >> 8;
-    const f32x2 t6 = tab[c6], t4 = tab[c4];
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[i] * t6[1];
-    const uint32_t w6 = e2m1_rne_pack8(y);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[i] * t4[1];
-    const uint32_t w4 = e2m1_rne_pack8(y);
-    float e6 = half_sse(w6, x, t6[0]);
-    float e4 = half_sse(w4, x, t4[0]);
-    const float o6 = xor1_f32(e6), o4 = xor1_f32(e4);
-    e6 = e6 + o6;  // (P0 + P1) + (P2 + P3): addition commutes bitwise
-    e4 = e4 + o4;
-    const bool four = e4 < e6;
-    o.codes = four ? w4 : w6;
-    o.scale = four ? c4 : c6;
-    o.four = four ? 1u : 0u;
-  }
-  if (nan_blk) {
-    o.codes = 0;
-    o.scale = FmtTraits<FMT>::kNan;
-    o.four = 0;
-  }
-  return o;
-}
-
-// ---------------------------------------------------------------- one lane per block
-struct BlockOut {
-  uint32_t c0, c1;  // codes of elements 0-7 and 8-15, element i in nibble i % 8
-  uint32_t scale;
-  uint32_t four;
-};
-
-// SSE of one candidate over a whole block: four fmaf chains over elements
-// 4k..4k+3 (each from +0), summed as (P0 + P1) + (P2 + P3).
-__device__ __forceinline__ float block_sse(uint32_t w0, uint32_t w1, const float (&x)[16], float S) {
-  float qa[8], qb[8];
-  e2m1_unpack8(w0, qa);
-  e2m1_unpack8(w1, qb);
-  float P[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float p = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * k + i;
-      const float d = __builtin_fmaf(-(e < 8 ? qa[e] : qb[e - 8]), S, x[e]);
-      p = __builtin_fmaf(d, d, p);
-    }
-    P[k] = p;
-  }
-  return (P[0] + P[1]) + (P[2] + P[3]);
-}
-
-// Quantize a whole block (chunks a, b) in one lane: no partner exchange and
-// no duplicated scale encode, which the lane-pair form pays for.  hbase as
-// in quantize_half, for element 0 of the block (idx0 a multiple of 16).
-__device__ __forceinline__ float max3_abs(float a, float b, float c) {
-  return __builtin_elementwise_maximum(
-      __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)), __builtin_fabsf(c));
-}
-
-// DIRECT: {S_EFF, INV_S} of the chosen codes are computed (decode, product,
-// correctly rounded reciprocal: the same formula as the LDS table) instead of
-// looked up -- for per-row outer scales, where no table is shared.
-template <int FMT, bool DIRECT>
-__device__ __forceinline__ f32x2 scale_of(const f32x2* tab, uint32_t code, float alpha) {
-  if constexpr (DIRECT) return scale_entry(FMT, code, alpha);
-  else return tab[code];
-}
-
-template <int FMT, int SELECT, int ROUND, bool DIRECT = false>
-__device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const f32x2* tab,
-                                                     const TensorScale& ts, uint32_t hbase) {
-  // block amax as a depth-3 tree of v_maximum3_f32 (IEEE maximum is
-  // associative and commutative, NaN included, so the order is immaterial)
-  const float m0 = max3_abs(x[0], x[1], x[2]), m1 = max3_abs(x[3], x[4], x[5]);
-  const float m2 = max3_abs(x[6], x[7], x[8]), m3 = max3_abs(x[9], x[10], x[11]);
-  const float m4 = max3_abs(x[12], x[13], x[14]);
-  const float m = __builtin_elementwise_maximum(
-      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, m1), m2),
-      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m3, m4), __builtin_fabsf(x[15])));
-  const bool nan_blk = ts.nan || (m != m);
-  BlockOut o;
-  if constexpr (SELECT == SELECT_6) {
-    const uint32_t c6 = encode_pair(FMT, m * ts.k6, 0.0f) & 0xFFu;
-    const f32x2 t = scale_of<FMT, DIRECT>(tab, c6, ts.alpha);
-    if constexpr (ROUND == ROUND_RNE) {
-      float y[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
-      o.c0 = e2m1_rne_pack8(y);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t[1];
-      o.c1 = e2m1_rne_pack8(y);
-    } else {
-      const uint32_t tt = hbase ^ (hbase >> 16);  // shared first step of fmix32
-      f32x2 yp[4];
-      uint32_t h[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) yp[j] = f32x2{x[2 * j] * t[1], x[2 * j + 1] * t[1]};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = fmix32_tail(tt ^ (uint32_t)i);
-      o.c0 = e2m1_sr_pack8(yp, h, __float_as_uint(x[0]), __float_as_uint(x[1]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) yp[j] = f32x2{x[8 + 2 * j] * t[1], x[9 + 2 * j] * t[1]};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = fmix32_tail(tt ^ (uint32_t)(8 + i));
-      o.c1 = e2m1_sr_pack8(yp, h, __float_as_uint(x[8]), __float_as_uint(x[9]));
-    }
-    o.scale = c6;
-    o.four = 0;
-  } else {
-    const uint32_t cc = encode_pair(FMT, m * ts.k6, m * ts.k4);
-    const uint32_t c6 = cc & 0xFFu, c4 = cc >> 8;
-    const f32x2 t6 = scale_of<FMT, DIRECT>(tab, c6, ts.alpha);
-    const f32x2 t4 = scale_of<FMT, DIRECT>(tab, c4, ts.alpha);
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[i] * t6[1];
-    const uint32_t a6 = e2m1_rne_pack8(y);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t6[1];
-    const uint32_t b6 = e2m1_rne_pack8(y);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[i] * t4[1];
-    const uint32_t a4 = e2m1_rne_pack8(y);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t4[1];
-    const uint32_t b4 = e2m1_rne_pack8(y);
-    const float e6 = block_sse(a6, b6, x, t6[0]);
-    const float e4 = block_sse(a4, b4, x, t4[0]);
-    const bool four = e4 < e6;
-    o.c0 = four ? a4 : a6;
-    o.c1 = four ? b4 : b6;
-    o.scale = four ? c4 : c6;
-    o.four = four ? 1u : 0u;
-  }
-  if (nan_blk) {
-    o.c0 = 0;
-    o.c1 = 0;
-    o.scale = FmtTraits<FMT>::kNan;
-    o.four = 0;
-  }
-  return o;
-}
-
-// The block as two 16-byte bf16 chunks.
-template <int FMT, int SELECT, int ROUND, bool DIRECT = false>
-__device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2* tab,
-                                                   const TensorScale& ts, uint32_t hbase) {
-  const float x[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                       bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
-                       bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                       bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
-  return quantize_block_x<FMT, SELECT, ROUND, DIRECT>(x, tab, ts, hbase);
-}
-
-// A block (16 values in one lane) quantized with a given block amax instead
-// of its own: 16x16 tile scales, where every row and column block of a tile
-// takes the tile's amax.  Max->6, round-to-nearest-even; a NaN amax (a NaN
-// in the tile) gives the NaN scale code and codes 0.
-template <int FMT>
-__device__ __forceinline__ BlockOut quantize_block_amax(const float (&x)[16], const f32x2* tab,
-                                                        const TensorScale& ts, float amax_t) {
-  BlockOut o;
-  const uint32_t c6 = encode_pair(FMT, amax_t * ts.k6, 0.0f) & 0xFFu;
-  const f32x2 t = tab[c6];
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
-  o.c0 = e2m1_rne_pack8(y);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t[1];
-  o.c1 = e2m1_rne_pack8(y);
-  o.scale = c6;
-  o.four = 0;
-  if (ts.nan || amax_t != amax_t) {
-    o.c0 = 0;
-    o.c1 = 0;
-    o.scale = FmtTraits<FMT>::kNan;
-  }
-  return o;
-}
-
-// NaN-propagating maximum of |x| over a block (a depth-3 tree of maximum3).
-__device__ __forceinline__ float block_absmax(const float (&x)[16]) {
-  const float m0 = max3_abs(x[0], x[1], x[2]), m1 = max3_abs(x[3], x[4], x[5]);
-  const float m2 = max3_abs(x[6], x[7], x[8]), m3 = max3_abs(x[9], x[10], x[11]);
-  const float m4 = max3_abs(x[12], x[13], x[14]);
-  return __builtin_elementwise_maximum(
-      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, m1), m2),
-      __builtin_elementwise_maximum(__builtin_elementwise_maximum(m3, m4), __builtin_fabsf(x[15])));
-}
-
-__device__ __forceinline__ void unpack16(uint4 a, uint4 b, float (&x)[16]) {
-  x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x); x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
-  x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z); x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
-  x[8] = bf16_lo(b.x); x[9] = bf16_hi(b.x); x[10] = bf16_lo(b.y); x[11] = bf16_hi(b.y);
-  x[12] = bf16_lo(b.z); x[13] = bf16_hi(b.z); x[14] = bf16_lo(b.w); x[15] = bf16_hi(b.w);
-}
-
-// Hash base of the 8 elements from index idx0 (a multiple of 8).  WIDE: the
-// tensor has more than 2^32 elements, so the key depends on the high word;
-// otherwise every index has high word 0 and key0 serves.
-template <int ROUND, bool WIDE>
-__device__ __forceinline__ uint32_t hash_base(uint64_t seed, uint64_t idx0, uint32_t key0) {
-  if constexpr (ROUND != ROUND_SR) return 0u;
-  const uint32_t hi = (uint32_t)(idx0 >> 32);
-  const uint32_t key = WIDE ? (hi == 0 ? key0 : sr_key(seed, hi)) : key0;
-  return (uint32_t)idx0 ^ key;
-}
-
-// Adds the per-lane 4/6 counts of the workgroup to *count4 (one atomic).
-// Same-address device atomics serialize (about 8 ns each on MI355X), so the
-// launchers keep the grid of a counting launch to about one workgroup per CU.
-template <int BLOCK>
-__device__ __forceinline__ void flush_count(unsigned long long* count4, uint32_t n4) {
-  __shared__ uint32_t red[BLOCK / 64];
-  for (int off = 32; off >= 1; off >>= 1) n4 += (uint32_t)__shfl_xor((int)n4, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = n4;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long t = 0;
-    for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
-    if (t) atomicAdd(count4, t);
-  }
-}
 
 // ---------------------------------------------------------------- row-wise
 // Workgroup tile = 256 lanes x kRowUnroll chunks; full tiles run without
@@ -403,22 +86,6 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
   if (SELECT == SELECT_4OVER6 && count4) flush_count<BLOCK>(count4, n4);
 }
 
-// Writes the wavefront's 128 chunks (lane l: chunks l and 64 + l) to its LDS
-// region so that lane l can read chunks 2l and 2l + 1 back.  The fences
-// and wave barriers keep the compiler from moving LDS accesses across them
-// (the hardware runs one wavefront's LDS operations in order): the previous
-// group's reads happen before the region is overwritten, the writes before
-// the reads that follow.
-__device__ __forceinline__ void bounce_pair(uint4* reg, int l, uint4 a, uint4 b) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  reg[l] = a;
-  reg[64 + l] = b;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Row-wise, one lane per block (Four-Over-Six and stochastic rounding, whose
 // per-block work dominates).  A wavefront handles groups of 64 blocks (128
@@ -811,19 +478,6 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
 }
 
 // ---------------------------------------------------------------- dispatch
-// Workgroups of kThreads lanes of kernel KERN one CU holds at once (its
-// register and LDS use), at least 1; looked up once per kernel.
-template <auto KERN>
-static int resident_per_cu() {
-  static std::atomic<int> cached{0};
-  int n = cached.load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERN, kThreads, 0) != hipSuccess || n < 1)
-      n = 1;
-    cached.store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 template <int FMT, int SELECT, int ROUND, bool WIDE>
 static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {

@@ -89,6 +89,22 @@ def _load():
     lib.or_quantize_2d.restype = ctypes.c_int
     lib.or_quantize_2d.argtypes = [_f32p, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                    ctypes.c_int, _u8p, _u8p, _u8p, _u8p]
+    lib.or_dequantized_amax.restype = ctypes.c_float
+    lib.or_dequantized_amax.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, _f32p,
+                                        ctypes.c_float, ctypes.c_int]
+    lib.or_requant_nvfp4_t.restype = ctypes.c_int
+    lib.or_requant_nvfp4_t.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, _f32p,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_uint64, _u8p, _u8p]
+    lib.or_requant_mxfp8_t.restype = ctypes.c_int
+    lib.or_requant_mxfp8_t.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, _f32p,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_uint64, _u8p, _u8p]
+    lib.or_e4m3_code_sr.restype = ctypes.c_int
+    lib.or_e4m3_code_sr.argtypes = [ctypes.c_float, ctypes.c_uint32]
+    lib.or_mxfp8_quantize_sr.restype = ctypes.c_int
+    lib.or_mxfp8_quantize_sr.argtypes = [_f32p, _i64, _i64, _i64, ctypes.c_uint64, _u8p, _u8p]
+    lib.or_mxfp8_dequantize.restype = ctypes.c_int
+    lib.or_mxfp8_dequantize.argtypes = [_u8p, _u8p, _i64, _i64, _f32p]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_num_threads.argtypes = []
     _lib = lib
@@ -362,3 +378,86 @@ def quantize_2d(x, amax, *, fmt=FMT_E4M3, global_max=None, want_t=True):
     if st != 0:
         raise ValueError(f"oracle quantize_2d rejected the arguments (status {st})")
     return (codes, scales, codes_t, scales_t) if want_t else (codes, scales)
+
+
+# ---------------------------------------------------------------- re-quantization
+def _source(codes, scales, amax, row_amaxes, fmt, select, global_max):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, half = codes.shape
+    assert (amax is None) != (row_amaxes is None), "one outer amax or one per row"
+    ra = None if row_amaxes is None else np.ascontiguousarray(np.asarray(row_amaxes, np.float32))
+    assert ra is None or ra.shape == (rows,)
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, select) if global_max is None else float(global_max)
+    return codes, scales, rows, half * 2, (0.0 if amax is None else float(amax)), ra, sg, fmt
+
+
+def dequantized_amax(codes, scales, *, amax=None, row_amaxes=None, fmt=FMT_E4M3,
+                     select=SELECT_4OVER6, global_max=None):
+    """max |x_hat| of an NVFP4 tensor (per-tensor amax, or one per row)."""
+    codes, scales, rows, cols, a, ra, sg, fmt = _source(codes, scales, amax, row_amaxes, fmt,
+                                                         select, global_max)
+    return _load().or_dequantized_amax(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, a,
+                                       _ptr(ra, _f32p), sg, fmt)
+
+
+def requant_t(codes, scales, *, amax=None, row_amaxes=None, fmt=FMT_E4M3, select=SELECT_4OVER6,
+              global_max=None, target="nvfp4", dst_amax=None, dst_fmt=FMT_E4M3,
+              dst_global_max=None, seed=0):
+    """Dequantize an NVFP4 tensor, transpose, re-quantize with stochastic
+    rounding.  target "nvfp4": returns (codes_t [cols, rows/2], scales_t
+    [cols, rows/16]) under outer amax dst_amax; "mxfp8": returns (elems_t
+    [cols, rows] E4M3 bytes, scales_t [cols, rows/32] E8M0 bytes)."""
+    codes, scales, rows, cols, a, ra, sg, fmt = _source(codes, scales, amax, row_amaxes, fmt,
+                                                         select, global_max)
+    lib = _load()
+    if target == "nvfp4":
+        dfmt = _fmt(dst_fmt)
+        dsg = default_global_max(dfmt, SELECT_6) if dst_global_max is None else float(dst_global_max)
+        ct = np.empty((cols, rows // 2), np.uint8)
+        st_ = np.empty((cols, rows // 16), np.uint8)
+        st = lib.or_requant_nvfp4_t(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, a,
+                                    _ptr(ra, _f32p), sg, fmt, float(dst_amax), dsg, dfmt,
+                                    int(seed), _ptr(ct, _u8p), _ptr(st_, _u8p))
+    elif target == "mxfp8":
+        ct = np.empty((cols, rows), np.uint8)
+        st_ = np.empty((cols, rows // 32), np.uint8)
+        st = lib.or_requant_mxfp8_t(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, a,
+                                    _ptr(ra, _f32p), sg, fmt, int(seed), _ptr(ct, _u8p),
+                                    _ptr(st_, _u8p))
+    else:
+        raise ValueError(f"unknown target {target!r}")
+    if st != 0:
+        raise ValueError(f"oracle requant_t rejected the arguments (status {st})")
+    return ct, st_
+
+
+def e4m3_code_sr(y, h):
+    return _load().or_e4m3_code_sr(float(y), int(h) & 0xFFFFFFFF)
+
+
+def mxfp8_quantize_sr(x, *, seed=0, row0=0):
+    """MXFP8 (blocks of 32 along rows, E8M0 scale, E4M3 elements) with
+    stochastic rounding.  Returns (elems [rows, cols], scales [rows, cols/32])."""
+    xf = as_f32(x)
+    assert xf.ndim == 2
+    rows, cols = xf.shape
+    el = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, cols // 32), np.uint8)
+    st = _load().or_mxfp8_quantize_sr(_ptr(xf, _f32p), rows, cols, int(row0), int(seed),
+                                      _ptr(el, _u8p), _ptr(sc, _u8p))
+    if st != 0:
+        raise ValueError(f"oracle mxfp8_quantize_sr rejected the arguments (status {st})")
+    return el, sc
+
+
+def mxfp8_dequantize(elems, scales):
+    el = np.ascontiguousarray(elems, np.uint8)
+    sc = np.ascontiguousarray(scales, np.uint8)
+    rows, cols = el.shape
+    out = np.empty((rows, cols), np.float32)
+    st = _load().or_mxfp8_dequantize(_ptr(el, _u8p), _ptr(sc, _u8p), rows, cols, _ptr(out, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle mxfp8_dequantize rejected the arguments (status {st})")
+    return out

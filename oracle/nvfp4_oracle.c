@@ -492,6 +492,173 @@ int or_dequantize_rowscaled(const uint8_t *codes, const uint8_t *scales, int64_t
   return bad ? OR_EINVAL : OR_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* Re-quantization for the backward pass ([E2E] Re-quantization with
+ * stochastic rounding; the quantized linear layer figure there): a tensor
+ * quantized for the forward pass is dequantized, transposed in that higher
+ * precision, and quantized again along the other dimension with stochastic
+ * rounding, so that the backward pass sees the forward tensor in
+ * expectation.  The source is the NVFP4 tensor (codes[rows, cols/2],
+ * scales[rows, cols/16]) with one outer amax (row_amax == NULL) or one per
+ * row; x_hat is what or_dequantize computes (q * D * alpha rounded once to
+ * binary32).  Targets: NVFP4 (the max->6 quantizer of this file with SR) or
+ * MXFP8 (the pages' choice for the backward GEMMs). */
+static float *dequant_source(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                             int64_t cols, float amax, const float *row_amax, float sg, int fmt) {
+  float *x = (float *)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+  int bad = row_amax ? or_dequantize_rowscaled(codes, scales, rows, cols, row_amax, sg, fmt, x, NULL, NULL)
+                     : or_dequantize(codes, scales, rows, cols, amax, sg, fmt, x, NULL, NULL);
+  if (bad) { free(x); return NULL; }
+  return x;
+}
+
+static float *transpose_f32(const float *x, int64_t rows, int64_t cols) {
+  float *t = (float *)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) t[c * rows + r] = x[r * cols + c];
+  return t;
+}
+
+/* Amax of the dequantized tensor (current scaling of the re-quantized
+ * tensor): max |x_hat|, NaN if any x_hat is NaN. */
+float or_dequantized_amax(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                          float amax, const float *row_amax, float sg, int fmt) {
+  float *x = dequant_source(codes, scales, rows, cols, amax, row_amax, sg, fmt);
+  if (!x) return NAN;
+  float m = or_tensor_amax(x, rows * cols);
+  free(x);
+  return m;
+}
+
+/* NVFP4 target: X_hat^T [cols, rows] quantized row-wise (blocks of 16 source
+ * rows of one column) with max->6 and SR, outer amax dst_amax with S_g =
+ * dst_sg; SR index = the element's index in X_hat^T (c * rows + r).
+ * rows % 16 == 0.  codes_t[cols, rows/2], scales_t[cols, rows/16]. */
+int or_requant_nvfp4_t(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                       float amax, const float *row_amax, float sg, int fmt, float dst_amax,
+                       float dst_sg, int dst_fmt, uint64_t seed, uint8_t *codes_t,
+                       uint8_t *scales_t) {
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return OR_EINVAL;
+  float *x = dequant_source(codes, scales, rows, cols, amax, row_amax, sg, fmt);
+  if (!x) return OR_EINVAL;
+  float *t = transpose_f32(x, rows, cols);
+  free(x);
+  int st = or_quantize(t, cols, rows, 0, dst_amax, dst_sg, dst_fmt, OR_SELECT_6, OR_ROUND_SR, seed,
+                       codes_t, scales_t, NULL, NULL, NULL);
+  free(t);
+  return st;
+}
+
+/* MXFP8 (OCP Microscaling; the pages name the format only): blocks of 32
+ * consecutive elements share one E8M0 scale X = 2^e, elements are E4M3
+ * (OCP E4M3FN, the byte of the block-scale format above) of x / X.
+ *   e = floor(log2(amax_b)) - 8, clamped below at -127 (amax_b = 0 gives
+ *       -127): 8 is the exponent of E4M3's largest binade, so the block's
+ *       largest element lands in [256, 512);
+ *   scale byte = e + 127;
+ *   y_i = fl(x_i * 2^-e) (binary32), magnitudes above 448 saturate to 448;
+ *   element = SR of y_i onto the E4M3 grid (or_e4m3_code_sr).
+ * A block holding a NaN, or an infinity, has no representable scale: its
+ * scale byte is 0xFF (E8M0's NaN) and its elements 0.
+ *
+ * Stochastic rounding onto E4M3 (the rule of gfx950's SR conversion to FP8,
+ * of the same form as or_e2m1_code_sr with E4M3's 20 discarded mantissa
+ * bits): with lo / hi the grid neighbours of a = |y| and p = (a - lo) /
+ * (hi - lo), F = floor(p * 2^20) and u = h >> 12, round up iff
+ * u + F >= 2^20.  a >= 448 gives 448; the sign is kept (-0 -> 0x80). */
+static int e4m3_code_sr_tab(const double *dec, float y, uint32_t h) {
+  int sign = signbit(y) ? 0x80 : 0;
+  double a = fabs((double)y);
+  if (a >= 448.0) return sign | 0x7E;
+  int lo = 0;
+  while (lo < 0x7E && dec[lo + 1] <= a) ++lo;
+  uint32_t F = (uint32_t)floor((a - dec[lo]) / (dec[lo + 1] - dec[lo]) * 1048576.0); /* exact */
+  uint32_t u = h >> 12;
+  return sign | ((u + F >= (1u << 20)) ? lo + 1 : lo);
+}
+
+int or_e4m3_code_sr(float y, uint32_t h) {
+  double dec[256];
+  scale_table(OR_FMT_E4M3, dec);
+  return e4m3_code_sr_tab(dec, y, h);
+}
+
+int or_mxfp8_quantize_sr(const float *x, int64_t rows, int64_t cols, int64_t row0, uint64_t seed,
+                         uint8_t *elems, uint8_t *scales) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return OR_EINVAL;
+  const int64_t nb = cols / 32;
+  double dec[256];
+  scale_table(OR_FMT_E4M3, dec);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float *xb = x + r * cols + b * 32;
+      uint8_t *eb = elems + r * cols + b * 32;
+      float amax_b = 0.0f;
+      int bad = 0;
+      for (int i = 0; i < 32; ++i) {
+        if (isnan(xb[i]) || isinf(xb[i])) bad = 1;
+        else if (fabsf(xb[i]) > amax_b) amax_b = fabsf(xb[i]);
+      }
+      if (bad) {
+        scales[r * nb + b] = 0xFF;
+        memset(eb, 0, 32);
+        continue;
+      }
+      int e = -127;
+      if (amax_b > 0.0f) {
+        int ex;
+        frexpf(amax_b, &ex); /* amax_b = m * 2^ex, m in [0.5, 1): floor(log2) = ex - 1 */
+        e = ex - 1 - 8;
+        if (e < -127) e = -127;
+      }
+      scales[r * nb + b] = (uint8_t)(e + 127);
+      const float inv = ldexpf(1.0f, -e);
+      for (int i = 0; i < 32; ++i) {
+        float y = xb[i] * inv;
+        uint64_t idx = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(b * 32 + i);
+        eb[i] = (uint8_t)e4m3_code_sr_tab(dec, y, or_sr_hash(seed, idx));
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* MXFP8 decode: E4M3 element value * 2^(scale - 127), rounded once to
+ * binary32; NaN for scale 0xFF or a NaN element. */
+int or_mxfp8_dequantize(const uint8_t *elems, const uint8_t *scales, int64_t rows, int64_t cols,
+                        float *out) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return OR_EINVAL;
+  const int64_t nb = cols / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      int sc = scales[r * nb + c / 32], el = elems[r * cols + c];
+      if (sc == 0xFF || (el & 0x7F) == 0x7F) {
+        out[r * cols + c] = NAN;
+        continue;
+      }
+      double v = or_scale_decode(OR_FMT_E4M3, el & 0x7F) * ldexp(1.0, sc - 127);
+      out[r * cols + c] = (float)((el & 0x80) ? -v : v);
+    }
+  return OR_OK;
+}
+
+/* MXFP8 target: X_hat^T [cols, rows] quantized to MXFP8 with SR along its
+ * rows (blocks of 32 source rows of one column); rows % 32 == 0.
+ * elems_t[cols, rows] (E4M3 bytes), scales_t[cols, rows/32] (E8M0). */
+int or_requant_mxfp8_t(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                       float amax, const float *row_amax, float sg, int fmt, uint64_t seed,
+                       uint8_t *elems_t, uint8_t *scales_t) {
+  if (rows < 0 || cols < 0 || rows % 32 != 0 || cols % 16 != 0) return OR_EINVAL;
+  float *x = dequant_source(codes, scales, rows, cols, amax, row_amax, sg, fmt);
+  if (!x) return OR_EINVAL;
+  float *t = transpose_f32(x, rows, cols);
+  free(x);
+  int st = or_mxfp8_quantize_sr(t, cols, rows, 0, seed, elems_t, scales_t);
+  free(t);
+  return st;
+}
+
 /* Sum of squared errors sum (x_i - x_hat_i)^2 in binary64, in index order
  * ([UE] 实现 reports the per-tensor MSE = SSE / n). */
 double or_sse(const float *x, const float *xhat, int64_t n) {

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -259,6 +259,66 @@ int nvfp4_dequantize_rowscaled(const uint8_t* codes, const uint8_t* scales, int6
 int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
                       float global_fp8_max, int scale_fmt, uint8_t* codes, uint8_t* scales,
                       uint8_t* codes_t, uint8_t* scales_t, void* stream);
+
+/*
+ * Re-quantization for the backward pass ("End-to-End 4-Bit Training",
+ * Re-quantization with stochastic rounding, and its quantized-linear-layer
+ * figure): an NVFP4 tensor saved from the forward pass is dequantized
+ * (x_hat = q * D * alpha rounded once to binary32, exactly as
+ * nvfp4_dequantize), transposed, and quantized again along the other
+ * dimension with stochastic rounding, so that the backward pass sees the
+ * forward tensor in expectation.
+ *
+ * Source (both calls): codes [rows, cols/2] (16-byte aligned), scales
+ * [rows, cols/16], scale_fmt and its S_g = global_fp8_max (> 0, the value
+ * the tensor was quantized with), and exactly one of amax (one device float:
+ * per-tensor outer scale) and row_amax ([rows] device floats: per-row outer
+ * scales, as nvfp4_quantize_rowscaled).  cols % 16 == 0.
+ */
+enum { NVFP4_TARGET_NVFP4 = 0, NVFP4_TARGET_MXFP8 = 1 };
+
+/*
+ * nvfp4_dequantized_amax -- *amax_out = max |x_hat| over the tensor (the
+ * current amax of the dequantized tensor, for the outer scale of an NVFP4
+ * re-quantization); NaN if any x_hat is NaN.  amax_out 4-byte aligned.
+ * Errors: NULL or misaligned pointers, both or neither of amax / row_amax,
+ * cols % 16 != 0, unknown scale_fmt, global_fp8_max not > 0 ->
+ * NVFP4_ERR_INVALID.
+ */
+int nvfp4_dequantized_amax(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           const float* amax, const float* row_amax, float global_fp8_max,
+                           int scale_fmt, float* amax_out, void* stream);
+
+/*
+ * nvfp4_requantize_t -- quantize X_hat^T ([cols, rows], row-major) with
+ * stochastic rounding.  The SR variate of an element is the hash of its
+ * index in X_hat^T, c * rows + r, under `seed` (as nvfp4_quantize).
+ *   target NVFP4_TARGET_NVFP4: max->6, E2M1 with SR, outer scale from
+ *     *dst_amax (device float; e.g. from nvfp4_dequantized_amax, or the
+ *     source amax) with S_g = dst_global_fp8_max (0 -> the max->6 default of
+ *     dst_scale_fmt).  rows % 16 == 0.  out_t = codes [cols, rows/2]
+ *     (16-byte aligned), out_scales_t = scales [cols, rows/16].
+ *   target NVFP4_TARGET_MXFP8 (OCP Microscaling, the pages' backward
+ *     format): blocks of 32 source rows of one column; E8M0 scale byte
+ *     e + 127 with e = floor(log2 amax_b) - 8 (at least -127); elements
+ *     x_hat * 2^-e clamped to +-448 and rounded onto E4M3 with SR
+ *     (round up iff (h >> 12) + floor(2^20 p) >= 2^20).  rows % 32 == 0.
+ *     out_t = E4M3 bytes [cols, rows] (16-byte aligned), out_scales_t =
+ *     E8M0 bytes [cols, rows/32].  dst_amax, dst_global_fp8_max and
+ *     dst_scale_fmt are ignored.
+ * NaN rules: a NaN x_hat makes its output block's scale the NaN code (0x7F /
+ * 0xFF for NVFP4, 0xFF for MXFP8) and the block's elements 0; so does an
+ * infinite x_hat for MXFP8 (its E8M0 exponent is not representable); a
+ * negative or non-finite *dst_amax gives NaN scale codes everywhere (NVFP4).
+ * Errors: as nvfp4_dequantized_amax, plus unknown target or dst_scale_fmt,
+ * rows not a multiple of the target's block, NULL or misaligned outputs ->
+ * NVFP4_ERR_INVALID.
+ */
+int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                       const float* amax, const float* row_amax, float global_fp8_max,
+                       int scale_fmt, int target, const float* dst_amax, float dst_global_fp8_max,
+                       int dst_scale_fmt, uint64_t seed, uint8_t* out_t, uint8_t* out_scales_t,
+                       void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(int status);

@@ -30,6 +30,12 @@ int nvfp4_test_scale_encode_range(int fmt, uint32_t first, int64_t n, uint8_t* c
 /* out[i] = 32-bit stochastic-rounding variate of element index idx0 + i. */
 int nvfp4_test_sr_hash(uint64_t seed, uint64_t idx0, int64_t n, uint32_t* out, void* stream);
 
+/* codes[i] = MXFP8 element byte of y[i] (already divided by the block's
+ * power-of-two scale) with 32-bit hash h[i]: clamped to +-448, then E4M3
+ * stochastic rounding, in groups of four through the re-quantizer's packing
+ * routine (every byte position of the instruction); n % 4 == 0. */
+int nvfp4_test_e4m3_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

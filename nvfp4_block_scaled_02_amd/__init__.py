@@ -5,9 +5,9 @@ ABI of include/nvfp4.h); this package is its Python binding.  Importing it
 does not load the library; the first call does, and raises if it is not built.
 """
 from .api import (Quantized, default_global_max, dequantize, dequantize_rowscaled,
-                  fakequant_bwd, fakequant_fwd, quantize, quantize_2d, quantize_rowscaled,
-                  row_amax, tensor_amax)
+                  dequantized_amax, fakequant_bwd, fakequant_fwd, quantize, quantize_2d,
+                  quantize_rowscaled, requantize_t, row_amax, tensor_amax)
 
 __all__ = ["Quantized", "default_global_max", "dequantize", "dequantize_rowscaled",
-           "fakequant_bwd", "fakequant_fwd", "quantize", "quantize_2d", "quantize_rowscaled",
-           "row_amax", "tensor_amax"]
+           "dequantized_amax", "fakequant_bwd", "fakequant_fwd", "quantize", "quantize_2d",
+           "quantize_rowscaled", "requantize_t", "row_amax", "tensor_amax"]

@@ -15,6 +15,7 @@ SCALE_E4M3, SCALE_UE5M3 = 0, 1
 SELECT_6, SELECT_4OVER6 = 0, 1
 ROUND_RNE, ROUND_SR = 0, 1
 AXIS_ROW, AXIS_COL = 1, 2
+TARGET_NVFP4, TARGET_MXFP8 = 0, 1
 
 # name -> (restype, argtypes); the exported surface of include/nvfp4.h and
 # include/nvfp4_testing.h
@@ -40,10 +41,14 @@ SIGNATURES = {
     "nvfp4_quantize_2d": (_int, [_vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_fakequant_fwd": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_fakequant_bwd": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_dequantized_amax": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _f32, _int, _vp, _vp]),
+    "nvfp4_requantize_t": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _f32, _int, _int, _vp, _f32,
+                                  _int, _u64, _vp, _vp, _vp]),
     "nvfp4_test_e2m1_rne_range": (_int, [_u32, _i64, _vp, _vp]),
     "nvfp4_test_e2m1_sr": (_int, [_vp, _vp, _i64, _vp, _vp]),
     "nvfp4_test_scale_encode_range": (_int, [_int, _u32, _i64, _vp, _vp]),
     "nvfp4_test_sr_hash": (_int, [_u64, _u64, _i64, _vp, _vp]),
+    "nvfp4_test_e4m3_sr": (_int, [_vp, _vp, _i64, _vp, _vp]),
 }
 
 _lib = None

@@ -247,6 +247,76 @@ def quantize_2d(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: st
                      gm, fmt, None)
 
 
+# ---------------------------------------------------------------- re-quantization
+_TARGET = {"nvfp4": N.TARGET_NVFP4, "mxfp8": N.TARGET_MXFP8}
+
+
+def _rq_source(codes, scales, amax, row_amaxes):
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if (amax is None) == (row_amaxes is None):
+        raise ValueError("pass exactly one of amax (per tensor) and row_amaxes (per row)")
+    if amax is not None:
+        _need(amax, torch.float32, "amax")
+    else:
+        _need(row_amaxes, torch.float32, "row_amaxes")
+    rows, half = codes.shape
+    return rows, 2 * half
+
+
+def dequantized_amax(codes: torch.Tensor, scales: torch.Tensor, *,
+                     amax: Optional[torch.Tensor] = None,
+                     row_amaxes: Optional[torch.Tensor] = None, global_max: float,
+                     fmt: str = "e4m3", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """max |x_hat| of an NVFP4 tensor (one outer amax, or one per row), as a
+    1-element float32 device tensor."""
+    rows, cols = _rq_source(codes, scales, amax, row_amaxes)
+    dev = codes.device
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=dev)
+    _need(out, torch.float32, "out")
+    st = N.lib().nvfp4_dequantized_amax(_ptr(codes), _ptr(scales), rows, cols, _ptr(amax),
+                                        _ptr(row_amaxes), float(global_max), _FMT[fmt], _ptr(out),
+                                        _stream(dev))
+    N.check(st, "nvfp4_dequantized_amax")
+    return out
+
+
+def requantize_t(codes: torch.Tensor, scales: torch.Tensor, *,
+                 amax: Optional[torch.Tensor] = None, row_amaxes: Optional[torch.Tensor] = None,
+                 global_max: float, fmt: str = "e4m3", target: str = "mxfp8",
+                 dst_amax: Optional[torch.Tensor] = None, dst_fmt: str = "e4m3",
+                 dst_global_max: float = 0.0, seed: int = 0, out: Optional[dict] = None):
+    """Dequantize an NVFP4 tensor, transpose it and re-quantize it with
+    stochastic rounding.  target "mxfp8": returns (elems_t [cols, rows]
+    E4M3 bytes, scales_t [cols, rows/32] E8M0 bytes).  target "nvfp4":
+    returns (codes_t [cols, rows/2], scales_t [cols, rows/16]) under the outer
+    amax dst_amax (default: the dequantized tensor's amax)."""
+    rows, cols = _rq_source(codes, scales, amax, row_amaxes)
+    dev = codes.device
+    out = dict(out or {})
+    if target == "nvfp4":
+        if dst_amax is None:
+            dst_amax = dequantized_amax(codes, scales, amax=amax, row_amaxes=row_amaxes,
+                                        global_max=global_max, fmt=fmt)
+        _need(dst_amax, torch.float32, "dst_amax")
+        out.setdefault("out_t", torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev))
+        out.setdefault("scales_t", torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev))
+    elif target == "mxfp8":
+        out.setdefault("out_t", torch.empty((cols, rows), dtype=torch.uint8, device=dev))
+        out.setdefault("scales_t", torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev))
+    else:
+        raise ValueError(f"unknown target {target!r}")
+    _need(out["out_t"], torch.uint8, "out_t")
+    _need(out["scales_t"], torch.uint8, "scales_t")
+    st = N.lib().nvfp4_requantize_t(
+        _ptr(codes), _ptr(scales), rows, cols, _ptr(amax), _ptr(row_amaxes), float(global_max),
+        _FMT[fmt], _TARGET[target], _ptr(dst_amax), float(dst_global_max), _FMT[dst_fmt],
+        int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out["out_t"]), _ptr(out["scales_t"]), _stream(dev))
+    N.check(st, "nvfp4_requantize_t")
+    return out["out_t"], out["scales_t"]
+
+
 def fakequant_fwd(x: torch.Tensor, s_pre: torch.Tensor, s_post: Optional[torch.Tensor] = None,
                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """x~ = s_post * clamp(round_E2M1(x / s_pre), -6, 6) per 16-element block."""

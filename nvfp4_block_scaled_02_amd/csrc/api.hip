@@ -244,6 +244,62 @@ int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float
   return status_of(launch_quantize_2d(a, (hipStream_t)stream));
 }
 
+static int rq_source(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     const float* amax, const float* row_amax, float global_fp8_max,
+                     int scale_fmt) {
+  if (!codes || !scales || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
+  if ((amax == nullptr) == (row_amax == nullptr)) return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (!aligned16(codes) || ((uintptr_t)amax & 3u) || ((uintptr_t)row_amax & 3u))
+    return NVFP4_ERR_INVALID;
+  return NVFP4_OK;
+}
+
+int nvfp4_dequantized_amax(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           const float* amax, const float* row_amax, float global_fp8_max,
+                           int scale_fmt, float* amax_out, void* stream) {
+  const int st = rq_source(codes, scales, rows, cols, amax, row_amax, global_fp8_max, scale_fmt);
+  if (st != NVFP4_OK) return st;
+  if (!amax_out || ((uintptr_t)amax_out & 3u)) return NVFP4_ERR_INVALID;
+  RequantArgs a = {};
+  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols;
+  a.amax = amax; a.row_amax = row_amax; a.sg = global_fp8_max; a.fmt = scale_fmt;
+  return status_of(launch_dequantized_amax(a, amax_out, (hipStream_t)stream));
+}
+
+int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                       const float* amax, const float* row_amax, float global_fp8_max,
+                       int scale_fmt, int target, const float* dst_amax, float dst_global_fp8_max,
+                       int dst_scale_fmt, uint64_t seed, uint8_t* out_t, uint8_t* out_scales_t,
+                       void* stream) {
+  const int st = rq_source(codes, scales, rows, cols, amax, row_amax, global_fp8_max, scale_fmt);
+  if (st != NVFP4_OK) return st;
+  if (!out_t || !out_scales_t || !aligned16(out_t)) return NVFP4_ERR_INVALID;
+  if (target == NVFP4_TARGET_NVFP4) {
+    if (rows % 16 != 0 || !dst_amax || ((uintptr_t)dst_amax & 3u)) return NVFP4_ERR_INVALID;
+    if (dst_scale_fmt != NVFP4_SCALE_E4M3 && dst_scale_fmt != NVFP4_SCALE_UE5M3)
+      return NVFP4_ERR_INVALID;
+    if (!(dst_global_fp8_max >= 0.0f) || isinf(dst_global_fp8_max)) return NVFP4_ERR_INVALID;
+  } else if (target == NVFP4_TARGET_MXFP8) {
+    if (rows % 32 != 0) return NVFP4_ERR_INVALID;
+  } else {
+    return NVFP4_ERR_INVALID;
+  }
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  RequantArgs a = {};
+  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols;
+  a.amax = amax; a.row_amax = row_amax; a.sg = global_fp8_max; a.fmt = scale_fmt;
+  a.target = target; a.seed = seed; a.out_t = out_t; a.out_scales_t = out_scales_t;
+  if (target == NVFP4_TARGET_NVFP4) {
+    a.dst_amax = dst_amax; a.dst_fmt = dst_scale_fmt;
+    a.dst_sg = resolve_sg(dst_global_fp8_max, dst_scale_fmt, NVFP4_SELECT_6);
+  } else {
+    a.dst_amax = nullptr; a.dst_fmt = FMT_E4M3; a.dst_sg = 0.0f;
+  }
+  return status_of(launch_requant_t(a, (hipStream_t)stream));
+}
+
 static int fq_common(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre) {
   if (!x || !s_pre || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
   if (!aligned16(x) || ((uintptr_t)s_pre & 3u)) return NVFP4_ERR_INVALID;
@@ -310,6 +366,12 @@ int nvfp4_test_scale_encode_range(int fmt, uint32_t first, int64_t n, uint8_t* c
     hipLaunchKernelGGL(test_scale_range_kernel<FMT_UE5M3>, dim3(test_grid(n)), dim3(256), 0,
                        (hipStream_t)stream, first, n, codes);
   return status_of(hipGetLastError());
+}
+
+int nvfp4_test_e4m3_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, void* stream) {
+  if (n < 0 || n % 4 != 0 || (n > 0 && (!y || !h || !codes))) return NVFP4_ERR_INVALID;
+  if (n == 0) return NVFP4_OK;
+  return status_of(launch_test_e4m3_sr(y, h, n, codes, (hipStream_t)stream));
 }
 
 int nvfp4_test_sr_hash(uint64_t seed, uint64_t idx0, int64_t n, uint32_t* out, void* stream) {

@@ -51,6 +51,23 @@ struct FakeQuantArgs {
   float *dx, *ds_pre, *ds_post;
 };
 
+// Re-quantization of an NVFP4 tensor: dequantize, transpose, quantize again
+// with stochastic rounding (target 0 = NVFP4, 1 = MXFP8).
+struct RequantArgs {
+  const uint8_t *codes, *scales;  // source [rows, cols/2], [rows, cols/16]
+  int64_t rows, cols;
+  const float* amax;      // per-tensor outer amax, or nullptr
+  const float* row_amax;  // one outer amax per row, or nullptr
+  float sg;               // resolved S_g of the source
+  int fmt;                // source scale format
+  int target;
+  const float* dst_amax;  // NVFP4 target: outer amax of the re-quantized tensor
+  float dst_sg;
+  int dst_fmt;
+  uint64_t seed;
+  uint8_t *out_t, *out_scales_t;
+};
+
 // Launchers (one translation unit each); return the hipError_t of the launch.
 hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipStream_t s);
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
@@ -62,6 +79,11 @@ hipError_t launch_quantize_2d(const QuantizeArgs& a, hipStream_t s);
 hipError_t launch_dequantize(const DequantizeArgs& a, hipStream_t s);
 hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s);
 hipError_t launch_fakequant_bwd(const FakeQuantArgs& a, hipStream_t s);
+hipError_t launch_requant_t(const RequantArgs& a, hipStream_t s);
+hipError_t launch_dequantized_amax(const RequantArgs& a, float* out, hipStream_t s);
+// test hook: E4M3 SR element bytes through the re-quantizer's packing routine
+hipError_t launch_test_e4m3_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes,
+                               hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

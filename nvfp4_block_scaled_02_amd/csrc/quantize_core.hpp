@@ -359,4 +359,64 @@ static int resident_per_cu() {
   return n;
 }
 
+// ---------------------------------------------------------------- column-wise staging
+// Column-wise outputs of a strip walker (a workgroup owns a strip of kSW
+// columns and walks down it in tiles of kTR rows) are staged in LDS and
+// written as 64-byte pieces per column: codes every kCtTiles tiles, scale
+// bytes every kStTiles tiles (and at the end of the walk).  Pieces below 64
+// bytes, or 32-byte pieces written at different times, cost extra DRAM
+// writes and bandwidth on MI355X.
+constexpr int kSW = 128;                        // strip width (columns)
+constexpr int kTR = 32;                         // tile height (rows)
+constexpr int kTilePitch = kSW * 2 + 16;         // LDS row pitch (bytes), padded
+constexpr int kCtTiles = 4;                     // codes_t: 4 tiles = 64 bytes per column
+constexpr int kCtWords = kCtTiles * kTR / 8;    // 16 code words per column per stage
+constexpr int kCtPitch = kCtWords + 1;          // LDS pitch (words), padded
+constexpr int kStTiles = 32;                    // scales_t: 32 tiles = 64 bytes per column
+constexpr int kStBytes = kStTiles * kTR / 16;   // 64 scale bytes per column per stage
+constexpr int kStPitch = kStBytes + 4;          // LDS pitch (bytes), padded
+
+// Writes the staged column-wise bytes of tile rows [t_lo, t_hi) (absolute
+// tile indices within one stage) of the strip at c0.  Only rows < rows and
+// columns < cols are written.  Consecutive lanes write consecutive words (or
+// bytes) of one column, so a wavefront store covers whole 64-byte pieces.
+__device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __restrict__ codes_t,
+                                              int64_t rows, int64_t cols, int64_t c0,
+                                              int64_t t_lo, int64_t t_hi) {
+  const int64_t row0 = (t_lo / kCtTiles) * kCtTiles * kTR;  // stage origin (rows)
+  const int w_lo = (int)(t_lo % kCtTiles) * (kTR / 8);
+  int64_t w_end = (rows - row0) / 8;  // words (8 rows each) inside the tensor
+  int w_hi = (int)((t_hi - 1) % kCtTiles + 1) * (kTR / 8);
+  if (w_end < w_hi) w_hi = (int)w_end;
+  const int64_t stride = rows >> 1;
+  // rolled: the flush runs once per stage, and unrolling lets the compiler
+  // keep every per-lane address live across the whole walk
+#pragma unroll 1
+  for (int u = 0; u < kSW * kCtWords / kThreads; ++u) {
+    const int j = u * kThreads + threadIdx.x;
+    const int col = j / kCtWords, wd = j % kCtWords;
+    if (wd >= w_lo && wd < w_hi && c0 + col < cols)
+      *reinterpret_cast<uint32_t*>(codes_t + (c0 + col) * stride + (row0 >> 1) + wd * 4) =
+          ct[col * kCtPitch + wd];
+  }
+}
+
+__device__ __forceinline__ void flush_scales_t(const uint8_t* st, uint8_t* __restrict__ scales_t,
+                                               int64_t rows, int64_t cols, int64_t c0,
+                                               int64_t t_lo, int64_t t_hi) {
+  const int64_t row0 = (t_lo / kStTiles) * kStTiles * kTR;
+  const int b_lo = (int)(t_lo % kStTiles) * (kTR / 16);
+  int64_t b_end = (rows - row0) / 16;
+  int b_hi = (int)((t_hi - 1) % kStTiles + 1) * (kTR / 16);
+  if (b_end < b_hi) b_hi = (int)b_end;
+  const int64_t stride = rows >> 4;
+#pragma unroll 1
+  for (int u = 0; u < kSW * kStBytes / kThreads; ++u) {
+    const int j = u * kThreads + threadIdx.x;
+    const int col = j / kStBytes, b = j % kStBytes;
+    if (b >= b_lo && b < b_hi && c0 + col < cols)
+      scales_t[(c0 + col) * stride + (row0 >> 4) + b] = st[col * kStPitch + b];
+  }
+}
+
 }  // namespace nvfp4

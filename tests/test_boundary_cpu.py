@@ -27,7 +27,7 @@ def _declared():
 
 def test_library_loads_and_version():
     lib = N.lib()
-    assert lib.nvfp4_abi_version() == 2
+    assert lib.nvfp4_abi_version() == 3
 
 
 def test_every_declared_symbol_is_exported_and_bound():
@@ -196,6 +196,45 @@ def test_quantize_2d_empty_ok():
     assert _q2d(codes_t=None, scales_t=None, rows=0) == N.OK
 
 
+def _rq(**kw):
+    a = dict(codes=FAKE, scales=FAKE, rows=64, cols=32, amax=FAKE, ra=None, gmax=448.0, fmt=0,
+             target=1, dst=FAKE, dgmax=0.0, dfmt=0, seed=0, out=FAKE, out_s=FAKE)
+    a.update(kw)
+    return N.lib().nvfp4_requantize_t(a["codes"], a["scales"], a["rows"], a["cols"], a["amax"],
+                                      a["ra"], a["gmax"], a["fmt"], a["target"], a["dst"],
+                                      a["dgmax"], a["dfmt"], a["seed"], a["out"], a["out_s"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(codes=None), dict(scales=None), dict(amax=None), dict(ra=FAKE), dict(cols=24),
+    dict(rows=-32), dict(fmt=5), dict(gmax=0.0), dict(gmax=float("inf")), dict(target=2),
+    dict(rows=48), dict(target=0, rows=40), dict(target=0, dst=None), dict(target=0, dfmt=3),
+    dict(target=0, dgmax=-1.0), dict(out=None), dict(out_s=None), dict(out=FAKE_ODD),
+    dict(codes=FAKE_ODD), dict(amax=FAKE + 2), dict(amax=None, ra=FAKE + 2),
+])
+def test_requantize_t_rejects(kw):
+    assert _rq(**kw) == N.ERR_INVALID
+
+
+def test_requantize_t_empty_ok():
+    assert _rq(rows=0) == N.OK
+    assert _rq(cols=0, target=0, rows=48) == N.OK
+    assert _rq(amax=None, ra=FAKE, rows=0) == N.OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(codes=None), dict(amax=None), dict(ra=FAKE), dict(cols=8), dict(fmt=4), dict(gmax=-1.0),
+    dict(out=None), dict(out=FAKE + 1),
+])
+def test_dequantized_amax_rejects(kw):
+    a = dict(codes=FAKE, scales=FAKE, rows=16, cols=32, amax=FAKE, ra=None, gmax=448.0, fmt=0,
+             out=FAKE)
+    a.update(kw)
+    assert N.lib().nvfp4_dequantized_amax(a["codes"], a["scales"], a["rows"], a["cols"],
+                                          a["amax"], a["ra"], a["gmax"], a["fmt"], a["out"],
+                                          None) == N.ERR_INVALID
+
+
 def test_test_hooks_reject():
     lib = N.lib()
     assert lib.nvfp4_test_e2m1_rne_range(1, (1 << 32), FAKE, None) == N.ERR_INVALID
@@ -203,6 +242,8 @@ def test_test_hooks_reject():
     assert lib.nvfp4_test_scale_encode_range(7, 0, 2, FAKE, None) == N.ERR_INVALID
     assert lib.nvfp4_test_e2m1_sr(None, FAKE, 4, FAKE, None) == N.ERR_INVALID
     assert lib.nvfp4_test_sr_hash(0, 0, -1, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_test_e4m3_sr(FAKE, FAKE, 6, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_test_e4m3_sr(FAKE, None, 4, FAKE, None) == N.ERR_INVALID
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -50,6 +50,9 @@ B_AMAX = 2.0                    # bf16 read
 B_QUANT = 2.0 + 0.5 + 1 / 16    # bf16 read, 4-bit codes + 1 scale byte per 16
 B_DEQ_MSE = 0.5 + 1 / 16 + 2.0 + 4.0  # codes + scales + bf16 read, f32 written
 B_DEQ = 0.5 + 1 / 16 + 4.0
+B_RQ_MX = 0.5 + 1 / 16 + 1.0 + 1 / 32   # NVFP4 codes + scales read, E4M3 + E8M0 written
+B_RQ_NV = 0.5 + 1 / 16 + 0.5 + 1 / 16   # NVFP4 read, NVFP4 (transposed) written
+B_DQ_AMAX = 0.5 + 1 / 16                # NVFP4 read
 B_FQ_FWD = {"tied": 2.0 + 0.25 + 4.0, "dual": 2.0 + 0.5 + 4.0}
 B_FQ_BWD = {"tied": 2.0 + 4.0 + 0.25 + 4.0 + 0.25, "dual": 2.0 + 4.0 + 0.5 + 4.0 + 0.5}
 B_FUSED = 2.0 + 2 * (0.5 + 1 / 16)
@@ -435,6 +438,67 @@ def run_weight_2d(args, torch, np, nv, synth, dev, timer):
     return finish(line, kernels, args)
 
 
+def run_requant(args, torch, np, nv, synth, dev, timer):
+    """Re-quantization of the saved activation for the backward pass: the
+    8192x4096 activation quantized per token with Four-Over-Six (outside the
+    timed region), then dequantize -> transpose -> SR re-quantize to MXFP8
+    (the step), and to NVFP4 with the dequantized amax."""
+    nsets = 8
+    xb = synth.make("activation")["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    x0 = to_dev(torch, np, xb, dev)
+    gm = nv.default_global_max("e4m3", "4over6")
+    src = []
+    for _ in range(nsets):
+        ra = nv.row_amax(x0)
+        q = nv.quantize_rowscaled(x0, ra, select="4over6")
+        src.append((q.codes, q.scales, ra))
+    mx = [(torch.empty((cols, rows), dtype=torch.uint8, device=dev),
+           torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)) for _ in range(nsets)]
+    nvo = [(torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev),
+            torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev)) for _ in range(nsets)]
+    dqa = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    for i in range(nsets):
+        nv.dequantized_amax(src[i][0], src[i][1], row_amaxes=src[i][2], global_max=gm, out=dqa[i])
+    del x0
+
+    def rq_mx(i):
+        c, s, ra = src[i % nsets]
+        nv.requantize_t(c, s, row_amaxes=ra, global_max=gm, target="mxfp8", seed=1234,
+                        out={"out_t": mx[i % nsets][0], "scales_t": mx[i % nsets][1]})
+
+    def rq_nv(i):
+        c, s, ra = src[i % nsets]
+        nv.requantize_t(c, s, row_amaxes=ra, global_max=gm, target="nvfp4", seed=1234,
+                        dst_amax=dqa[i % nsets],
+                        out={"out_t": nvo[i % nsets][0], "scales_t": nvo[i % nsets][1]})
+
+    def dq_amax(i):
+        c, s, ra = src[i % nsets]
+        nv.dequantized_amax(c, s, row_amaxes=ra, global_max=gm, out=dqa[i % nsets])
+
+    if args.profile_once:
+        profile_once(torch, dev, [rq_mx, dq_amax, rq_nv], nsets)
+        return None
+    reps = max(args.steps, 40)
+    us = {"requant_t_mxfp8_sr": timer.avg_us(rq_mx, reps, nsets),
+          "dequantized_amax": timer.avg_us(dq_amax, reps, nsets),
+          "requant_t_nvfp4_sr": timer.avg_us(rq_nv, reps, nsets)}
+    bpe = {"requant_t_mxfp8_sr": B_RQ_MX, "dequantized_amax": B_DQ_AMAX,
+           "requant_t_nvfp4_sr": B_RQ_NV}
+    kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
+    ms_step = us["requant_t_mxfp8_sr"] / 1e3
+    line = base_line("NVFP4 -> MXFP8 transposed SR re-quantization GB/s at 8192x4096",
+                     n * B_RQ_MX / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     "activation 8192x4096 (seed 2) quantized per token with Four-Over-Six "
+                     "(E4M3, FP8 max 256); dequantize -> transpose -> MXFP8 (E8M0 / E4M3) "
+                     "with SR seed 1234", {"rows": rows, "cols": cols, "elements": n}, n)
+    return finish(line, {"requant_t_mxfp8_sr": kernels["requant_t_mxfp8_sr"],
+                         "requant_t_nvfp4_sr": kernels["requant_t_nvfp4_sr"],
+                         "dequantized_amax": kernels["dequantized_amax"]}, args)
+
+
 def run_gradient(args, torch, np, nv, synth, dev, timer):
     log("generating the 16384x8192 gradient")
     xb = synth.make("gradient")["x"]
@@ -492,7 +556,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="activation",
                     choices=["activation", "weight-1k", "weight", "qat", "gradient",
-                             "activation-pertoken", "weight-2d"])
+                             "activation-pertoken", "weight-2d", "requant"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 256 MiB copy and each kernel of the workload twice (for PMC counters)")
@@ -522,6 +586,8 @@ def main():
         line = run_activation_pertoken(args, torch, np, nv, synth, dev, timer)
     elif args.workload == "weight-2d":
         line = run_weight_2d(args, torch, np, nv, synth, dev, timer)
+    elif args.workload == "requant":
+        line = run_requant(args, torch, np, nv, synth, dev, timer)
     else:
         line = run_gradient(args, torch, np, nv, synth, dev, timer)
     if line is not None:

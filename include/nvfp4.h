@@ -270,7 +270,7 @@ int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float
  * forward tensor in expectation.
  *
  * Source (both calls): codes [rows, cols/2] (16-byte aligned), scales
- * [rows, cols/16], scale_fmt and its S_g = global_fp8_max (> 0, the value
+ * [rows, cols/16] (2-byte aligned), scale_fmt and its S_g = global_fp8_max (> 0, the value
  * the tensor was quantized with), and exactly one of amax (one device float:
  * per-tensor outer scale) and row_amax ([rows] device floats: per-row outer
  * scales, as nvfp4_quantize_rowscaled).  cols % 16 == 0.

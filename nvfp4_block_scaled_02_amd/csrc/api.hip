@@ -251,7 +251,8 @@ static int rq_source(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
   if ((amax == nullptr) == (row_amax == nullptr)) return NVFP4_ERR_INVALID;
   if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
   if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
-  if (!aligned16(codes) || ((uintptr_t)amax & 3u) || ((uintptr_t)row_amax & 3u))
+  if (!aligned16(codes) || ((uintptr_t)scales & 1u) || ((uintptr_t)amax & 3u) ||
+      ((uintptr_t)row_amax & 3u))
     return NVFP4_ERR_INVALID;
   return NVFP4_OK;
 }

@@ -96,6 +96,17 @@ __device__ __forceinline__ double shift1_in_quad_f64(double v) {
 // Exact decode of byte `sel` of a packed word into {low nibble, high nibble}.
 #define NVFP4_DEC_PK_FP4(word, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((word), 1.0f, (sel))
 
+// Workgroup barrier that orders LDS only: fences scoped to the workgroup and
+// to the local (LDS) address space wait for this wavefront's LDS operations
+// (lgkmcnt) but not for its global loads, so loads issued before the barrier
+// stay in flight across it (__syncthreads() would wait for them).  Global
+// memory is not ordered by it.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A register with no defined value, for destinations whose every byte is
 // written before use (the empty asm emits nothing, so no copy is made).
 __device__ __forceinline__ uint32_t scratch_vgpr() {

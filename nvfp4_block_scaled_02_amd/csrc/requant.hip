@@ -55,19 +55,15 @@ __device__ __forceinline__ uint32_t e4m3_sr_pack4(float y0, float y1, float y2, 
 // at least -127 (the E8M0 byte is e + 127, read from amax's exponent field);
 // elements y = x * 2^-e clamped to +-448, then SR onto E4M3 with the hash of
 // element index idx0 + i (hbase = lo32(idx0) ^ key, idx0 a multiple of 32).
-// A NaN or an infinity in the block: scale 0xFF, elements 0.
-__device__ __forceinline__ uint32_t mxfp8_block(const float (&x)[32], uint32_t hbase,
-                                                uint32_t (&w)[8]) {
-  float m[11];
+// A NaN or an infinity in the block: scale 0xFF, elements 0.  `at(i)` gives
+// value i (it is called twice per value: for the amax and the conversion).
+template <typename At>
+__device__ __forceinline__ uint32_t mxfp8_block(At at, uint32_t hbase, uint32_t (&w)[8]) {
+  float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 10; ++j) m[j] = max3_abs(x[3 * j], x[3 * j + 1], x[3 * j + 2]);
-  m[10] = __builtin_elementwise_maximum(__builtin_fabsf(x[30]), __builtin_fabsf(x[31]));
-  const float m01 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[0], m[1]), m[2]);
-  const float m02 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[3], m[4]), m[5]);
-  const float m03 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[6], m[7]), m[8]);
-  const float m04 = __builtin_elementwise_maximum(m[9], m[10]);
-  const float amax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m01, m02),
-                                                   __builtin_elementwise_maximum(m03, m04));
+  for (int i = 0; i < 32; i += 4)
+    amax = __builtin_elementwise_maximum(amax, __builtin_elementwise_maximum(
+        max3_abs(at(i), at(i + 1), at(i + 2)), __builtin_fabsf(at(i + 3))));
   const bool bad = !(amax <= 3.40282347e38f);  // NaN or infinity
   const uint32_t biased = __float_as_uint(amax) >> 23;
   const uint32_t sb = biased > 8u ? biased - 8u : 0u;  // e + 127
@@ -75,8 +71,8 @@ __device__ __forceinline__ uint32_t mxfp8_block(const float (&x)[32], uint32_t h
   const uint32_t tt = hbase ^ (hbase >> 16);  // shared first step of fmix32
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint32_t v = e4m3_sr_pack4(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv,
-                                     x[4 * j + 3] * inv, fmix32_tail(tt ^ (uint32_t)(4 * j)),
+    const uint32_t v = e4m3_sr_pack4(at(4 * j) * inv, at(4 * j + 1) * inv, at(4 * j + 2) * inv,
+                                     at(4 * j + 3) * inv, fmix32_tail(tt ^ (uint32_t)(4 * j)),
                                      fmix32_tail(tt ^ (uint32_t)(4 * j + 1)),
                                      fmix32_tail(tt ^ (uint32_t)(4 * j + 2)),
                                      fmix32_tail(tt ^ (uint32_t)(4 * j + 3)));
@@ -91,7 +87,17 @@ struct RqTile {
   static constexpr int kTR = TARGET == kTargetNvfp4 ? 32 : 64;  // tile height (rows)
   static constexpr int kCB = TARGET == kTargetNvfp4 ? 16 : 32;  // column block (rows)
 };
-constexpr int kRqPitch = kSW * 4 + 16;  // binary32 tile row pitch (bytes), padded
+constexpr int kRqPitch = kSW * 4;  // binary32 tile row pitch (bytes)
+
+// Byte offset, within a tile row, of column c (0 <= c < kSW).  The 16-byte
+// piece h of row block b (columns 16b + 4h .. +4) sits at piece slot
+// h ^ ((b >> 1) & 3): the eight lanes of one tile row that store their row
+// blocks in the same instruction then cover all 32 banks of a 128-byte LDS
+// pass instead of four of them; a column read (one row, consecutive columns)
+// still touches each bank once per pass.
+__host__ __device__ constexpr int rq_col_off(int c) {
+  return (c >> 4) * 64 + 16 * (((c >> 2) & 3) ^ ((c >> 5) & 3)) + 4 * (c & 3);
+}
 constexpr int kMxStTiles = 32;          // MXFP8 scales: 32 tiles of 64 rows = 64 bytes
 constexpr int kMxStBytes = kMxStTiles * 2;
 constexpr int kMxStPitch = kMxStBytes + 4;
@@ -124,24 +130,27 @@ struct RqLoad {
   static constexpr int kN = RqTile<TARGET>::kTR * (kSW / 16) / kThreads;  // 1 or 2
   uint2 cw[kN];
   uint32_t sb[kN];
-  float al[kN];
+  float al[kN];  // per-tensor: unused; per row: the row's amax
 };
 
+// The loads are unconditional (addresses clamped into the tensor; a block
+// outside it is zeroed where it is used): the number of loads in flight is
+// then the same on every path, so waiting for the oldest buffer never has to
+// wait for the newer ones too.
 template <int TARGET, bool ROWSC>
 __device__ __forceinline__ void rq_load(RqLoad<TARGET>& L, const uint8_t* __restrict__ codes,
                                         const uint8_t* __restrict__ scales,
-                                        const float* __restrict__ row_amax, float sg, float alpha0,
-                                        int64_t rows, int64_t cols, int64_t r0, int64_t c0) {
+                                        const float* __restrict__ row_amax, int64_t rows,
+                                        int64_t cols, int64_t r0, int64_t c0) {
 #pragma unroll
   for (int u = 0; u < RqLoad<TARGET>::kN; ++u) {
     const int k = u * kThreads + (int)threadIdx.x;
-    const int64_t r = r0 + (k >> 3), c = c0 + (k & 7) * 16;
-    const bool ok = r < rows && c < cols;  // cols % 16 == 0: a block is whole or absent
-    L.cw[u] = ok ? ld_nt(reinterpret_cast<const uint2*>(codes + r * (cols >> 1) + (c >> 1)))
-                 : make_uint2(0, 0);
-    L.sb[u] = ok ? (uint32_t)scales[r * (cols >> 4) + (c >> 4)] : 0u;
-    if constexpr (ROWSC) L.al[u] = ok ? outer_alpha(row_amax[r], sg) : 0.0f;
-    else L.al[u] = ok ? alpha0 : 0.0f;
+    int64_t r = r0 + (k >> 3), c = c0 + (k & 7) * 16;
+    r = r < rows ? r : rows - 1;
+    c = c < cols ? c : cols - 16;
+    L.cw[u] = ld_nt(reinterpret_cast<const uint2*>(codes + r * (cols >> 1) + (c >> 1)));
+    L.sb[u] = (uint32_t)scales[r * (cols >> 4) + (c >> 4)];
+    if constexpr (ROWSC) L.al[u] = row_amax[r];
   }
 }
 
@@ -178,32 +187,37 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
   const int64_t v = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;  // XCD b % 8 takes a run
   const int lane = threadIdx.x;
   const int cb_col = lane & (kSW - 1), cb_row = (lane / kSW) * kCB;  // this lane's column block
+  const int col_off = rq_col_off(cb_col);
   for (int64_t unit = v; unit < units; unit += G) {
     const int64_t g = unit / tiles_c;
     const int64_t c0 = (unit - g * tiles_c) * kSW;
     const int64_t tr0 = g * seg;
     const int64_t tr1 = tr0 + seg < tiles_r ? tr0 + seg : tiles_r;
     int64_t ct_lo = tr0, st_lo = tr0;  // first tile of the open stages
-    RqLoad<TARGET> L;
-    rq_load<TARGET, ROWSC>(L, codes, scales, row_amax, sg, alpha0, rows, cols, tr0 * kTR, c0);
-    for (int64_t tr = tr0; tr < tr1; ++tr) {
+    // Two tiles are in flight ahead of the one being processed.  The three
+    // load buffers rotate by name (the walk is unrolled by three): copying a
+    // buffer whose loads are outstanding would make the copy wait for them.
+    // Past the end of the walk the last tile is requested again (unused).
+    auto step = [&](const RqLoad<TARGET>& L, RqLoad<TARGET>& ahead, int64_t tr) {
       const int64_t r0 = tr * kTR;
-      RqLoad<TARGET> Ln;  // the next tile is requested before this one is processed
-      if (tr + 1 < tr1)
-        rq_load<TARGET, ROWSC>(Ln, codes, scales, row_amax, sg, alpha0, rows, cols, r0 + kTR, c0);
+      const int64_t t_ahead = tr + 2 < tr1 ? tr + 2 : tr1 - 1;
+      rq_load<TARGET, ROWSC>(ahead, codes, scales, row_amax, rows, cols, t_ahead * kTR, c0);
       // ---- dequantize the lane's row blocks into the binary32 tile
 #pragma unroll
       for (int u = 0; u < RqLoad<TARGET>::kN; ++u) {
         const int k = u * kThreads + lane;
-        const float D = decode_scale(SRC_FMT, L.sb[u]);
-        const float a = L.al[u];
+        const bool ok = r0 + (k >> 3) < rows && c0 + (k & 7) * 16 < cols;
+        const uint32_t wx = ok ? L.cw[u].x : 0u, wy = ok ? L.cw[u].y : 0u;
+        const float D = ok ? decode_scale(SRC_FMT, L.sb[u]) : 0.0f;
+        const float a = !ok ? 0.0f : ROWSC ? outer_alpha(L.al[u], sg) : alpha0;
         float4* dst = reinterpret_cast<float4*>(tile + (k >> 3) * kRqPitch + (k & 7) * 64);
-        dst[0] = dequant4(NVFP4_DEC_PK_FP4(L.cw[u].x, 0), NVFP4_DEC_PK_FP4(L.cw[u].x, 1), D, a);
-        dst[1] = dequant4(NVFP4_DEC_PK_FP4(L.cw[u].x, 2), NVFP4_DEC_PK_FP4(L.cw[u].x, 3), D, a);
-        dst[2] = dequant4(NVFP4_DEC_PK_FP4(L.cw[u].y, 0), NVFP4_DEC_PK_FP4(L.cw[u].y, 1), D, a);
-        dst[3] = dequant4(NVFP4_DEC_PK_FP4(L.cw[u].y, 2), NVFP4_DEC_PK_FP4(L.cw[u].y, 3), D, a);
+        const int sw = ((k & 7) >> 1) & 3;  // piece h goes to slot h ^ sw
+        dst[0 ^ sw] = dequant4(NVFP4_DEC_PK_FP4(wx, 0), NVFP4_DEC_PK_FP4(wx, 1), D, a);
+        dst[1 ^ sw] = dequant4(NVFP4_DEC_PK_FP4(wx, 2), NVFP4_DEC_PK_FP4(wx, 3), D, a);
+        dst[2 ^ sw] = dequant4(NVFP4_DEC_PK_FP4(wy, 0), NVFP4_DEC_PK_FP4(wy, 1), D, a);
+        dst[3 ^ sw] = dequant4(NVFP4_DEC_PK_FP4(wy, 2), NVFP4_DEC_PK_FP4(wy, 3), D, a);
       }
-      __syncthreads();
+      lds_sync();
       // ---- the lane's column block, quantized
       const int64_t c = c0 + cb_col, r = r0 + cb_row;
       const uint64_t idx0 = (uint64_t)c * (uint64_t)rows + (uint64_t)r;  // index in X^T
@@ -212,19 +226,20 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
         float xc[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          xc[i] = *reinterpret_cast<const float*>(tile + (cb_row + i) * kRqPitch + cb_col * 4);
+          xc[i] = *reinterpret_cast<const float*>(tile + (cb_row + i) * kRqPitch + col_off);
         const BlockOut o = quantize_block_x<DST_FMT, SELECT_6, ROUND_SR>(xc, tab, ts, hb);
         const int wd = (int)(tr % kCtTiles) * (kTR / 8) + (cb_row >> 3);
         ct[cb_col * kCtPitch + wd] = o.c0;
         ct[cb_col * kCtPitch + wd + 1] = o.c1;
         st[cb_col * kStPitch + (int)(tr % kStTiles) * (kTR / 16) + (cb_row >> 4)] = (uint8_t)o.scale;
       } else {
+        // all 32 values read at once (occupancy is bounded by LDS, not VGPRs)
+        const uint8_t* colp = tile + cb_row * kRqPitch + col_off;
         float xc[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-          xc[i] = *reinterpret_cast<const float*>(tile + (cb_row + i) * kRqPitch + cb_col * 4);
+        for (int i = 0; i < 32; ++i) xc[i] = *reinterpret_cast<const float*>(colp + i * kRqPitch);
         uint32_t w[8];
-        const uint32_t sc = mxfp8_block(xc, hb, w);
+        const uint32_t sc = mxfp8_block([&xc](int i) { return xc[i]; }, hb, w);
         if (c < cols && r < rows) {  // rows % 32 == 0: a block is whole or absent
           uint4* p = reinterpret_cast<uint4*>(out_t + c * rows + r);
           p[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -232,7 +247,7 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
         }
         st[cb_col * kMxStPitch + (int)(tr % kMxStTiles) * 2 + (cb_row >> 5)] = (uint8_t)sc;
       }
-      __syncthreads();  // staged outputs complete; the tile may be rewritten
+      lds_sync();  // staged outputs complete; the tile may be rewritten
       // ---- flush closed stages
       const bool last = tr + 1 == tr1;
       if constexpr (NV) {
@@ -250,17 +265,30 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
           st_lo = tr + 1;
         }
       }
-      if (tr + 1 < tr1) L = Ln;
+    };
+    RqLoad<TARGET> A, B, C;
+    rq_load<TARGET, ROWSC>(A, codes, scales, row_amax, rows, cols, tr0 * kTR, c0);
+    rq_load<TARGET, ROWSC>(B, codes, scales, row_amax, rows, cols,
+                           (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0);
+    int64_t tr = tr0;
+    for (; tr + 3 <= tr1; tr += 3) {
+      step(A, C, tr);
+      step(B, A, tr + 1);
+      step(C, B, tr + 2);
     }
+    if (tr < tr1) step(A, C, tr);
+    if (tr + 1 < tr1) step(B, A, tr + 1);
   }
 }
 
 // ---------------------------------------------------------------- dequantized amax
-// max |x_hat| over an NVFP4 tensor: per block the largest magnitude code
-// times |D| times alpha (x_hat is monotone in |q|), reduced like the tensor
-// amax (integer max of the sign-cleared binary32 patterns: NaN beats
-// infinity beats every finite value).  A lane takes one block (8 code bytes
-// and its scale byte) per step.
+// max |x_hat| over an NVFP4 tensor.  |x_hat| = fl(fl(|q| |D|) alpha) is
+// monotone in |q| |D| (q |D| is exact, and multiplying by alpha >= 0 and
+// rounding are monotone), so the maximum is fl(max(|q| |D|) alpha): per
+// block the largest magnitude code times |D|, the maximum over the tensor
+// (or over a row, for per-row alpha_r), one multiply by alpha at the end.
+// Maxima are integer maxima of the sign-cleared binary32 patterns (NaN
+// beats infinity beats every finite value), as for the tensor amax.
 __device__ __forceinline__ uint32_t max_mag_code(uint2 w) {
   uint32_t m = 0;
 #pragma unroll
@@ -272,37 +300,100 @@ __device__ __forceinline__ uint32_t max_mag_code(uint2 w) {
   return m;
 }
 
-template <int FMT, bool ROWSC>
-__global__ void __launch_bounds__(kThreads)
-dq_amax_kernel(const uint2* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t nblocks,
-               int64_t row_blocks, const float* __restrict__ amax, float sg,
-               uint32_t* __restrict__ out) {
-  const float alpha0 = ROWSC ? 0.0f : outer_alpha(*amax, sg);
-  uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nblocks; i += stride) {
-    const uint2 w = ld_nt(codes + i);
-    const uint32_t sb = scales[i];
-    const float a = ROWSC ? outer_alpha(amax[i / row_blocks], sg) : alpha0;
-    const float q = NVFP4_DEC_PK_FP4(max_mag_code(w), 0)[0];
-    const float D = __builtin_fabsf(decode_scale(FMT, sb));
-    const uint32_t bits = __float_as_uint((q * D) * a) & 0x7FFFFFFFu;
-    m = m > bits ? m : bits;
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
-    m = m > o ? m : o;
-  }
-  __shared__ uint32_t red[kThreads / 64];
+template <int FMT>
+__device__ __forceinline__ uint32_t qd_bits(uint2 w, uint32_t sb) {
+  const float q = NVFP4_DEC_PK_FP4(max_mag_code(w), 0)[0];
+  return __float_as_uint(q * __builtin_fabsf(decode_scale(FMT, sb))) & 0x7FFFFFFFu;
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+constexpr int kDqaUnroll = 4;
+constexpr int kDqaThreads = 1024;
+
+// Workgroup maximum of m, folded into *out by one atomic (skipped when the
+// running maximum already covers it).
+__device__ __forceinline__ void dq_amax_flush(uint32_t m, uint32_t* out) {
+  for (int off = 32; off >= 1; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  __shared__ uint32_t red[kDqaThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
-    for (int w2 = 1; w2 < kThreads / 64; ++w2) r = r > red[w2] ? r : red[w2];
-    // the running maximum only grows: skip the atomic when it already covers r
+    for (int w2 = 1; w2 < (int)(blockDim.x >> 6); ++w2) r = umax(r, red[w2]);
     const uint32_t cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (r > cur) atomicMax(out, r);
   }
+}
+
+// Per-tensor alpha: a lane takes two blocks (a 16-byte chunk of codes, two
+// scale bytes) per load, four loads in flight, one workgroup per CU.
+template <int FMT>
+__global__ void __launch_bounds__(kDqaThreads)
+dq_amax_kernel(const uint4* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t npairs,
+               int64_t nblocks, const float* __restrict__ amax, float sg,
+               uint32_t* __restrict__ out) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kDqaThreads;
+  int64_t i = (int64_t)blockIdx.x * kDqaThreads + threadIdx.x;
+  for (; i + (kDqaUnroll - 1) * stride < npairs; i += kDqaUnroll * stride) {
+    uint4 w[kDqaUnroll];
+    uint32_t s2[kDqaUnroll];
+#pragma unroll
+    for (int u = 0; u < kDqaUnroll; ++u) {
+      w[u] = ld_nt(codes + i + u * stride);
+      s2[u] = scales[i + u * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < kDqaUnroll; ++u)
+      m = umax(m, umax(qd_bits<FMT>(make_uint2(w[u].x, w[u].y), s2[u] & 0xFFu),
+                       qd_bits<FMT>(make_uint2(w[u].z, w[u].w), s2[u] >> 8)));
+  }
+  for (; i < npairs; i += stride) {
+    const uint4 w = ld_nt(codes + i);
+    const uint32_t s2 = scales[i];
+    m = umax(m, umax(qd_bits<FMT>(make_uint2(w.x, w.y), s2 & 0xFFu),
+                     qd_bits<FMT>(make_uint2(w.z, w.w), s2 >> 8)));
+  }
+  if ((nblocks & 1) && blockIdx.x == 0 && threadIdx.x == 0)  // the block after the last pair
+    m = umax(m, qd_bits<FMT>(reinterpret_cast<const uint2*>(codes)[nblocks - 1],
+                             reinterpret_cast<const uint8_t*>(scales)[nblocks - 1]));
+  const float alpha = outer_alpha(*amax, sg);
+  dq_amax_flush(__float_as_uint(__uint_as_float(m) * alpha) & 0x7FFFFFFFu, out);
+}
+
+// Per-row alpha_r: a wavefront per row (its lanes over the row's blocks,
+// four loads in flight), the row maximum times alpha_r.
+template <int FMT>
+__global__ void __launch_bounds__(kDqaThreads)
+dq_amax_rows_kernel(const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
+                    int64_t rows, int64_t row_blocks, const float* __restrict__ row_amax, float sg,
+                    uint32_t* __restrict__ out) {
+  const int l = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (kDqaThreads / 64);
+  uint32_t best = 0;
+  for (int64_t r = (int64_t)blockIdx.x * (kDqaThreads / 64) + (threadIdx.x >> 6); r < rows; r += nwaves) {
+    const uint2* cr = codes + r * row_blocks;
+    const uint8_t* sr = scales + r * row_blocks;
+    uint32_t m = 0;
+    int64_t j = l;
+    for (; j + (kDqaUnroll - 1) * 64 < row_blocks; j += kDqaUnroll * 64) {
+      uint2 w[kDqaUnroll];
+      uint32_t sb[kDqaUnroll];
+#pragma unroll
+      for (int u = 0; u < kDqaUnroll; ++u) {
+        w[u] = ld_nt(cr + j + u * 64);
+        sb[u] = sr[j + u * 64];
+      }
+#pragma unroll
+      for (int u = 0; u < kDqaUnroll; ++u) m = umax(m, qd_bits<FMT>(w[u], sb[u]));
+    }
+    for (; j < row_blocks; j += 64) m = umax(m, qd_bits<FMT>(ld_nt(cr + j), sr[j]));
+    for (int off = 32; off >= 1; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    const float v = __uint_as_float(m) * outer_alpha(row_amax[r], sg);
+    best = umax(best, __float_as_uint(v) & 0x7FFFFFFFu);
+  }
+  dq_amax_flush(best, out);
 }
 
 __global__ void __launch_bounds__(64) dq_amax_init_kernel(uint32_t* out) {
@@ -353,21 +444,32 @@ hipError_t launch_dequantized_amax(const RequantArgs& a, float* out, hipStream_t
   hipLaunchKernelGGL(dq_amax_init_kernel, dim3(1), dim3(64), 0, s, o);
   const int64_t nblocks = a.rows * a.cols / 16;
   if (nblocks == 0) return hipGetLastError();
-  int64_t grid = (nblocks + kThreads - 1) / kThreads;
-  const int64_t cap = (int64_t)device_cu_count() * 2;  // one atomic per workgroup
-  grid = grid < cap ? grid : cap;
-  const bool rowsc = a.row_amax != nullptr;
-  const float* am = rowsc ? a.row_amax : a.amax;
-  const uint2* c = reinterpret_cast<const uint2*>(a.codes);
-  const int64_t rb = a.cols / 16;
-  const dim3 gd((unsigned)grid), bd(kThreads);
-  if (a.fmt == FMT_UE5M3) {
-    if (rowsc) hipLaunchKernelGGL((dq_amax_kernel<FMT_UE5M3, true>), gd, bd, 0, s, c, a.scales, nblocks, rb, am, a.sg, o);
-    else hipLaunchKernelGGL((dq_amax_kernel<FMT_UE5M3, false>), gd, bd, 0, s, c, a.scales, nblocks, rb, am, a.sg, o);
-  } else {
-    if (rowsc) hipLaunchKernelGGL((dq_amax_kernel<FMT_E4M3, true>), gd, bd, 0, s, c, a.scales, nblocks, rb, am, a.sg, o);
-    else hipLaunchKernelGGL((dq_amax_kernel<FMT_E4M3, false>), gd, bd, 0, s, c, a.scales, nblocks, rb, am, a.sg, o);
+  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (one atomic) per CU
+  const dim3 bd(kDqaThreads);
+  if (a.row_amax != nullptr) {
+    int64_t grid = (a.rows + kDqaThreads / 64 - 1) / (kDqaThreads / 64);
+    grid = grid < cap ? grid : cap;
+    const uint2* c = reinterpret_cast<const uint2*>(a.codes);
+    if (a.fmt == FMT_UE5M3)
+      hipLaunchKernelGGL(dq_amax_rows_kernel<FMT_UE5M3>, dim3((unsigned)grid), bd, 0, s, c, a.scales,
+                         a.rows, a.cols / 16, a.row_amax, a.sg, o);
+    else
+      hipLaunchKernelGGL(dq_amax_rows_kernel<FMT_E4M3>, dim3((unsigned)grid), bd, 0, s, c, a.scales,
+                         a.rows, a.cols / 16, a.row_amax, a.sg, o);
+    return hipGetLastError();
   }
+  const int64_t npairs = nblocks / 2;
+  int64_t grid = (npairs + (int64_t)kDqaThreads * kDqaUnroll - 1) / ((int64_t)kDqaThreads * kDqaUnroll);
+  grid = grid < cap ? grid : cap;
+  grid = grid < 1 ? 1 : grid;
+  const uint4* c = reinterpret_cast<const uint4*>(a.codes);
+  const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.scales);
+  if (a.fmt == FMT_UE5M3)
+    hipLaunchKernelGGL(dq_amax_kernel<FMT_UE5M3>, dim3((unsigned)grid), bd, 0, s, c, sc, npairs,
+                       nblocks, a.amax, a.sg, o);
+  else
+    hipLaunchKernelGGL(dq_amax_kernel<FMT_E4M3>, dim3((unsigned)grid), bd, 0, s, c, sc, npairs,
+                       nblocks, a.amax, a.sg, o);
   return hipGetLastError();
 }
 

@@ -211,6 +211,7 @@ def _rq(**kw):
     dict(rows=48), dict(target=0, rows=40), dict(target=0, dst=None), dict(target=0, dfmt=3),
     dict(target=0, dgmax=-1.0), dict(out=None), dict(out_s=None), dict(out=FAKE_ODD),
     dict(codes=FAKE_ODD), dict(amax=FAKE + 2), dict(amax=None, ra=FAKE + 2),
+    dict(scales=FAKE + 1),
 ])
 def test_requantize_t_rejects(kw):
     assert _rq(**kw) == N.ERR_INVALID

@@ -21,6 +21,7 @@ from . import build as _build
 
 FMT_E4M3, FMT_UE5M3 = 0, 1
 SELECT_6, SELECT_4OVER6 = 0, 1
+SELECT_4OVER6_MAE, SELECT_4OVER6_MAXERR, SELECT_SWEEP = 2, 3, 4
 ROUND_RNE, ROUND_SR = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +78,11 @@ def _load():
     lib.or_fakequant_fwd.argtypes = [_f32p, _i64, _i64, _f32p, _f32p, _f32p]
     lib.or_fakequant_bwd.restype = ctypes.c_int
     lib.or_fakequant_bwd.argtypes = [_f32p, _f32p, _i64, _i64, _f32p, _f32p, _f32p, _f32p, _f32p]
+    lib.or_fakequant_fwd_amax.restype = ctypes.c_int
+    lib.or_fakequant_fwd_amax.argtypes = [_f32p, _i64, _i64, _f32p, _f32p, _f32p]
+    lib.or_fakequant_bwd_amax.restype = ctypes.c_int
+    lib.or_fakequant_bwd_amax.argtypes = [_f32p, _f32p, _i64, _i64, _f32p, _f32p, _f32p, _f32p,
+                                          _f32p]
     lib.or_row_amax.restype = ctypes.c_int
     lib.or_row_amax.argtypes = [_f32p, _i64, _i64, _f32p]
     lib.or_quantize_rowscaled.restype = ctypes.c_int
@@ -184,7 +190,8 @@ def default_global_max(fmt, select):
     fmt = _fmt(fmt)
     if fmt == FMT_UE5M3:
         return 114688.0
-    return 256.0 if int(select) == SELECT_4OVER6 else 448.0
+    four = (SELECT_4OVER6, SELECT_4OVER6_MAE, SELECT_4OVER6_MAXERR)
+    return 256.0 if int(select) in four else 448.0
 
 
 # ---------------------------------------------------------------- tensors
@@ -255,21 +262,25 @@ def sse(x, xhat):
     return _load().or_sse(_ptr(xf, _f32p), _ptr(xh, _f32p), xf.size)
 
 
-def fakequant_fwd(x, s_pre, s_post=None):
+def fakequant_fwd(x, s_pre, s_post=None, *, amax=False):
+    """x~ per block; with amax=True the per-block parameters are amaxes and
+    s = fl(a / 6)."""
     xf = as_f32(x)
     rows, cols = xf.shape
     sp = np.ascontiguousarray(s_pre, dtype=np.float32)
     so = None if s_post is None else np.ascontiguousarray(s_post, dtype=np.float32)
     out = np.empty((rows, cols), np.float32)
-    st = _load().or_fakequant_fwd(_ptr(xf, _f32p), rows, cols, _ptr(sp, _f32p),
-                                  _ptr(so, _f32p), _ptr(out, _f32p))
+    fn = _load().or_fakequant_fwd_amax if amax else _load().or_fakequant_fwd
+    st = fn(_ptr(xf, _f32p), rows, cols, _ptr(sp, _f32p), _ptr(so, _f32p), _ptr(out, _f32p))
     if st != 0:
         raise ValueError(f"oracle fakequant_fwd rejected the arguments (status {st})")
     return out
 
 
-def fakequant_bwd(x, g, s_pre, s_post=None):
-    """Returns (dx, ds) for tied scales, (dx, ds_pre, ds_post) for dual."""
+def fakequant_bwd(x, g, s_pre, s_post=None, *, amax=False):
+    """Returns (dx, ds) for tied scales, (dx, ds_pre, ds_post) for dual; with
+    amax=True the parameters are amaxes (s = a / 6) and the gradients are
+    with respect to them."""
     xf = as_f32(x)
     rows, cols = xf.shape
     gf = np.ascontiguousarray(g, dtype=np.float32)
@@ -278,9 +289,9 @@ def fakequant_bwd(x, g, s_pre, s_post=None):
     dx = np.empty((rows, cols), np.float32)
     dpre = np.empty(sp.shape, np.float32)
     dpost = None if s_post is None else np.empty(sp.shape, np.float32)
-    st = _load().or_fakequant_bwd(_ptr(xf, _f32p), _ptr(gf, _f32p), rows, cols, _ptr(sp, _f32p),
-                                  _ptr(so, _f32p), _ptr(dx, _f32p), _ptr(dpre, _f32p),
-                                  _ptr(dpost, _f32p))
+    fn = _load().or_fakequant_bwd_amax if amax else _load().or_fakequant_bwd
+    st = fn(_ptr(xf, _f32p), _ptr(gf, _f32p), rows, cols, _ptr(sp, _f32p), _ptr(so, _f32p),
+            _ptr(dx, _f32p), _ptr(dpre, _f32p), _ptr(dpost, _f32p))
     if st != 0:
         raise ValueError(f"oracle fakequant_bwd rejected the arguments (status {st})")
     if s_post is None:

@@ -48,7 +48,10 @@
 #define OR_FMT_E4M3 0
 #define OR_FMT_UE5M3 1
 #define OR_SELECT_6 0
-#define OR_SELECT_4OVER6 1
+#define OR_SELECT_4OVER6 1        /* Four-Over-Six, smaller squared error */
+#define OR_SELECT_4OVER6_MAE 2    /* Four-Over-Six, smaller absolute error */
+#define OR_SELECT_4OVER6_MAXERR 3 /* Four-Over-Six, smaller largest error */
+#define OR_SELECT_SWEEP 4         /* smallest squared error over every scale code */
 #define OR_ROUND_RNE 0
 #define OR_ROUND_SR 1
 
@@ -237,34 +240,58 @@ static void make_consts(or_consts *c, int fmt, float alpha) {
   }
 }
 
-/* One candidate encoding of one 16-element block with max mapped to Q
- * ([UE] 数学推导: s = quant(amax_b / Q_max); [E2E] Low-precision formats:
- * value = fp4 * fp8 * fp32):
- *   s_raw = a_b * K_Q  -> scale code  (nearest, ties to even, saturating)
- *   y_i   = x_i * INV_S[code]         -> E2M1 code (RNE, or SR)
- *   d_i   = fmaf(-q_i, S_EFF[code], x_i)
- *   SSE   = (P0 + P1) + (P2 + P3),  P_k = fmaf(d_i, d_i, P_k) over
- *           i = 4k .. 4k+3 in order, each P_k starting at +0.
- * The SSE decides the Four-Over-Six choice, so it is taken in binary32 in
- * this fixed order. */
-static float encode_block(const or_consts *c, const float *xb, float amax_b, float kq,
-                          int rounding, uint64_t seed, uint64_t idx0, int *scale_code,
-                          uint8_t nib[16]) {
-  float s_raw = amax_b * kq;
-  int code = scale_encode_tab(c->dec, c->maxc, s_raw);
-  float S = c->seff[code], I = c->inv[code];
+/* The error of one candidate encoding of a block, by the selection rule
+ * ([46a] Methodologie, [46b] Key claims: the smallest maximum error, the
+ * smallest absolute error (L1 / MAE), the smallest squared error (MSE); n = 16
+ * is constant, so sums stand for means).  From the residuals
+ * d_i = fmaf(-q_i, S_EFF, x_i):
+ *   MSE:    P_k = fmaf(d_i, d_i, P_k)      over i = 4k .. 4k+3, from +0;
+ *   MAE:    P_k = P_k + |d_i|              over i = 4k .. 4k+3, from +0;
+ *           error = (P0 + P1) + (P2 + P3)  (binary32, this order);
+ *   MAXERR: error = max |d_i|  (exact, order-free). */
+static float block_error(const float d[16], int select) {
+  if (select == OR_SELECT_4OVER6_MAXERR) {
+    float m = 0.0f;
+    for (int i = 0; i < 16; ++i)
+      if (fabsf(d[i]) > m || isnan(d[i])) m = isnan(d[i]) ? NAN : fabsf(d[i]);
+    return m;
+  }
   float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < 16; ++i)
+    P[i / 4] = select == OR_SELECT_4OVER6_MAE ? P[i / 4] + fabsf(d[i]) : fmaf(d[i], d[i], P[i / 4]);
+  return (P[0] + P[1]) + (P[2] + P[3]);
+}
+
+/* The encoding of one 16-element block under scale code `code`
+ * ([E2E] Low-precision formats: value = fp4 * fp8 * fp32):
+ *   y_i = x_i * INV_S[code] -> E2M1 code (RNE, or SR);
+ *   d_i = fmaf(-q_i, S_EFF[code], x_i), and the block error by `select`
+ *   (the squared error for max->6 and the sweep). */
+static float encode_block_code(const or_consts *c, const float *xb, int code, int rounding,
+                               int select, uint64_t seed, uint64_t idx0, uint8_t nib[16]) {
+  float S = c->seff[code], I = c->inv[code];
+  float d[16];
   for (int i = 0; i < 16; ++i) {
     float y = xb[i] * I;
     int n = rounding == OR_ROUND_SR ? or_e2m1_code_sr(y, or_sr_hash(seed, idx0 + (uint64_t)i))
                                     : or_e2m1_code(y);
     nib[i] = (uint8_t)n;
     float q = (float)or_e2m1_value(n);
-    float d = fmaf(-q, S, xb[i]);
-    P[i / 4] = fmaf(d, d, P[i / 4]);
+    d[i] = fmaf(-q, S, xb[i]);
   }
+  return block_error(d, select);
+}
+
+/* One candidate encoding with the block max mapped to Q ([UE] 数学推导:
+ * s = quant(amax_b / Q_max)): s_raw = a_b * K_Q -> scale code (nearest,
+ * ties to even, saturating), then encode_block_code. */
+static float encode_block(const or_consts *c, const float *xb, float amax_b, float kq,
+                          int rounding, int select, uint64_t seed, uint64_t idx0, int *scale_code,
+                          uint8_t nib[16]) {
+  float s_raw = amax_b * kq;
+  int code = scale_encode_tab(c->dec, c->maxc, s_raw);
   *scale_code = code;
-  return (P[0] + P[1]) + (P[2] + P[3]);
+  return encode_block_code(c, xb, code, rounding, select, seed, idx0, nib);
 }
 
 /* Row-wise NVFP4 quantization of x[rows, cols] (cols % 16 == 0): every run of
@@ -274,10 +301,16 @@ static float encode_block(const or_consts *c, const float *xb, float amax_b, flo
  * block.  select = Four-Over-Six encodes every block with max->6 and max->4
  * and keeps max->4 only if its SSE is strictly lower ([46b] Method; [46a]
  * Methodologie); *count4 (if given) is increased by the number of such
- * blocks.  rounding = SR uses the hash of element index (row0 + r) * cols + c,
+ * blocks.  select = 4OVER6_MAE / 4OVER6_MAXERR: the same choice by the
+ * absolute-error sum or the largest error.  select = SWEEP: every finite scale
+ * code is tried and the smallest squared error kept (the MSE scale sweep that
+ * initializes scale learning, [SL] How Scale Learning Works and its ModelOpt
+ * configuration); rounding must then be RNE and *count4 is untouched.
+ * rounding = SR uses the hash of element index (row0 + r) * cols + c,
  * row0 being the global row of x's first row.  Column-wise quantization is
  * this function applied to the transpose.  sse_sel / sse6 (optional) receive
- * each block's SSE for the chosen and for the max->6 encoding.
+ * each block's error (by the selection rule; the squared error for max->6 and
+ * the sweep) for the chosen and for the max->6 encoding.
  * A negative or non-finite amax writes the NaN scale code to every block and
  * code 0 to every element; with a usable amax, a block holding a NaN element
  * gets the NaN scale code and code 0 for its elements.  Infinite elements
@@ -287,7 +320,7 @@ int or_quantize(const float *x, int64_t rows, int64_t cols, int64_t row0, float 
                 uint64_t *count4, float *sse_sel, float *sse6) {
   if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
   if (fmt != OR_FMT_E4M3 && fmt != OR_FMT_UE5M3) return OR_EINVAL;
-  if (select != OR_SELECT_6 && select != OR_SELECT_4OVER6) return OR_EINVAL;
+  if (select < OR_SELECT_6 || select > OR_SELECT_SWEEP) return OR_EINVAL;
   if (rounding != OR_ROUND_RNE && rounding != OR_ROUND_SR) return OR_EINVAL;
   if (rounding == OR_ROUND_SR && select != OR_SELECT_6) return OR_EINVAL;
   const int64_t nb = cols / 16;
@@ -322,20 +355,38 @@ int or_quantize(const float *x, int64_t rows, int64_t cols, int64_t row0, float 
         continue;
       }
       uint64_t idx0 = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(b * 16);
-      uint8_t nib6[16], nib4[16];
+      uint8_t nib6[16], nib4[16], nibs[16];
       int code6, code4 = 0;
-      float e6 = encode_block(c, xb, amax_b, c->k6, rounding, seed, idx0, &code6, nib6);
+      /* the max->6 candidate's error by the block's rule (squared error for
+       * max->6 itself and for the sweep) */
+      const int rule = select == OR_SELECT_SWEEP ? OR_SELECT_4OVER6 : select;
+      float e6 = encode_block(c, xb, amax_b, c->k6, rounding, rule, seed, idx0, &code6, nib6);
       float e = e6;
       const uint8_t *nib = nib6;
       int code = code6;
-      if (select == OR_SELECT_4OVER6) {
-        float e4 = encode_block(c, xb, amax_b, c->k4, rounding, seed, idx0, &code4, nib4);
+      if (select == OR_SELECT_4OVER6 || select == OR_SELECT_4OVER6_MAE ||
+          select == OR_SELECT_4OVER6_MAXERR) {
+        float e4 = encode_block(c, xb, amax_b, c->k4, rounding, select, seed, idx0, &code4, nib4);
         if (e4 < e6) {
           e = e4;
           nib = nib4;
           code = code4;
           n4 += 1;
         }
+      } else if (select == OR_SELECT_SWEEP) {
+        /* every finite scale code in ascending order; a strictly smaller
+         * squared error replaces the best (ties keep the smaller code) */
+        float best = INFINITY;
+        for (int cc = 0; cc <= c->maxc; ++cc) {
+          float ec = encode_block_code(c, xb, cc, rounding, OR_SELECT_4OVER6, seed, idx0, nibs);
+          if (ec < best) {
+            best = ec;
+            code = cc;
+            memcpy(nib4, nibs, 16);
+          }
+        }
+        e = best;
+        nib = nib4;
       }
       scales[r * nb + b] = (uint8_t)code;
       for (int j = 0; j < 8; ++j)
@@ -718,9 +769,51 @@ int or_fakequant_fwd(const float *x, int64_t rows, int64_t cols, const float *s_
  *                  (0 when s_pre = 0)
  * Every product and sum is binary64, summed in index order i = 0..15, and
  * rounded once to binary32.  ds_post is written only for dual scales. */
+static int fq_bwd(const float *x, const float *g, int64_t rows, int64_t cols, const float *s_pre,
+                  const float *s_post, double div, float *dx, float *ds_pre, float *ds_post);
+
 int or_fakequant_bwd(const float *x, const float *g, int64_t rows, int64_t cols,
                      const float *s_pre, const float *s_post, float *dx, float *ds_pre,
                      float *ds_post) {
+  return fq_bwd(x, g, rows, cols, s_pre, s_post, 1.0, dx, ds_pre, ds_post);
+}
+
+/* amax reparameterization ([SL] How Scale Learning Works: the trained
+ * quantity is amax, not the scale): per block s = fl(a / 6) (binary32), the
+ * fake quantization of that s, and dL/da = dL/ds * ds/da = dL/ds / 6, the
+ * division applied to the binary64 block sums before their one rounding. */
+static float *amax_to_scale(const float *a, int64_t n) {
+  if (!a) return NULL;
+  float *s = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+  for (int64_t i = 0; i < n; ++i) s[i] = a[i] / 6.0f;
+  return s;
+}
+
+int or_fakequant_fwd_amax(const float *x, int64_t rows, int64_t cols, const float *a_pre,
+                          const float *a_post, float *xq) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  float *sp = amax_to_scale(a_pre, rows * cols / 16), *so = amax_to_scale(a_post, rows * cols / 16);
+  int st = or_fakequant_fwd(x, rows, cols, sp, so, xq);
+  free(sp);
+  free(so);
+  return st;
+}
+
+int or_fakequant_bwd_amax(const float *x, const float *g, int64_t rows, int64_t cols,
+                          const float *a_pre, const float *a_post, float *dx, float *da_pre,
+                          float *da_post) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
+  float *sp = amax_to_scale(a_pre, rows * cols / 16), *so = amax_to_scale(a_post, rows * cols / 16);
+  int st = fq_bwd(x, g, rows, cols, sp, so, 6.0, dx, da_pre, da_post);
+  free(sp);
+  free(so);
+  return st;
+}
+
+/* div: the scale gradients' binary64 block sums are divided by div (1 for
+ * the scale itself, 6 for the amax) before the rounding to binary32. */
+static int fq_bwd(const float *x, const float *g, int64_t rows, int64_t cols, const float *s_pre,
+                  const float *s_post, double div, float *dx, float *ds_pre, float *ds_post) {
   if (rows < 0 || cols < 0 || cols % 16 != 0) return OR_EINVAL;
   const int64_t nb = cols / 16;
 #pragma omp parallel for schedule(static)
@@ -749,14 +842,14 @@ int or_fakequant_bwd(const float *x, const float *g, int64_t rows, int64_t cols,
         }
       }
       if (!s_post) {
-        ds_pre[blk] = (float)acc_s;
+        ds_pre[blk] = (float)(acc_s / div);
       } else {
-        ds_post[blk] = (float)acc_post;
+        ds_post[blk] = (float)(acc_post / div);
         if (sp_pre == 0.0f) {
           ds_pre[blk] = 0.0f;
         } else {
           double spd = (double)sp_pre;
-          ds_pre[blk] = (float)(-((double)s_post[blk] * acc_t) / (spd * spd));
+          ds_pre[blk] = (float)((-((double)s_post[blk] * acc_t) / (spd * spd)) / div);
         }
       }
     }

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -68,7 +68,15 @@ enum {
 enum { NVFP4_SCALE_E4M3 = 0, NVFP4_SCALE_UE5M3 = 1 };
 
 /* Block-scale selection: every block max -> 6, or Four-Over-Six (MSE). */
-enum { NVFP4_SELECT_6 = 0, NVFP4_SELECT_4OVER6 = 1 };
+/* Block-scale selection ("Four Over Six" summaries: Methodologie, Key claims;
+ * "Scale Learning" blog: the MSE scale sweep that initializes the scales). */
+enum {
+  NVFP4_SELECT_6 = 0,               /* block max -> 6 */
+  NVFP4_SELECT_4OVER6 = 1,          /* max -> 4 or 6, smaller squared error (MSE) */
+  NVFP4_SELECT_4OVER6_MAE = 2,      /* max -> 4 or 6, smaller absolute error (MAE) */
+  NVFP4_SELECT_4OVER6_MAXERR = 3,   /* max -> 4 or 6, smaller largest error */
+  NVFP4_SELECT_SWEEP = 4            /* every scale code, smallest squared error */
+};
 
 /* Element rounding: round-to-nearest-even, or stochastic (max->6 only). */
 enum { NVFP4_ROUND_RNE = 0, NVFP4_ROUND_SR = 1 };
@@ -99,10 +107,11 @@ int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* s
  *                   nvfp4_tensor_amax, or a stale/periodic value).  The outer
  *                   scale is alpha = A / (6 * global_fp8_max) in binary32
  *                   (alpha = 1 if A = 0).
- *   global_fp8_max  S_g > 0, or 0 for the default: 448 (E4M3, max->6),
- *                   256 (E4M3, Four-Over-Six), 114688 (UE5M3).
+ *   global_fp8_max  S_g > 0, or 0 for the default: 448 (E4M3, max->6 and
+ *                   the sweep), 256 (E4M3, the Four-Over-Six rules), 114688
+ *                   (UE5M3).
  *   scale_fmt       NVFP4_SCALE_E4M3 or NVFP4_SCALE_UE5M3.
- *   select          NVFP4_SELECT_6 or NVFP4_SELECT_4OVER6.
+ *   select          an NVFP4_SELECT_* rule (below).
  *   rounding        NVFP4_ROUND_RNE or NVFP4_ROUND_SR (requires SELECT_6).
  *   axes            NVFP4_AXIS_ROW, NVFP4_AXIS_COL or both.
  *   seed            stochastic rounding only: the variate of the element at
@@ -116,13 +125,19 @@ int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* s
  * s_raw = a * K_Q with K_Q = 1/(Q*alpha); code = nearest scale code (ties to
  * even, saturating); y_i = x_i * (1/(D[code]*alpha)); E2M1 code of y_i (RNE,
  * or SR); SSE over the block in a fixed 4x4 fmaf tree; max->4 is kept only if
- * its SSE is strictly lower.
+ * its SSE is strictly lower.  With the residuals d_i = fmaf(-q_i, S, x_i):
+ * SELECT_4OVER6_MAE compares the sums of |d_i| (the same 4x4 tree, with
+ * additions), SELECT_4OVER6_MAXERR the largest |d_i|.  SELECT_SWEEP encodes
+ * the block with every finite scale code (ascending) and keeps the one with
+ * the strictly smallest SSE (ties keep the smaller code): the MSE scale sweep
+ * that initializes scale learning; it does not touch count4.
  * A negative or non-finite *amax: every scale byte = the NaN code (0x7F E4M3,
  * 0xFF UE5M3), every element code 0.  A NaN element with a usable amax: same
  * for its block.
  * Errors (NVFP4_ERR_INVALID): x/amax NULL; rows or cols < 0; ROW with
  * cols % 16 != 0 or codes/scales NULL; COL with rows % 16 != 0 or
- * codes_t/scales_t NULL; unknown enum; axes == 0; SR with Four-Over-Six;
+ * codes_t/scales_t NULL; unknown enum; axes == 0; SR with any select but
+ * SELECT_6;
  * global_fp8_max negative or non-finite; misaligned pointers.
  * rows == 0 or cols == 0: nothing to do, NVFP4_OK.
  */
@@ -194,6 +209,22 @@ int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const flo
 int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
                         const float* s_pre, const float* s_post, float* grad_x,
                         float* grad_s_pre, float* grad_s_post, void* stream);
+
+/*
+ * nvfp4_fakequant_fwd_amax / nvfp4_fakequant_bwd_amax -- the same with the
+ * trained quantity reparameterized as the block amax ("Scale Learning", How
+ * Scale Learning Works: ModelOpt trains amax rather than the scale): per
+ * block s_pre = fl(a_pre / 6), s_post = fl(a_post / 6) in binary32, then
+ * exactly the scale form; the gradients are with respect to the amaxes,
+ * dL/da = dL/ds * ds/da = dL/ds / 6, the division applied to the binary64
+ * block sums before their one rounding.  Arguments, layouts and errors as
+ * nvfp4_fakequant_fwd / nvfp4_fakequant_bwd with a_* in place of s_*.
+ */
+int nvfp4_fakequant_fwd_amax(const uint16_t* x, int64_t rows, int64_t cols, const float* a_pre,
+                             const float* a_post, float* xq_out, void* stream);
+int nvfp4_fakequant_bwd_amax(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
+                             const float* a_pre, const float* a_post, float* grad_x,
+                             float* grad_a_pre, float* grad_a_post, void* stream);
 
 /* ---------------------------------------------------------------------
  * Per-row outer scales ("End-to-End 4-Bit Training", Recipe details:

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 SCALE_E4M3, SCALE_UE5M3 = 0, 1
 SELECT_6, SELECT_4OVER6 = 0, 1
+SELECT_4OVER6_MAE, SELECT_4OVER6_MAXERR, SELECT_SWEEP = 2, 3, 4
 ROUND_RNE, ROUND_SR = 0, 1
 AXIS_ROW, AXIS_COL = 1, 2
 TARGET_NVFP4, TARGET_MXFP8 = 0, 1
@@ -41,6 +42,8 @@ SIGNATURES = {
     "nvfp4_quantize_2d": (_int, [_vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_fakequant_fwd": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_fakequant_bwd": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_fakequant_fwd_amax": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_fakequant_bwd_amax": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_dequantized_amax": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _f32, _int, _vp, _vp]),
     "nvfp4_requantize_t": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _f32, _int, _int, _vp, _f32,
                                   _int, _u64, _vp, _vp, _vp]),

@@ -13,7 +13,8 @@ import torch
 from . import _native as N
 
 _FMT = {"e4m3": N.SCALE_E4M3, "ue5m3": N.SCALE_UE5M3}
-_SELECT = {"6": N.SELECT_6, "4over6": N.SELECT_4OVER6}
+_SELECT = {"6": N.SELECT_6, "4over6": N.SELECT_4OVER6, "4over6-mae": N.SELECT_4OVER6_MAE,
+           "4over6-maxerr": N.SELECT_4OVER6_MAXERR, "sweep": N.SELECT_SWEEP}
 _ROUND = {"rne": N.ROUND_RNE, "sr": N.ROUND_SR}
 _AXES = {"row": N.AXIS_ROW, "col": N.AXIS_COL, "both": N.AXIS_ROW | N.AXIS_COL}
 
@@ -22,7 +23,7 @@ def default_global_max(fmt: str = "e4m3", select: str = "4over6") -> float:
     """FP8 maximum S_g the outer scale maps the tensor amax to."""
     if fmt == "ue5m3":
         return 114688.0
-    return 256.0 if select == "4over6" else 448.0
+    return 256.0 if select.startswith("4over6") else 448.0
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -318,8 +319,9 @@ def requantize_t(codes: torch.Tensor, scales: torch.Tensor, *,
 
 
 def fakequant_fwd(x: torch.Tensor, s_pre: torch.Tensor, s_post: Optional[torch.Tensor] = None,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """x~ = s_post * clamp(round_E2M1(x / s_pre), -6, 6) per 16-element block."""
+                  out: Optional[torch.Tensor] = None, *, amax: bool = False) -> torch.Tensor:
+    """x~ = s_post * clamp(round_E2M1(x / s_pre), -6, 6) per 16-element block.
+    amax=True: s_pre / s_post hold block amaxes and s = a / 6."""
     _need(x, torch.bfloat16, "x")
     _need(s_pre, torch.float32, "s_pre")
     if s_post is not None:
@@ -328,16 +330,19 @@ def fakequant_fwd(x: torch.Tensor, s_pre: torch.Tensor, s_post: Optional[torch.T
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
     _need(out, torch.float32, "out")
-    st = N.lib().nvfp4_fakequant_fwd(_ptr(x), rows, cols, _ptr(s_pre), _ptr(s_post), _ptr(out),
-                                     _stream(x.device))
-    N.check(st, "nvfp4_fakequant_fwd")
+    entry = "nvfp4_fakequant_fwd_amax" if amax else "nvfp4_fakequant_fwd"
+    st = getattr(N.lib(), entry)(_ptr(x), rows, cols, _ptr(s_pre), _ptr(s_post), _ptr(out),
+                                 _stream(x.device))
+    N.check(st, entry)
     return out
 
 
 def fakequant_bwd(x: torch.Tensor, grad: torch.Tensor, s_pre: torch.Tensor,
-                  s_post: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+                  s_post: Optional[torch.Tensor] = None, out: Optional[dict] = None, *,
+                  amax: bool = False):
     """Straight-through backward.  Returns (dx, ds) for tied scales and
-    (dx, ds_pre, ds_post) for dual scales."""
+    (dx, ds_pre, ds_post) for dual scales.  amax=True: the parameters are
+    block amaxes (s = a / 6) and the gradients are with respect to them."""
     _need(x, torch.bfloat16, "x")
     _need(grad, torch.float32, "grad")
     _need(s_pre, torch.float32, "s_pre")
@@ -357,7 +362,8 @@ def fakequant_bwd(x: torch.Tensor, grad: torch.Tensor, s_pre: torch.Tensor,
         dpost = out.get("ds_post")
         if dpost is None:
             dpost = torch.empty(s_post.shape, dtype=torch.float32, device=dev)
-    st = N.lib().nvfp4_fakequant_bwd(_ptr(x), _ptr(grad), rows, cols, _ptr(s_pre), _ptr(s_post),
-                                     _ptr(dx), _ptr(dpre), _ptr(dpost), _stream(dev))
-    N.check(st, "nvfp4_fakequant_bwd")
+    entry = "nvfp4_fakequant_bwd_amax" if amax else "nvfp4_fakequant_bwd"
+    st = getattr(N.lib(), entry)(_ptr(x), _ptr(grad), rows, cols, _ptr(s_pre), _ptr(s_post),
+                                 _ptr(dx), _ptr(dpre), _ptr(dpost), _stream(dev))
+    N.check(st, entry)
     return (dx, dpre) if s_post is None else (dx, dpre, dpost)

@@ -108,7 +108,8 @@ const char* nvfp4_status_string(int status) {
 static float resolve_sg(float global_fp8_max, int scale_fmt, int select) {
   if (global_fp8_max != 0.0f) return global_fp8_max;
   if (scale_fmt == NVFP4_SCALE_UE5M3) return NVFP4_GLOBAL_MAX_UE5M3;
-  return select == NVFP4_SELECT_4OVER6 ? NVFP4_GLOBAL_MAX_E4M3_4OVER6 : NVFP4_GLOBAL_MAX_E4M3;
+  return (select >= NVFP4_SELECT_4OVER6 && select <= NVFP4_SELECT_4OVER6_MAXERR)
+             ? NVFP4_GLOBAL_MAX_E4M3_4OVER6 : NVFP4_GLOBAL_MAX_E4M3;
 }
 
 int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* stream) {
@@ -124,7 +125,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* a
                    uint8_t* scales_t, unsigned long long* count4, void* stream) {
   if (!x || !amax || !size_ok(rows, cols)) return NVFP4_ERR_INVALID;
   if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (select != NVFP4_SELECT_6 && select != NVFP4_SELECT_4OVER6) return NVFP4_ERR_INVALID;
+  if (select < NVFP4_SELECT_6 || select > NVFP4_SELECT_SWEEP) return NVFP4_ERR_INVALID;
   if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
   if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
   if (axes != NVFP4_AXIS_ROW && axes != NVFP4_AXIS_COL && axes != (NVFP4_AXIS_ROW | NVFP4_AXIS_COL))
@@ -183,7 +184,7 @@ int nvfp4_quantize_rowscaled(const uint16_t* x, int64_t rows, int64_t cols, cons
                              unsigned long long* count4, void* stream) {
   if (!x || !row_amax || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
   if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (select != NVFP4_SELECT_6 && select != NVFP4_SELECT_4OVER6) return NVFP4_ERR_INVALID;
+  if (select < NVFP4_SELECT_6 || select > NVFP4_SELECT_SWEEP) return NVFP4_ERR_INVALID;
   if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
   if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
   if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
@@ -307,20 +308,21 @@ static int fq_common(const uint16_t* x, int64_t rows, int64_t cols, const float*
   return NVFP4_OK;
 }
 
-int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
-                        const float* s_post, float* xq_out, void* stream) {
+static int fq_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
+                  const float* s_post, float* xq_out, bool amax_param, void* stream) {
   int st = fq_common(x, rows, cols, s_pre);
   if (st != NVFP4_OK) return st;
   if (!xq_out || !aligned16(xq_out) || ((uintptr_t)s_post & 3u)) return NVFP4_ERR_INVALID;
   if (rows == 0 || cols == 0) return NVFP4_OK;
   FakeQuantArgs a = {};
   a.x = x; a.rows = rows; a.cols = cols; a.s_pre = s_pre; a.s_post = s_post; a.xq = xq_out;
+  a.amax_param = amax_param;
   return status_of(launch_fakequant_fwd(a, (hipStream_t)stream));
 }
 
-int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
-                        const float* s_pre, const float* s_post, float* grad_x,
-                        float* grad_s_pre, float* grad_s_post, void* stream) {
+static int fq_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
+                  const float* s_pre, const float* s_post, float* grad_x, float* grad_s_pre,
+                  float* grad_s_post, bool amax_param, void* stream) {
   int st = fq_common(x, rows, cols, s_pre);
   if (st != NVFP4_OK) return st;
   if (!grad_xq || !grad_x || !grad_s_pre) return NVFP4_ERR_INVALID;
@@ -331,8 +333,32 @@ int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, i
   if (rows == 0 || cols == 0) return NVFP4_OK;
   FakeQuantArgs a = {};
   a.x = x; a.g = grad_xq; a.rows = rows; a.cols = cols; a.s_pre = s_pre; a.s_post = s_post;
-  a.dx = grad_x; a.ds_pre = grad_s_pre; a.ds_post = grad_s_post;
+  a.dx = grad_x; a.ds_pre = grad_s_pre; a.ds_post = grad_s_post; a.amax_param = amax_param;
   return status_of(launch_fakequant_bwd(a, (hipStream_t)stream));
+}
+
+int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
+                        const float* s_post, float* xq_out, void* stream) {
+  return fq_fwd(x, rows, cols, s_pre, s_post, xq_out, false, stream);
+}
+
+int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
+                        const float* s_pre, const float* s_post, float* grad_x,
+                        float* grad_s_pre, float* grad_s_post, void* stream) {
+  return fq_bwd(x, grad_xq, rows, cols, s_pre, s_post, grad_x, grad_s_pre, grad_s_post, false,
+                stream);
+}
+
+int nvfp4_fakequant_fwd_amax(const uint16_t* x, int64_t rows, int64_t cols, const float* a_pre,
+                             const float* a_post, float* xq_out, void* stream) {
+  return fq_fwd(x, rows, cols, a_pre, a_post, xq_out, true, stream);
+}
+
+int nvfp4_fakequant_bwd_amax(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
+                             const float* a_pre, const float* a_post, float* grad_x,
+                             float* grad_a_pre, float* grad_a_post, void* stream) {
+  return fq_bwd(x, grad_xq, rows, cols, a_pre, a_post, grad_x, grad_a_pre, grad_a_post, true,
+                stream);
 }
 
 // ---------------------------------------------------------------- test hooks

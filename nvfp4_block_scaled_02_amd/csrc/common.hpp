@@ -7,7 +7,11 @@
 namespace nvfp4 {
 
 enum { FMT_E4M3 = 0, FMT_UE5M3 = 1 };
-enum { SELECT_6 = 0, SELECT_4OVER6 = 1 };
+// block-scale selection: max->6; Four-Over-Six by squared error, absolute
+// error or largest error; or the smallest squared error over every code
+enum { SELECT_6 = 0, SELECT_4OVER6 = 1, SELECT_4OVER6_MAE = 2, SELECT_4OVER6_MAXERR = 3,
+       SELECT_SWEEP = 4 };
+constexpr bool is_four_six(int select) { return select >= SELECT_4OVER6 && select <= SELECT_4OVER6_MAXERR; }
 enum { ROUND_RNE = 0, ROUND_SR = 1 };
 enum { AXIS_ROW = 1, AXIS_COL = 2 };
 
@@ -49,6 +53,7 @@ struct FakeQuantArgs {
   const float *s_pre, *s_post;
   float* xq;
   float *dx, *ds_pre, *ds_post;
+  bool amax_param;  // s_pre / s_post hold amaxes (s = a / 6); gradients w.r.t. them
 };
 
 // Re-quantization of an NVFP4 tensor: dequantize, transpose, quantize again

@@ -27,7 +27,22 @@ __device__ __forceinline__ float fq_inv(float s) {
 // 4 lanes share a block's scales.
 constexpr int kFqUnroll = 4;
 
-template <bool DUAL>
+// AMAX: the per-block parameters are amaxes a, the scales s = fl(a / 6), and
+// the scale gradients dL/da = dL/ds / 6 (the binary64 sums divided before
+// their rounding): the amax reparameterization of scale learning.
+template <bool AMAX>
+__device__ __forceinline__ float param_scale(float p) {
+  if constexpr (AMAX) return p / 6.0f;
+  else return p;
+}
+
+template <bool AMAX>
+__device__ __forceinline__ double param_grad(double g) {
+  if constexpr (AMAX) return g / 6.0;
+  else return g;
+}
+
+template <bool DUAL, bool AMAX>
 __global__ void __launch_bounds__(kThreads)
 fakequant_fwd_kernel(const uint2* __restrict__ x, int64_t nquads, const float* __restrict__ s_pre,
                      const float* __restrict__ s_post, float4* __restrict__ xq) {
@@ -42,6 +57,11 @@ fakequant_fwd_kernel(const uint2* __restrict__ x, int64_t nquads, const float* _
       w[u] = ok ? ld_nt(x + qd) : make_uint2(0, 0);
       sp[u] = ok ? s_pre[qd >> 2] : 0.0f;
       so[u] = DUAL ? (ok ? s_post[qd >> 2] : 0.0f) : sp[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kFqUnroll; ++u) {
+      sp[u] = param_scale<AMAX>(sp[u]);
+      so[u] = param_scale<AMAX>(so[u]);
     }
 #pragma unroll
     for (int u = 0; u < kFqUnroll; ++u) {
@@ -76,7 +96,7 @@ __device__ __forceinline__ double quad_seq_sum(const double (&t)[4], const doubl
 
 constexpr int kBwUnroll = 2;
 
-template <bool DUAL>
+template <bool DUAL, bool AMAX>
 __global__ void __launch_bounds__(kThreads)
 fakequant_bwd_kernel(const uint2* __restrict__ x, const float4* __restrict__ g, int64_t nquads,
                      const float* __restrict__ s_pre, const float* __restrict__ s_post,
@@ -96,6 +116,11 @@ fakequant_bwd_kernel(const uint2* __restrict__ x, const float4* __restrict__ g, 
       gv[u] = ok ? ld_nt(g + qd) : make_float4(0.f, 0.f, 0.f, 0.f);
       sp[u] = ok ? s_pre[qd >> 2] : 0.0f;
       so[u] = DUAL ? (ok ? s_post[qd >> 2] : 0.0f) : sp[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kBwUnroll; ++u) {
+      sp[u] = param_scale<AMAX>(sp[u]);
+      so[u] = param_scale<AMAX>(so[u]);
     }
 #pragma unroll
     for (int u = 0; u < kBwUnroll; ++u) {
@@ -128,7 +153,7 @@ fakequant_bwd_kernel(const uint2* __restrict__ x, const float4* __restrict__ g, 
           t[i] = (double)d;
         }
         const double s = quad_seq_sum(t, gd, lane4 == 0);
-        if (ok && lane4 == 3) ds_pre[qd >> 2] = (float)s;
+        if (ok && lane4 == 3) ds_pre[qd >> 2] = (float)param_grad<AMAX>(s);
       } else {
         const double ratio = sp[u] == 0.0f ? 0.0 : (double)so[u] / (double)sp[u];
         double tq[4], tx[4];
@@ -141,9 +166,10 @@ fakequant_bwd_kernel(const uint2* __restrict__ x, const float4* __restrict__ g, 
         const double spost = quad_seq_sum(tq, gd, lane4 == 0);
         const double tsum = quad_seq_sum(tx, gd, lane4 == 0);
         if (ok && lane4 == 3) {
-          ds_post[qd >> 2] = (float)spost;
+          ds_post[qd >> 2] = (float)param_grad<AMAX>(spost);
           const double spd = (double)sp[u];
-          ds_pre[qd >> 2] = sp[u] == 0.0f ? 0.0f : (float)(-((double)so[u] * tsum) / (spd * spd));
+          ds_pre[qd >> 2] =
+              sp[u] == 0.0f ? 0.0f : (float)param_grad<AMAX>(-((double)so[u] * tsum) / (spd * spd));
         }
       }
       if (ok) st_nt(make_float4(o[0], o[1], o[2], o[3]), dx + qd);
@@ -158,34 +184,44 @@ static int64_t grid_for(int64_t units, int64_t per_wg) {
   return grid < 1 ? 1 : grid;
 }
 
-hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s) {
+template <bool AMAX>
+static hipError_t launch_fwd(const FakeQuantArgs& a, hipStream_t s) {
   const int64_t nquads = a.rows * a.cols / 4;
   const int64_t grid = grid_for(nquads, (int64_t)kThreads * kFqUnroll);
   if (a.s_post)
-    hipLaunchKernelGGL(fakequant_fwd_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((fakequant_fwd_kernel<true, AMAX>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        reinterpret_cast<const uint2*>(a.x), nquads, a.s_pre, a.s_post,
                        reinterpret_cast<float4*>(a.xq));
   else
-    hipLaunchKernelGGL(fakequant_fwd_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((fakequant_fwd_kernel<false, AMAX>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        reinterpret_cast<const uint2*>(a.x), nquads, a.s_pre, a.s_post,
                        reinterpret_cast<float4*>(a.xq));
   return hipGetLastError();
 }
 
-hipError_t launch_fakequant_bwd(const FakeQuantArgs& a, hipStream_t s) {
+template <bool AMAX>
+static hipError_t launch_bwd(const FakeQuantArgs& a, hipStream_t s) {
   const int64_t nquads = a.rows * a.cols / 4;
   const int64_t grid = grid_for(nquads, (int64_t)kThreads * kBwUnroll);
   if (a.s_post)
-    hipLaunchKernelGGL(fakequant_bwd_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((fakequant_bwd_kernel<true, AMAX>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        reinterpret_cast<const uint2*>(a.x), reinterpret_cast<const float4*>(a.g),
                        nquads, a.s_pre, a.s_post, reinterpret_cast<float4*>(a.dx), a.ds_pre,
                        a.ds_post);
   else
-    hipLaunchKernelGGL(fakequant_bwd_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((fakequant_bwd_kernel<false, AMAX>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        reinterpret_cast<const uint2*>(a.x), reinterpret_cast<const float4*>(a.g),
                        nquads, a.s_pre, a.s_post, reinterpret_cast<float4*>(a.dx), a.ds_pre,
                        a.ds_post);
   return hipGetLastError();
+}
+
+hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s) {
+  return a.amax_param ? launch_fwd<true>(a, s) : launch_fwd<false>(a, s);
+}
+
+hipError_t launch_fakequant_bwd(const FakeQuantArgs& a, hipStream_t s) {
+  return a.amax_param ? launch_bwd<true>(a, s) : launch_bwd<false>(a, s);
 }
 
 }  // namespace nvfp4

@@ -83,7 +83,7 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
       }
     }
   }
-  if (SELECT == SELECT_4OVER6 && count4) flush_count<BLOCK>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<BLOCK>(count4, n4);
 }
 
 
@@ -140,7 +140,7 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
       n4 += o.four;
     }
   }
-  if (SELECT == SELECT_4OVER6 && count4) flush_count<BLOCK>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<BLOCK>(count4, n4);
 }
 
 // ---------------------------------------------------------------- per-row outer scales
@@ -182,7 +182,7 @@ quantize_rowscaled_kernel(const uint4* __restrict__ x, int64_t nblocks, int64_t 
       n4 += o.four;
     }
   }
-  if (SELECT == SELECT_4OVER6 && count4) flush_count<kThreads>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
 }
 
 // Long rows (at least 64 blocks): a wavefront owns whole rows.  Per row it
@@ -249,7 +249,7 @@ quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_b
       }
     }
   }
-  if (SELECT == SELECT_4OVER6 && count4) flush_count<kThreads>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
 }
 
 // ---------------------------------------------------------------- column-wise
@@ -421,7 +421,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
       }
     }
   }
-  if (SELECT == SELECT_4OVER6 && count4) flush_count<kThreads>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -430,9 +430,9 @@ template <int FMT, int SELECT, int ROUND, bool WIDE>
 static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int cus = device_cu_count();
-  const bool counting = a.select == SELECT_4OVER6 && a.count4 != nullptr;
+  const bool counting = is_four_six(a.select) && a.count4 != nullptr;
   if (a.axes == AXIS_ROW) {
-    if constexpr (SELECT == SELECT_4OVER6 || ROUND == ROUND_SR) {
+    if constexpr (SELECT != SELECT_6 || ROUND == ROUND_SR) {
       // one lane per block: these paths are bound by per-block arithmetic
       const int64_t nblocks = a.rows * a.cols / 16;
       const int64_t ngroups = (nblocks + 63) / 64;
@@ -492,15 +492,20 @@ static hipError_t launch_fmt(const QuantizeArgs& a, hipStream_t s) {
     return wide ? launch_typed<FMT, SELECT_6, ROUND_SR, true>(a, s)
                 : launch_typed<FMT, SELECT_6, ROUND_SR, false>(a, s);
   }
-  if (a.select == SELECT_4OVER6) return launch_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
-  return launch_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
+  switch (a.select) {
+    case SELECT_4OVER6: return launch_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
+    case SELECT_4OVER6_MAE: return launch_typed<FMT, SELECT_4OVER6_MAE, ROUND_RNE, false>(a, s);
+    case SELECT_4OVER6_MAXERR: return launch_typed<FMT, SELECT_4OVER6_MAXERR, ROUND_RNE, false>(a, s);
+    case SELECT_SWEEP: return launch_typed<FMT, SELECT_SWEEP, ROUND_RNE, false>(a, s);
+    default: return launch_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
+  }
 }
 
 template <int FMT, int SELECT, int ROUND, bool WIDE>
 static hipError_t launch_rowscaled_typed(const QuantizeArgs& a, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int64_t cus = device_cu_count();
-  const bool counting = a.select == SELECT_4OVER6 && a.count4 != nullptr;
+  const bool counting = is_four_six(a.select) && a.count4 != nullptr;
   const int64_t nblocks = a.rows * a.cols / 16;
   const int64_t row_blocks = a.cols / 16;
   const int64_t cap = counting ? cus : cus * 8;  // counting: one atomic per workgroup
@@ -532,8 +537,13 @@ static hipError_t launch_rowscaled_fmt(const QuantizeArgs& a, hipStream_t s) {
     return wide ? launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, true>(a, s)
                 : launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, false>(a, s);
   }
-  if (a.select == SELECT_4OVER6) return launch_rowscaled_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
-  return launch_rowscaled_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
+  switch (a.select) {
+    case SELECT_4OVER6: return launch_rowscaled_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
+    case SELECT_4OVER6_MAE: return launch_rowscaled_typed<FMT, SELECT_4OVER6_MAE, ROUND_RNE, false>(a, s);
+    case SELECT_4OVER6_MAXERR: return launch_rowscaled_typed<FMT, SELECT_4OVER6_MAXERR, ROUND_RNE, false>(a, s);
+    case SELECT_SWEEP: return launch_rowscaled_typed<FMT, SELECT_SWEEP, ROUND_RNE, false>(a, s);
+    default: return launch_rowscaled_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
+  }
 }
 
 hipError_t launch_quantize_rowscaled(const QuantizeArgs& a, hipStream_t s) {

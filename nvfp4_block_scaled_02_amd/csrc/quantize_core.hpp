@@ -153,6 +153,36 @@ __device__ __forceinline__ float block_sse(uint32_t w0, uint32_t w1, const float
   return (P[0] + P[1]) + (P[2] + P[3]);
 }
 
+// Error of one candidate over a whole block by the selection rule, from the
+// residuals d_e = fmaf(-q_e, S, x_e): the squared error (block_sse), the
+// absolute error (the same 4x4 tree with additions of |d|) or the largest
+// |d| (an IEEE maximum, order-free).
+template <int SELECT>
+__device__ __forceinline__ float block_err(uint32_t w0, uint32_t w1, const float (&x)[16], float S) {
+  if constexpr (SELECT == SELECT_4OVER6_MAE || SELECT == SELECT_4OVER6_MAXERR) {
+    float qa[8], qb[8];
+    e2m1_unpack8(w0, qa);
+    e2m1_unpack8(w1, qb);
+    float d[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      d[e] = __builtin_fabsf(__builtin_fmaf(-(e < 8 ? qa[e] : qb[e - 8]), S, x[e]));
+    if constexpr (SELECT == SELECT_4OVER6_MAXERR) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(d[e], d[e + 1]));
+      return m;
+    } else {
+      float P[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) P[k] = ((0.0f + d[4 * k]) + d[4 * k + 1] + d[4 * k + 2]) + d[4 * k + 3];
+      return (P[0] + P[1]) + (P[2] + P[3]);
+    }
+  } else {
+    return block_sse(w0, w1, x, S);
+  }
+}
+
 // Quantize a whole block (chunks a, b) in one lane: no partner exchange and
 // no duplicated scale encode, which the lane-pair form pays for.  hbase as
 // in quantize_half, for element 0 of the block (idx0 a multiple of 16).
@@ -211,6 +241,38 @@ __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const
     }
     o.scale = c6;
     o.four = 0;
+  } else if constexpr (SELECT == SELECT_SWEEP) {
+    // every finite scale code, ascending; a strictly smaller squared error
+    // replaces the best (ties keep the smaller code); round-to-nearest only
+    auto enc = [&](uint32_t c, uint32_t& w0, uint32_t& w1) {
+      const f32x2 t = scale_of<FMT, DIRECT>(tab, c, ts.alpha);
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = x[i] * t[1];
+      w0 = e2m1_rne_pack8(y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t[1];
+      w1 = e2m1_rne_pack8(y);
+      return block_sse(w0, w1, x, t[0]);
+    };
+    uint32_t b0, b1;
+    float best = enc(0u, b0, b1);
+    uint32_t bc = 0;
+#pragma unroll 1
+    for (uint32_t c = 1; c < (uint32_t)FmtTraits<FMT>::kCodes; ++c) {
+      uint32_t w0, w1;
+      const float e = enc(c, w0, w1);
+      if (e < best) {
+        best = e;
+        bc = c;
+        b0 = w0;
+        b1 = w1;
+      }
+    }
+    o.c0 = b0;
+    o.c1 = b1;
+    o.scale = bc;
+    o.four = 0;
   } else {
     const uint32_t cc = encode_pair(FMT, m * ts.k6, m * ts.k4);
     const uint32_t c6 = cc & 0xFFu, c4 = cc >> 8;
@@ -229,8 +291,8 @@ __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = x[8 + i] * t4[1];
     const uint32_t b4 = e2m1_rne_pack8(y);
-    const float e6 = block_sse(a6, b6, x, t6[0]);
-    const float e4 = block_sse(a4, b4, x, t4[0]);
+    const float e6 = block_err<SELECT>(a6, b6, x, t6[0]);
+    const float e4 = block_err<SELECT>(a4, b4, x, t4[0]);
     const bool four = e4 < e6;
     o.c0 = four ? a4 : a6;
     o.c1 = four ? b4 : b6;

@@ -27,7 +27,7 @@ def _declared():
 
 def test_library_loads_and_version():
     lib = N.lib()
-    assert lib.nvfp4_abi_version() == 3
+    assert lib.nvfp4_abi_version() == 4
 
 
 def test_every_declared_symbol_is_exported_and_bound():
@@ -58,8 +58,9 @@ def _q(**kw):
 
 @pytest.mark.parametrize("kw", [
     dict(x=None), dict(amax=None), dict(rows=-1), dict(cols=-16), dict(cols=24),
-    dict(fmt=2), dict(select=2), dict(rnd=2), dict(axes=0), dict(axes=4),
-    dict(rnd=1, select=1), dict(gmax=-1.0), dict(gmax=float("inf")), dict(gmax=float("nan")),
+    dict(fmt=2), dict(select=5), dict(select=-1), dict(rnd=2), dict(axes=0), dict(axes=4),
+    dict(rnd=1, select=1), dict(rnd=1, select=2), dict(rnd=1, select=3), dict(rnd=1, select=4),
+    dict(gmax=-1.0), dict(gmax=float("inf")), dict(gmax=float("nan")),
     dict(codes=None), dict(scales=None), dict(axes=2, rows=24), dict(axes=2, codes_t=None),
     dict(axes=3, scales_t=None), dict(axes=2, cols=20, rows=16), dict(x=FAKE_ODD),
     dict(codes=FAKE_ODD), dict(scales=FAKE + 2), dict(count4=FAKE_ODD),
@@ -143,8 +144,8 @@ def _qrs(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(x=None), dict(ra=None), dict(rows=-1), dict(cols=24), dict(fmt=2), dict(select=2),
-    dict(rnd=2), dict(rnd=1, select=1), dict(gmax=-1.0), dict(gmax=float("nan")),
+    dict(x=None), dict(ra=None), dict(rows=-1), dict(cols=24), dict(fmt=2), dict(select=5),
+    dict(rnd=2), dict(rnd=1, select=1), dict(rnd=1, select=4), dict(gmax=-1.0), dict(gmax=float("nan")),
     dict(codes=None), dict(scales=None), dict(codes=FAKE_ODD), dict(scales=FAKE + 2),
     dict(x=FAKE_ODD), dict(ra=FAKE + 2), dict(count4=FAKE_ODD),
 ])
@@ -234,6 +235,20 @@ def test_dequantized_amax_rejects(kw):
     assert N.lib().nvfp4_dequantized_amax(a["codes"], a["scales"], a["rows"], a["cols"],
                                           a["amax"], a["ra"], a["gmax"], a["fmt"], a["out"],
                                           None) == N.ERR_INVALID
+
+
+@pytest.mark.parametrize("entry", ["nvfp4_fakequant_fwd_amax", "nvfp4_fakequant_bwd_amax"])
+def test_fakequant_amax_rejects(entry):
+    lib = N.lib()
+    if entry.endswith("fwd_amax"):
+        f = lambda **k: lib.nvfp4_fakequant_fwd_amax(k.get("x", FAKE), 16, k.get("cols", 32),
+                                                     k.get("a", FAKE), None, k.get("o", FAKE), None)
+    else:
+        f = lambda **k: lib.nvfp4_fakequant_bwd_amax(k.get("x", FAKE), FAKE, 16, k.get("cols", 32),
+                                                     k.get("a", FAKE), None, k.get("o", FAKE),
+                                                     FAKE, None, None)
+    for kw in (dict(x=None), dict(a=None), dict(cols=24), dict(o=FAKE_ODD), dict(x=FAKE_ODD)):
+        assert f(**kw) == N.ERR_INVALID, kw
 
 
 def test_test_hooks_reject():

@@ -329,6 +329,8 @@ def run_qat(args, torch, np, nv, synth, dev, timer):
     _, s = nv.dequantize(q.codes, q.scales, amax, global_max=448.0, want_block_scale=True)
     ss = [s, s.clone()]
     sp = [(s * 1.125).contiguous(), (s * 1.125).contiguous()]
+    aa = [(s * 6.0).contiguous() for _ in range(nsets)]
+    ap = [(s * 6.75).contiguous() for _ in range(nsets)]
     xq = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(nsets)]
     outs = [{"dx": torch.empty((rows, cols), dtype=torch.float32, device=dev),
              "ds_pre": torch.empty_like(s), "ds_post": torch.empty_like(s)} for _ in range(nsets)]
@@ -343,9 +345,15 @@ def run_qat(args, torch, np, nv, synth, dev, timer):
             xs[i % 2], ss[i % 2], sp[i % 2], out=xq[i % 2]), reps, nsets),
         "fakequant_bwd_dual": timer.avg_us(lambda i: nv.fakequant_bwd(
             xs[i % 2], gs[i % 2], ss[i % 2], sp[i % 2], out=outs[i % 2]), reps, nsets),
+        # the amax reparameterization (block amaxes 6 s in place of the scales)
+        "fakequant_fwd_dual_amax": timer.avg_us(lambda i: nv.fakequant_fwd(
+            xs[i % 2], aa[i % 2], ap[i % 2], out=xq[i % 2], amax=True), reps, nsets),
+        "fakequant_bwd_dual_amax": timer.avg_us(lambda i: nv.fakequant_bwd(
+            xs[i % 2], gs[i % 2], aa[i % 2], ap[i % 2], out=outs[i % 2], amax=True), reps, nsets),
     }
     bpe = {"fakequant_fwd_tied": B_FQ_FWD["tied"], "fakequant_bwd_tied": B_FQ_BWD["tied"],
-           "fakequant_fwd_dual": B_FQ_FWD["dual"], "fakequant_bwd_dual": B_FQ_BWD["dual"]}
+           "fakequant_fwd_dual": B_FQ_FWD["dual"], "fakequant_bwd_dual": B_FQ_BWD["dual"],
+           "fakequant_fwd_dual_amax": B_FQ_FWD["dual"], "fakequant_bwd_dual_amax": B_FQ_BWD["dual"]}
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = (us["fakequant_fwd_dual"] + us["fakequant_bwd_dual"]) / 1e3
     step_bytes = n * (bpe["fakequant_fwd_dual"] + bpe["fakequant_bwd_dual"])
@@ -499,6 +507,46 @@ def run_requant(args, torch, np, nv, synth, dev, timer):
                          "dequantized_amax": kernels["dequantized_amax"]}, args)
 
 
+def run_select(args, torch, np, nv, synth, dev, timer):
+    """The block-scale selection rules on the 8192x4096 activation, row-wise,
+    per-tensor outer scale: Four-Over-Six by squared, absolute and largest
+    error (with the count), and the MSE scale sweep over every E4M3 code (the
+    step: the scale-learning initialization)."""
+    nsets = 8
+    xb = synth.make("activation")["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    x0 = to_dev(torch, np, xb, dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    amax = nv.tensor_amax(x0)
+    outs = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+             "count4": torch.zeros(1, dtype=torch.int64, device=dev)} for _ in range(nsets)]
+    nocount = [{"codes": o["codes"], "scales": o["scales"]} for o in outs]
+
+    def q(select, count):
+        return lambda i: nv.quantize(xs[i % nsets], amax, select=select,
+                                     out=(outs if count else nocount)[i % nsets])
+
+    reps = max(args.steps, 40)
+    us = {"quantize_4over6_mse": timer.avg_us(q("4over6", True), reps, nsets),
+          "quantize_4over6_mae": timer.avg_us(q("4over6-mae", True), reps, nsets),
+          "quantize_4over6_maxerr": timer.avg_us(q("4over6-maxerr", True), reps, nsets),
+          "quantize_sweep_mse": timer.avg_us(q("sweep", False), max(args.steps // 10, 5), nsets)}
+    kernels = {k: kernel_entry(us[k], n, B_QUANT) for k in us}
+    ms_step = us["quantize_sweep_mse"] / 1e3
+    line = base_line("NVFP4 MSE scale sweep (all E4M3 codes) GB/s at 8192x4096 bf16",
+                     n * B_QUANT / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     "activation 8192x4096 bf16 (seed 2), per-tensor outer scale (FP8 max 448 for "
+                     "the sweep, 256 for the Four-Over-Six rules); row-wise",
+                     {"rows": rows, "cols": cols, "elements": n,
+                      "timing": "per-kernel event averages"}, n)
+    line = finish(line, kernels, args)
+    # the sweep is bound by its per-candidate arithmetic, not by HBM
+    line["roofline"]["bound"] = "alu"
+    return line
+
+
 def run_gradient(args, torch, np, nv, synth, dev, timer):
     log("generating the 16384x8192 gradient")
     xb = synth.make("gradient")["x"]
@@ -556,7 +604,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="activation",
                     choices=["activation", "weight-1k", "weight", "qat", "gradient",
-                             "activation-pertoken", "weight-2d", "requant"])
+                             "activation-pertoken", "weight-2d", "requant", "select"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 256 MiB copy and each kernel of the workload twice (for PMC counters)")
@@ -588,6 +636,8 @@ def main():
         line = run_weight_2d(args, torch, np, nv, synth, dev, timer)
     elif args.workload == "requant":
         line = run_requant(args, torch, np, nv, synth, dev, timer)
+    elif args.workload == "select":
+        line = run_select(args, torch, np, nv, synth, dev, timer)
     else:
         line = run_gradient(args, torch, np, nv, synth, dev, timer)
     if line is not None:

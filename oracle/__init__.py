@@ -111,6 +111,21 @@ def _load():
     lib.or_mxfp8_quantize_sr.argtypes = [_f32p, _i64, _i64, _i64, ctypes.c_uint64, _u8p, _u8p]
     lib.or_mxfp8_dequantize.restype = ctypes.c_int
     lib.or_mxfp8_dequantize.argtypes = [_u8p, _u8p, _i64, _i64, _f32p]
+    lib.or_rht_signs.restype = ctypes.c_uint32
+    lib.or_rht_signs.argtypes = [ctypes.c_uint64]
+    lib.or_rht16.restype = None
+    lib.or_rht16.argtypes = [_f32p, ctypes.c_uint32, _f32p]
+    lib.or_irht16.restype = None
+    lib.or_irht16.argtypes = [_f32p, ctypes.c_uint32, _f32p]
+    lib.or_rht_amax.restype = ctypes.c_float
+    lib.or_rht_amax.argtypes = [_f32p, _i64, _i64, ctypes.c_int, ctypes.c_uint64]
+    lib.or_quantize_rht.restype = ctypes.c_int
+    lib.or_quantize_rht.argtypes = [_f32p, _i64, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                    ctypes.c_int, _u8p, _u8p, _u64p]
+    lib.or_dequantize_rht.restype = ctypes.c_int
+    lib.or_dequantize_rht.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_int, ctypes.c_uint64, _f32p]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_num_threads.argtypes = []
     _lib = lib
@@ -471,4 +486,62 @@ def mxfp8_dequantize(elems, scales):
     st = _load().or_mxfp8_dequantize(_ptr(el, _u8p), _ptr(sc, _u8p), rows, cols, _ptr(out, _f32p))
     if st != 0:
         raise ValueError(f"oracle mxfp8_dequantize rejected the arguments (status {st})")
+    return out
+
+
+# ---------------------------------------------------------------- random Hadamard transform
+AXIS_ROW, AXIS_COL = 1, 2
+
+
+def rht_signs(sign_seed):
+    """Bit j set: s_j = -1 (the tensor's sign vector)."""
+    return _load().or_rht_signs(int(sign_seed))
+
+
+def rht16(x16, sign_seed=0, *, inverse=False):
+    x = np.ascontiguousarray(np.asarray(x16, np.float32).reshape(16))
+    y = np.empty(16, np.float32)
+    fn = _load().or_irht16 if inverse else _load().or_rht16
+    fn(_ptr(x, _f32p), rht_signs(sign_seed), _ptr(y, _f32p))
+    return y
+
+
+def rht_amax(x, *, axis=AXIS_ROW, sign_seed=0):
+    xf = as_f32(x)
+    return _load().or_rht_amax(_ptr(xf, _f32p), xf.shape[0], xf.shape[1], int(axis), int(sign_seed))
+
+
+def quantize_rht(x, amax, *, axis=AXIS_ROW, sign_seed=0, fmt=FMT_E4M3, select=SELECT_4OVER6,
+                 rounding=ROUND_RNE, seed=0, global_max=None):
+    """Quantization of the block-wise transformed tensor.  axis ROW: row-wise
+    layout; COL: the column-wise layout (of the transpose).  Returns (codes,
+    scales, count4)."""
+    xf = as_f32(x)
+    rows, cols = xf.shape
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, select) if global_max is None else float(global_max)
+    R, C = (rows, cols) if axis == AXIS_ROW else (cols, rows)
+    codes = np.empty((R, C // 2), np.uint8)
+    scales = np.empty((R, C // 16), np.uint8)
+    cnt = np.zeros(1, np.uint64)
+    st = _load().or_quantize_rht(_ptr(xf, _f32p), rows, cols, float(amax), sg, fmt, int(select),
+                                 int(rounding), int(seed), int(sign_seed), int(axis),
+                                 _ptr(codes, _u8p), _ptr(scales, _u8p), _ptr(cnt, _u64p))
+    if st != 0:
+        raise ValueError(f"oracle quantize_rht rejected the arguments (status {st})")
+    return codes, scales, int(cnt[0])
+
+
+def dequantize_rht(codes, scales, amax, *, sign_seed=0, fmt=FMT_E4M3, select=SELECT_4OVER6,
+                   global_max=None):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, half = codes.shape
+    fmt = _fmt(fmt)
+    sg = default_global_max(fmt, select) if global_max is None else float(global_max)
+    out = np.empty((rows, half * 2), np.float32)
+    st = _load().or_dequantize_rht(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, half * 2,
+                                   float(amax), sg, fmt, int(sign_seed), _ptr(out, _f32p))
+    if st != 0:
+        raise ValueError(f"oracle dequantize_rht rejected the arguments (status {st})")
     return out

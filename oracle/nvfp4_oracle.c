@@ -857,6 +857,124 @@ static int fq_bwd(const float *x, const float *g, int64_t rows, int64_t cols, co
   return OR_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* 16-point random Hadamard transform ([46b] Method: NVIDIA's recipe applies
+ * a random Hadamard transform to both inputs of the weight-gradient GEMM;
+ * [E2E] Quantized communications: an orthogonal rotation that spreads
+ * outliers and is inverted exactly; [UE] 背景: part of the NVFP4 recipe).
+ * Per 16-element block (the NVFP4 block, along the quantized axis):
+ *   y = H16 * diag(s) * x / 4,
+ * H16 the Sylvester Hadamard matrix (entries +-1, H16 H16 = 16 I), s a
+ * +-1 vector shared by the whole tensor: s_j = -1 iff the top bit of the
+ * counter hash of (sign_seed, j) is set (j = 0..15).  Binary32, in this
+ * order: t_j = x_j * (s_j * 0.25) (exact unless the result is subnormal),
+ * then the fast Walsh-Hadamard butterfly, stages h = 1, 2, 4, 8, each
+ * replacing (t_i, t_{i+h}) by (t_i + t_{i+h}, t_i - t_{i+h}) for the i with
+ * bit h clear.  The inverse (H16 / 4 is symmetric and orthogonal):
+ * t_j = y_j * 0.25, the same butterfly, then x_j = s_j * t_j. */
+uint32_t or_rht_signs(uint64_t sign_seed) {
+  uint32_t m = 0;
+  for (int j = 0; j < 16; ++j)
+    if (or_sr_hash(sign_seed, (uint64_t)j) >> 31) m |= 1u << j;
+  return m;
+}
+
+static void fwht16(float t[16]) {
+  for (int h = 1; h < 16; h <<= 1)
+    for (int i = 0; i < 16; ++i)
+      if (!(i & h)) {
+        float a = t[i], b = t[i + h];
+        t[i] = a + b;
+        t[i + h] = a - b;
+      }
+}
+
+void or_rht16(const float x[16], uint32_t signs, float y[16]) {
+  for (int j = 0; j < 16; ++j) y[j] = x[j] * (((signs >> j) & 1) ? -0.25f : 0.25f);
+  fwht16(y);
+}
+
+void or_irht16(const float y[16], uint32_t signs, float x[16]) {
+  for (int j = 0; j < 16; ++j) x[j] = y[j] * 0.25f;
+  fwht16(x);
+  for (int j = 0; j < 16; ++j)
+    if ((signs >> j) & 1) x[j] = -x[j];
+}
+
+/* The tensor with every block transformed: axis 1 = row blocks (16
+ * consecutive elements of a row), axis 2 = column blocks (16 consecutive
+ * rows of a column). */
+static float *rht_tensor(const float *x, int64_t rows, int64_t cols, int axis, uint32_t signs) {
+  float *y = (float *)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+  float a[16], b[16];
+  if (axis == 1) {
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; c += 16) {
+        or_rht16(x + r * cols + c, signs, b);
+        memcpy(y + r * cols + c, b, sizeof b);
+      }
+  } else {
+    for (int64_t r = 0; r < rows; r += 16)
+      for (int64_t c = 0; c < cols; ++c) {
+        for (int i = 0; i < 16; ++i) a[i] = x[(r + i) * cols + c];
+        or_rht16(a, signs, b);
+        for (int i = 0; i < 16; ++i) y[(r + i) * cols + c] = b[i];
+      }
+  }
+  return y;
+}
+
+/* Amax of the transformed tensor (the outer scale of its quantization). */
+float or_rht_amax(const float *x, int64_t rows, int64_t cols, int axis, uint64_t sign_seed) {
+  if (rows < 0 || cols < 0 || (axis == 1 && cols % 16) || (axis == 2 && rows % 16) ||
+      (axis != 1 && axis != 2))
+    return NAN;
+  float *y = rht_tensor(x, rows, cols, axis, or_rht_signs(sign_seed));
+  float m = or_tensor_amax(y, rows * cols);
+  free(y);
+  return m;
+}
+
+/* Quantization of the transformed tensor: axis 1 = row-wise (codes[rows,
+ * cols/2], scales[rows, cols/16]), axis 2 = column-wise (the layout of the
+ * transposed tensor, codes[cols, rows/2], scales[cols, rows/16]); every other
+ * argument as or_quantize (SR indices in the output orientation). */
+int or_quantize_rht(const float *x, int64_t rows, int64_t cols, float amax, float sg, int fmt,
+                    int select, int rounding, uint64_t seed, uint64_t sign_seed, int axis,
+                    uint8_t *codes, uint8_t *scales, uint64_t *count4) {
+  if (rows < 0 || cols < 0 || (axis != 1 && axis != 2)) return OR_EINVAL;
+  if ((axis == 1 && cols % 16) || (axis == 2 && rows % 16)) return OR_EINVAL;
+  float *y = rht_tensor(x, rows, cols, axis, or_rht_signs(sign_seed));
+  int st;
+  if (axis == 1) {
+    st = or_quantize(y, rows, cols, 0, amax, sg, fmt, select, rounding, seed, codes, scales, count4,
+                     NULL, NULL);
+  } else {
+    float *t = transpose_f32(y, rows, cols);
+    st = or_quantize(t, cols, rows, 0, amax, sg, fmt, select, rounding, seed, codes, scales, count4,
+                     NULL, NULL);
+    free(t);
+  }
+  free(y);
+  return st;
+}
+
+/* Dequantization followed by the inverse transform of every row block:
+ * out = RHT^-1(x_hat) (binary32), for tensors quantized row-wise by
+ * or_quantize_rht with axis 1 (or column-wise, given the transposed layout). */
+int or_dequantize_rht(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                      float amax, float sg, int fmt, uint64_t sign_seed, float *out) {
+  int st = or_dequantize(codes, scales, rows, cols, amax, sg, fmt, out, NULL, NULL);
+  if (st != OR_OK) return st;
+  const uint32_t signs = or_rht_signs(sign_seed);
+  float b[16];
+  for (int64_t i = 0; i < rows * cols; i += 16) {
+    or_irht16(out + i, signs, b);
+    memcpy(out + i, b, sizeof b);
+  }
+  return OR_OK;
+}
+
 /* Number of OpenMP threads the parallel loops above use. */
 int or_num_threads(void) {
 #ifdef _OPENMP

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 
 /* Status codes. */
 enum {
@@ -350,6 +350,49 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows
                        int scale_fmt, int target, const float* dst_amax, float dst_global_fp8_max,
                        int dst_scale_fmt, uint64_t seed, uint8_t* out_t, uint8_t* out_scales_t,
                        void* stream);
+
+/*
+ * 16-point random Hadamard transform around quantization ("Four Over Six"
+ * notes, Method: NVIDIA's recipe applies it to both inputs of the weight-
+ * gradient GEMM; "End-to-End 4-Bit Training", Quantized communications: an
+ * orthogonal rotation that spreads outliers and is inverted exactly).  Per
+ * NVFP4 block (16 consecutive elements of a row for axis ROW, 16 consecutive
+ * rows of a column for axis COL):
+ *   y = H16 diag(s) x / 4,
+ * H16 the Sylvester Hadamard matrix, s_j = -1 iff the top bit of the counter
+ * hash of (sign_seed, j) is set (one sign vector per tensor), computed in
+ * binary32 as x_j * (+-0.25) followed by the fast Walsh-Hadamard butterfly
+ * (stages 1, 2, 4, 8; (a, b) -> (a + b, a - b)).  The inverse scales by
+ * 0.25, runs the same butterfly and applies the signs.
+ *
+ * nvfp4_rht_amax -- *amax_out = max |y| over the transformed tensor (the
+ * outer amax for nvfp4_quantize_rht; NaN if any element is NaN).  x [rows,
+ * cols] bf16; ROW: cols % 16 == 0, x 16-byte aligned; COL: rows % 16 == 0.
+ *
+ * nvfp4_quantize_rht -- nvfp4_quantize of the transformed tensor, along one
+ * axis: ROW writes codes [rows, cols/2] and scales [rows, cols/16]; COL
+ * writes the column-wise layout (of the transpose), codes [cols, rows/2] and
+ * scales [cols, rows/16].  amax, global_fp8_max, scale_fmt, select,
+ * rounding, seed and count4 as nvfp4_quantize (SR indices in the output
+ * orientation).
+ *
+ * nvfp4_dequantize_rht -- x_hat of an NVFP4 tensor [rows, cols] (as
+ * nvfp4_dequantize), then the inverse transform of every 16-element row
+ * block: out_f32 [rows, cols] (16-byte aligned).  For a COL-quantized
+ * tensor pass its layout ([cols, rows]); the result is then the transpose.
+ * Errors: NULL or misaligned pointers, shapes not multiples of 16 along the
+ * blocked axis, unknown enums, SR with a select other than SELECT_6 ->
+ * NVFP4_ERR_INVALID.
+ */
+int nvfp4_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint64_t sign_seed,
+                   float* amax_out, void* stream);
+int nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                       float global_fp8_max, int scale_fmt, int select, int rounding, int axis,
+                       uint64_t seed, uint64_t sign_seed, uint8_t* codes, uint8_t* scales,
+                       unsigned long long* count4, void* stream);
+int nvfp4_dequantize_rht(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                         const float* amax, float global_fp8_max, int scale_fmt,
+                         uint64_t sign_seed, float* out_f32, void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(int status);

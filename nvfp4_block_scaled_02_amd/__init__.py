@@ -5,9 +5,11 @@ ABI of include/nvfp4.h); this package is its Python binding.  Importing it
 does not load the library; the first call does, and raises if it is not built.
 """
 from .api import (Quantized, default_global_max, dequantize, dequantize_rowscaled,
-                  dequantized_amax, fakequant_bwd, fakequant_fwd, quantize, quantize_2d,
-                  quantize_rowscaled, requantize_t, row_amax, tensor_amax)
+                  dequantize_rht, dequantized_amax, fakequant_bwd, fakequant_fwd, quantize,
+                  quantize_2d, quantize_rht, quantize_rowscaled, requantize_t, rht_amax, row_amax,
+                  tensor_amax)
 
 __all__ = ["Quantized", "default_global_max", "dequantize", "dequantize_rowscaled",
-           "dequantized_amax", "fakequant_bwd", "fakequant_fwd", "quantize", "quantize_2d",
-           "quantize_rowscaled", "requantize_t", "row_amax", "tensor_amax"]
+           "dequantize_rht", "dequantized_amax", "fakequant_bwd", "fakequant_fwd", "quantize",
+           "quantize_2d", "quantize_rht", "quantize_rowscaled", "requantize_t", "rht_amax",
+           "row_amax", "tensor_amax"]

@@ -47,6 +47,10 @@ SIGNATURES = {
     "nvfp4_dequantized_amax": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _f32, _int, _vp, _vp]),
     "nvfp4_requantize_t": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _f32, _int, _int, _vp, _f32,
                                   _int, _u64, _vp, _vp, _vp]),
+    "nvfp4_rht_amax": (_int, [_vp, _i64, _i64, _int, _u64, _vp, _vp]),
+    "nvfp4_quantize_rht": (_int, [_vp, _i64, _i64, _vp, _f32, _int, _int, _int, _int, _u64, _u64,
+                                  _vp, _vp, _vp, _vp]),
+    "nvfp4_dequantize_rht": (_int, [_vp, _vp, _i64, _i64, _vp, _f32, _int, _u64, _vp, _vp]),
     "nvfp4_test_e2m1_rne_range": (_int, [_u32, _i64, _vp, _vp]),
     "nvfp4_test_e2m1_sr": (_int, [_vp, _vp, _i64, _vp, _vp]),
     "nvfp4_test_scale_encode_range": (_int, [_int, _u32, _i64, _vp, _vp]),

@@ -318,6 +318,71 @@ def requantize_t(codes: torch.Tensor, scales: torch.Tensor, *,
     return out["out_t"], out["scales_t"]
 
 
+# ---------------------------------------------------------------- random Hadamard transform
+_AXIS1 = {"row": N.AXIS_ROW, "col": N.AXIS_COL}
+
+
+def rht_amax(x: torch.Tensor, *, axis: str = "row", sign_seed: int = 0,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """max |y| of the tensor with every block (row blocks or column blocks)
+    transformed by the 16-point random Hadamard transform."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, "out")
+    st = N.lib().nvfp4_rht_amax(_ptr(x), rows, cols, _AXIS1[axis], int(sign_seed) & (2 ** 64 - 1),
+                                _ptr(out), _stream(x.device))
+    N.check(st, "nvfp4_rht_amax")
+    return out
+
+
+def quantize_rht(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, axis: str = "row",
+                 sign_seed: int = 0, fmt: str = "e4m3", select: str = "4over6",
+                 rounding: str = "rne", seed: int = 0, global_max: float = 0.0,
+                 count4: bool = False, out: Optional[dict] = None) -> Quantized:
+    """NVFP4 quantization of the block-wise transformed tensor along one axis
+    ("row": row-wise layout; "col": the column-wise layout of the transpose).
+    amax defaults to the transformed tensor's amax."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if amax is None:
+        amax = rht_amax(x, axis=axis, sign_seed=sign_seed)
+    _need(amax, torch.float32, "amax")
+    R, C = (rows, cols) if axis == "row" else (cols, rows)
+    dev = x.device
+    out = dict(out or {})
+    out.setdefault("codes", torch.empty((R, C // 2), dtype=torch.uint8, device=dev))
+    out.setdefault("scales", torch.empty((R, C // 16), dtype=torch.uint8, device=dev))
+    if count4 and "count4" not in out:
+        out["count4"] = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = N.lib().nvfp4_quantize_rht(
+        _ptr(x), rows, cols, _ptr(amax), float(global_max), _FMT[fmt], _SELECT[select],
+        _ROUND[rounding], _AXIS1[axis], int(seed) & (2 ** 64 - 1), int(sign_seed) & (2 ** 64 - 1),
+        _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out.get("count4")), _stream(dev))
+    N.check(st, "nvfp4_quantize_rht")
+    gm = float(global_max) if global_max else default_global_max(fmt, select)
+    return Quantized(out["codes"], out["scales"], None, None, amax, gm, fmt, out.get("count4"))
+
+
+def dequantize_rht(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
+                   global_max: float, fmt: str = "e4m3", sign_seed: int = 0,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x_hat followed by the inverse transform of every row block (float32)."""
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    _need(amax, torch.float32, "amax")
+    rows, half = codes.shape
+    if out is None:
+        out = torch.empty((rows, 2 * half), dtype=torch.float32, device=codes.device)
+    _need(out, torch.float32, "out")
+    st = N.lib().nvfp4_dequantize_rht(_ptr(codes), _ptr(scales), rows, 2 * half, _ptr(amax),
+                                      float(global_max), _FMT[fmt], int(sign_seed) & (2 ** 64 - 1),
+                                      _ptr(out), _stream(codes.device))
+    N.check(st, "nvfp4_dequantize_rht")
+    return out
+
+
 def fakequant_fwd(x: torch.Tensor, s_pre: torch.Tensor, s_post: Optional[torch.Tensor] = None,
                   out: Optional[torch.Tensor] = None, *, amax: bool = False) -> torch.Tensor:
     """x~ = s_post * clamp(round_E2M1(x / s_pre), -6, 6) per 16-element block.

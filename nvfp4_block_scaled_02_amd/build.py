@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["api.hip", "amax.hip", "quantize.hip", "dequantize.hip", "fakequant.hip", "requant.hip"]
+SOURCES = ["api.hip", "amax.hip", "quantize.hip", "dequantize.hip", "fakequant.hip", "requant.hip", "rht.hip"]
 ARCH = os.environ.get("NVFP4_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

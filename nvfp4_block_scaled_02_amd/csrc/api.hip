@@ -302,6 +302,80 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows
   return status_of(launch_requant_t(a, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------- random Hadamard transform
+// Sign mask of the tensor: bit j set iff the top bit of the counter hash of
+// (sign_seed, j) is set.
+static uint32_t rht_signs(uint64_t sign_seed) {
+  const uint32_t k = sr_key(sign_seed, 0u);
+  uint32_t m = 0;
+  for (uint32_t j = 0; j < 16; ++j)
+    if (fmix32(j ^ k) >> 31) m |= 1u << j;
+  return m;
+}
+
+int nvfp4_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint64_t sign_seed,
+                   float* amax_out, void* stream) {
+  if (!x || !amax_out || !size_ok(rows, cols) || ((uintptr_t)amax_out & 3u)) return NVFP4_ERR_INVALID;
+  if (axis == NVFP4_AXIS_ROW) {
+    if (cols % 16 != 0 || !aligned16(x)) return NVFP4_ERR_INVALID;
+  } else if (axis == NVFP4_AXIS_COL) {
+    if (rows % 16 != 0 || ((uintptr_t)x & 1u)) return NVFP4_ERR_INVALID;
+  } else {
+    return NVFP4_ERR_INVALID;
+  }
+  return status_of(launch_rht_amax(x, rows, cols, axis, rht_signs(sign_seed), amax_out,
+                                   (hipStream_t)stream));
+}
+
+int nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
+                       float global_fp8_max, int scale_fmt, int select, int rounding, int axis,
+                       uint64_t seed, uint64_t sign_seed, uint8_t* codes, uint8_t* scales,
+                       unsigned long long* count4, void* stream) {
+  if (!x || !amax || !codes || !scales || !size_ok(rows, cols)) return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (select < NVFP4_SELECT_6 || select > NVFP4_SELECT_SWEEP) return NVFP4_ERR_INVALID;
+  if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
+  if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (axis == NVFP4_AXIS_ROW) {
+    if (cols % 16 != 0) return NVFP4_ERR_INVALID;
+  } else if (axis == NVFP4_AXIS_COL) {
+    if (rows % 16 != 0 || cols % 8 != 0) return NVFP4_ERR_INVALID;
+  } else {
+    return NVFP4_ERR_INVALID;
+  }
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 3u) || ((uintptr_t)amax & 3u) ||
+      ((uintptr_t)count4 & 7u))
+    return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  QuantizeArgs a;
+  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax;
+  a.sg = resolve_sg(global_fp8_max, scale_fmt, select);
+  a.fmt = scale_fmt; a.select = select; a.rounding = rounding; a.axes = axis; a.seed = seed;
+  a.codes = axis == NVFP4_AXIS_ROW ? codes : nullptr;
+  a.scales = axis == NVFP4_AXIS_ROW ? scales : nullptr;
+  a.codes_t = axis == NVFP4_AXIS_COL ? codes : nullptr;
+  a.scales_t = axis == NVFP4_AXIS_COL ? scales : nullptr;
+  a.count4 = count4;
+  return status_of(launch_quantize_rht(a, rht_signs(sign_seed), (hipStream_t)stream));
+}
+
+int nvfp4_dequantize_rht(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                         const float* amax, float global_fp8_max, int scale_fmt,
+                         uint64_t sign_seed, float* out_f32, void* stream) {
+  if (!codes || !scales || !amax || !out_f32 || !size_ok(rows, cols) || cols % 16 != 0)
+    return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (((uintptr_t)codes & 7u) || !aligned16(out_f32) || ((uintptr_t)amax & 3u))
+    return NVFP4_ERR_INVALID;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  DequantizeArgs a = {};
+  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = amax;
+  a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32;
+  return status_of(launch_dequantize_rht(a, rht_signs(sign_seed), (hipStream_t)stream));
+}
+
 static int fq_common(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre) {
   if (!x || !s_pre || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
   if (!aligned16(x) || ((uintptr_t)s_pre & 3u)) return NVFP4_ERR_INVALID;

@@ -82,6 +82,13 @@ hipError_t launch_quantize_rowscaled(const QuantizeArgs& a, hipStream_t s);
 // 16x16 tile scales (max->6, RNE); a.axes = ROW or ROW | COL
 hipError_t launch_quantize_2d(const QuantizeArgs& a, hipStream_t s);
 hipError_t launch_dequantize(const DequantizeArgs& a, hipStream_t s);
+// every block transformed by the 16-point random Hadamard transform with sign
+// mask `signs` first; a.axes = ROW or COL
+hipError_t launch_quantize_rht(const QuantizeArgs& a, uint32_t signs, hipStream_t s);
+// amax of the transformed tensor (axis ROW or COL), and dequantize + inverse
+hipError_t launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint32_t signs,
+                           float* out, hipStream_t s);
+hipError_t launch_dequantize_rht(const DequantizeArgs& a, uint32_t signs, hipStream_t s);
 hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s);
 hipError_t launch_fakequant_bwd(const FakeQuantArgs& a, hipStream_t s);
 hipError_t launch_requant_t(const RequantArgs& a, hipStream_t s);

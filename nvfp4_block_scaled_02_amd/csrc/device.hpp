@@ -134,7 +134,7 @@ __device__ __forceinline__ void e2m1_unpack8(uint32_t w, float (&q)[8]) {
 
 // ---------------------------------------------------------------- SR
 // MurmurHash3 fmix32 finalizer (A. Appleby, public domain).
-__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+__host__ __device__ inline uint32_t fmix32(uint32_t h) {
   h ^= h >> 16;
   h *= 0x85ebca6bu;
   h ^= h >> 13;

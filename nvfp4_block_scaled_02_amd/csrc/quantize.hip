@@ -97,11 +97,12 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
 // memory rate on the max->6 path.  Codes are stored 8 bytes per lane, scale
 // bytes 1 per lane: whole 512- and 64-byte pieces per wavefront.  Register
 // use is held to 64 so that 8 wavefronts per SIMD stay resident.
-template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
-__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8)))
-quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float* __restrict__ amax,
-                       float sg, uint64_t seed, uint32_t key0, uint2* __restrict__ codes,
-                       uint8_t* __restrict__ scales, unsigned long long* count4) {
+template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK, bool RHT>
+__device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t nblocks,
+                                            const float* __restrict__ amax, float sg, uint64_t seed,
+                                            uint32_t key0, uint2* __restrict__ codes,
+                                            uint8_t* __restrict__ scales,
+                                            unsigned long long* count4, uint32_t rht_signs) {
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint4 stage[BLOCK * 2];
   const TensorScale ts = tensor_scale(*amax, sg);
@@ -120,7 +121,8 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
     bounce_pair(reg, l, a, b);
     const int64_t bk = g * 64 + l;
     const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
-    const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
+    const BlockOut o = quantize_block<FMT, SELECT, ROUND, false, RHT>(reg[2 * l], reg[2 * l + 1],
+                                                                      tab, ts, hb, rht_signs);
     codes[bk] = make_uint2(o.c0, o.c1);
     scales[bk] = (uint8_t)o.scale;
     n4 += o.four;
@@ -133,7 +135,8 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
     bounce_pair(reg, l, a, b);
     const int64_t bk = g * 64 + l;
     const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
-    const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
+    const BlockOut o = quantize_block<FMT, SELECT, ROUND, false, RHT>(reg[2 * l], reg[2 * l + 1],
+                                                                      tab, ts, hb, rht_signs);
     if (bk < nblocks) {
       codes[bk] = make_uint2(o.c0, o.c1);
       scales[bk] = (uint8_t)o.scale;
@@ -141,6 +144,28 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
     }
   }
   if (is_four_six(SELECT) && count4) flush_count<BLOCK>(count4, n4);
+}
+
+template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8)))
+quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float* __restrict__ amax,
+                       float sg, uint64_t seed, uint32_t key0, uint2* __restrict__ codes,
+                       uint8_t* __restrict__ scales, unsigned long long* count4) {
+  blocks_body<FMT, SELECT, ROUND, WIDE, BLOCK, false>(x, nblocks, amax, sg, seed, key0, codes,
+                                                      scales, count4, 0u);
+}
+
+// The same with every block transformed by the 16-point random Hadamard
+// transform first (its butterfly needs more registers than the 64 that eight
+// wavefronts per SIMD allow).
+template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
+__global__ void __launch_bounds__(BLOCK)
+quantize_blocks_rht_kernel(const uint4* __restrict__ x, int64_t nblocks,
+                           const float* __restrict__ amax, float sg, uint64_t seed, uint32_t key0,
+                           uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                           unsigned long long* count4, uint32_t rht_signs) {
+  blocks_body<FMT, SELECT, ROUND, WIDE, BLOCK, true>(x, nblocks, amax, sg, seed, key0, codes,
+                                                     scales, count4, rht_signs);
 }
 
 // ---------------------------------------------------------------- per-row outer scales
@@ -308,14 +333,15 @@ __device__ __forceinline__ float tile_amax(const float* am, int t) {
 // column-wise codes are the transpose of the row-wise ones.  DO_COL = false
 // skips the column-wise pass (row-wise layout only).
 template <int FMT, int SELECT, int ROUND, bool WIDE, bool DO_ROW, bool DO_COL = true,
-          bool TILE2D = false>
+          bool TILE2D = false, bool RHT = false>
 __global__ void __launch_bounds__(kThreads)
 quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                       const float* __restrict__ amax, float sg, uint64_t seed, uint32_t key0,
                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                       uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
-                      unsigned long long* count4, int64_t seg) {
+                      unsigned long long* count4, int64_t seg, uint32_t rht_signs = 0) {
   static_assert(kSW * kTR / 16 == kThreads, "one row block and one column block per lane");
+  static_assert(!(RHT && (DO_ROW || TILE2D)), "the transform applies to column blocks only here");
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kTilePitch];
   __shared__ uint32_t ct[DO_COL ? kSW * kCtPitch : 1];
@@ -388,6 +414,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
           xc[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(
                                       tile + (cb_row + i) * kTilePitch + cb_col * 2) << 16);
         const int64_t c = c0 + cb_col, r = r0 + cb_row;
+        if constexpr (RHT) rht16(xc, rht_signs);
         BlockOut o;
         if constexpr (TILE2D) {
           o = quantize_block_amax<FMT>(xc, tab, ts, tile_amax(am, (cb_row >> 4) * 8 + (cb_col >> 4)));
@@ -480,7 +507,7 @@ static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
   const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
   const int64_t grid = units < target ? units : target;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows, a.cols, a.amax,
-                     a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t, a.count4, seg);
+                     a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t, a.count4, seg, 0u);
   return hipGetLastError();
 }
 
@@ -550,6 +577,61 @@ hipError_t launch_quantize_rowscaled(const QuantizeArgs& a, hipStream_t s) {
   return a.fmt == FMT_E4M3 ? launch_rowscaled_fmt<FMT_E4M3>(a, s) : launch_rowscaled_fmt<FMT_UE5M3>(a, s);
 }
 
+// ---------------------------------------------------------------- transformed blocks
+// Quantization of the tensor with every block transformed by the 16-point
+// random Hadamard transform first: row blocks through the one-lane-per-block
+// stream, column blocks through the strip walker (column-wise only).
+template <int FMT, int SELECT, int ROUND, bool WIDE>
+static hipError_t launch_rht_typed(const QuantizeArgs& a, uint32_t signs, hipStream_t s) {
+  const uint32_t key0 = sr_key(a.seed, 0u);
+  const int cus = device_cu_count();
+  const bool counting = is_four_six(a.select) && a.count4 != nullptr;
+  if (a.axes == AXIS_ROW) {
+    const int64_t nblocks = a.rows * a.cols / 16;
+    const int64_t ngroups = (nblocks + 63) / 64;
+    constexpr int B = kThreads;
+    int64_t grid = (ngroups + B / 64 - 1) / (B / 64);
+    const int64_t cap = counting ? (int64_t)cus * 2 : (int64_t)cus * 8;
+    grid = grid < cap ? grid : cap;
+    hipLaunchKernelGGL((quantize_blocks_rht_kernel<FMT, SELECT, ROUND, WIDE, B>),
+                       dim3((unsigned)grid), dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x),
+                       nblocks, a.amax, a.sg, a.seed, key0, reinterpret_cast<uint2*>(a.codes),
+                       a.scales, a.count4, signs);
+    return hipGetLastError();
+  }
+  constexpr auto kern = quantize_tiles_kernel<FMT, SELECT, ROUND, WIDE, false, true, false, true>;
+  const int64_t tiles_r = (a.rows + kTR - 1) / kTR, tiles_c = (a.cols + kSW - 1) / kSW;
+  const int64_t target = (int64_t)cus * (counting ? 2 : resident_per_cu<kern>());
+  int64_t seg = (tiles_r * tiles_c + target - 1) / target;
+  seg = seg < 1 ? 1 : (seg > tiles_r ? tiles_r : seg);
+  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
+  const int64_t grid = units < target ? units : target;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows, a.cols, a.amax,
+                     a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t, a.count4, seg,
+                     signs);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_rht_fmt(const QuantizeArgs& a, uint32_t signs, hipStream_t s) {
+  if (a.rounding == ROUND_SR) {
+    const bool wide = (uint64_t)a.rows * (uint64_t)a.cols > (1ull << 32);
+    return wide ? launch_rht_typed<FMT, SELECT_6, ROUND_SR, true>(a, signs, s)
+                : launch_rht_typed<FMT, SELECT_6, ROUND_SR, false>(a, signs, s);
+  }
+  switch (a.select) {
+    case SELECT_4OVER6: return launch_rht_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, signs, s);
+    case SELECT_4OVER6_MAE: return launch_rht_typed<FMT, SELECT_4OVER6_MAE, ROUND_RNE, false>(a, signs, s);
+    case SELECT_4OVER6_MAXERR: return launch_rht_typed<FMT, SELECT_4OVER6_MAXERR, ROUND_RNE, false>(a, signs, s);
+    case SELECT_SWEEP: return launch_rht_typed<FMT, SELECT_SWEEP, ROUND_RNE, false>(a, signs, s);
+    default: return launch_rht_typed<FMT, SELECT_6, ROUND_RNE, false>(a, signs, s);
+  }
+}
+
+hipError_t launch_quantize_rht(const QuantizeArgs& a, uint32_t signs, hipStream_t s) {
+  return a.fmt == FMT_E4M3 ? launch_rht_fmt<FMT_E4M3>(a, signs, s) : launch_rht_fmt<FMT_UE5M3>(a, signs, s);
+}
+
 template <int FMT>
 static hipError_t launch_2d_fmt(const QuantizeArgs& a, hipStream_t s) {
   constexpr auto kBoth = quantize_tiles_kernel<FMT, SELECT_6, ROUND_RNE, false, true, true, true>;
@@ -564,7 +646,7 @@ static hipError_t launch_2d_fmt(const QuantizeArgs& a, hipStream_t s) {
   const int64_t grid = units < target ? units : target;
   hipLaunchKernelGGL(both ? kBoth : kRow, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows,
                      a.cols, a.amax, a.sg, a.seed, 0u, a.codes, a.scales, a.codes_t, a.scales_t,
-                     nullptr, seg);
+                     nullptr, seg, 0u);
   return hipGetLastError();
 }
 

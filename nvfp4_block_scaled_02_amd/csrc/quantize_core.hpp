@@ -308,14 +308,53 @@ __device__ __forceinline__ BlockOut quantize_block_x(const float (&x)[16], const
   return o;
 }
 
-// The block as two 16-byte bf16 chunks.
-template <int FMT, int SELECT, int ROUND, bool DIRECT = false>
+// 16-point random Hadamard transform of a block in registers ("Four Over Six"
+// notes, Method: applied to both inputs of the weight-gradient GEMM; "End-to-
+// End 4-Bit Training", Quantized communications: orthogonal, spreads
+// outliers): y = H16 diag(s) x / 4 with s_j = -1 iff bit j of `signs` is set,
+// as x_j * (+-0.25) and then the fast Walsh-Hadamard butterfly, stages
+// h = 1, 2, 4, 8, (t_i, t_{i+h}) -> (t_i + t_{i+h}, t_i - t_{i+h}).
+__device__ __forceinline__ void rht16(float (&t)[16], uint32_t signs) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] *= ((signs >> j) & 1u) ? -0.25f : 0.25f;
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!(i & h)) {
+        const float a = t[i], b = t[i + h];
+        t[i] = a + b;
+        t[i + h] = a - b;
+      }
+}
+
+// The inverse: t_j = y_j * 0.25, the same butterfly, then the signs.
+__device__ __forceinline__ void irht16(float (&t)[16], uint32_t signs) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] *= 0.25f;
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!(i & h)) {
+        const float a = t[i], b = t[i + h];
+        t[i] = a + b;
+        t[i + h] = a - b;
+      }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] = ((signs >> j) & 1u) ? -t[j] : t[j];
+}
+
+// The block as two 16-byte bf16 chunks; RHT: transformed first.
+template <int FMT, int SELECT, int ROUND, bool DIRECT = false, bool RHT = false>
 __device__ __forceinline__ BlockOut quantize_block(uint4 a, uint4 b, const f32x2* tab,
-                                                   const TensorScale& ts, uint32_t hbase) {
-  const float x[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                       bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
-                       bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
-                       bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+                                                   const TensorScale& ts, uint32_t hbase,
+                                                   uint32_t rht_signs = 0) {
+  float x[16] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
+                 bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w),
+                 bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y),
+                 bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w)};
+  if constexpr (RHT) rht16(x, rht_signs);
   return quantize_block_x<FMT, SELECT, ROUND, DIRECT>(x, tab, ts, hbase);
 }
 

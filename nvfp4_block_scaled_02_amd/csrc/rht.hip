@@ -1,0 +1,172 @@
+// rht.hip -- the 16-point random Hadamard transform around NVFP4 quantization
+// on gfx950 ("Four Over Six" notes, Method: applied to both inputs of the
+// weight-gradient GEMM; "End-to-End 4-Bit Training", Quantized
+// communications: an orthogonal rotation that spreads outliers and is
+// inverted exactly): the amax of the transformed tensor (the outer scale of
+// its quantization), and dequantization followed by the inverse transform.
+// The quantization of the transformed tensor itself is in quantize.hip (the
+// transform runs in registers inside the block quantizers).
+#include "quantize_core.hpp"
+
+namespace nvfp4 {
+
+constexpr int kRhtThreads = 1024;
+constexpr int kRhtUnroll = 2;
+
+// Workgroup maximum of m folded into *out (one atomic, skipped when the
+// running maximum already covers it).
+__device__ __forceinline__ void rht_amax_flush(uint32_t m, uint32_t* out) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+    m = m > o ? m : o;
+  }
+  __shared__ uint32_t red[kRhtThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int w = 1; w < kRhtThreads / 64; ++w) r = r > red[w] ? r : red[w];
+    const uint32_t cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (r > cur) atomicMax(out, r);
+  }
+}
+
+// Largest sign-cleared binary32 pattern of a transformed block (NaN beats
+// infinity beats every finite value).
+__device__ __forceinline__ uint32_t block_max_bits(const float (&y)[16]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t b = __float_as_uint(y[i]) & 0x7FFFFFFFu;
+    m = m > b ? m : b;
+  }
+  return m;
+}
+
+// Row blocks: a lane transforms whole blocks (two 16-byte chunks).
+__global__ void __launch_bounds__(kRhtThreads)
+rht_amax_rows_kernel(const uint4* __restrict__ x, int64_t nblocks, uint32_t signs,
+                     uint32_t* __restrict__ out) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kRhtThreads;
+  int64_t i = (int64_t)blockIdx.x * kRhtThreads + threadIdx.x;
+  for (; i + (kRhtUnroll - 1) * stride < nblocks; i += kRhtUnroll * stride) {
+    uint4 a[kRhtUnroll], b[kRhtUnroll];
+#pragma unroll
+    for (int u = 0; u < kRhtUnroll; ++u) {
+      a[u] = ld_nt(x + 2 * (i + u * stride));
+      b[u] = ld_nt(x + 2 * (i + u * stride) + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < kRhtUnroll; ++u) {
+      float y[16];
+      unpack16(a[u], b[u], y);
+      rht16(y, signs);
+      const uint32_t v = block_max_bits(y);
+      m = m > v ? m : v;
+    }
+  }
+  for (; i < nblocks; i += stride) {
+    float y[16];
+    unpack16(ld_nt(x + 2 * i), ld_nt(x + 2 * i + 1), y);
+    rht16(y, signs);
+    const uint32_t v = block_max_bits(y);
+    m = m > v ? m : v;
+  }
+  rht_amax_flush(m, out);
+}
+
+// Column blocks: a lane transforms the 16 values of one column in one group
+// of 16 rows (each of its loads is one bf16; the wavefront's lanes take
+// consecutive columns, so every load instruction reads 128 contiguous bytes).
+__global__ void __launch_bounds__(kRhtThreads)
+rht_amax_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t signs,
+                     uint32_t* __restrict__ out) {
+  uint32_t m = 0;
+  const int64_t items = (rows / 16) * cols;
+  const bool narrow = (items >> 32) == 0;
+  const int64_t stride = (int64_t)gridDim.x * kRhtThreads;
+  for (int64_t w = (int64_t)blockIdx.x * kRhtThreads + threadIdx.x; w < items; w += stride) {
+    const int64_t g = narrow ? (int64_t)((uint32_t)w / (uint32_t)cols) : w / cols;
+    const int64_t c = w - g * cols;
+    const uint16_t* p = x + g * 16 * cols + c;
+    float y[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) y[r] = __uint_as_float((uint32_t)p[r * cols] << 16);
+    rht16(y, signs);
+    const uint32_t v = block_max_bits(y);
+    m = m > v ? m : v;
+  }
+  rht_amax_flush(m, out);
+}
+
+__global__ void __launch_bounds__(64) rht_amax_init_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[0] = 0u;
+}
+
+hipError_t launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint32_t signs,
+                           float* out, hipStream_t s) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(rht_amax_init_kernel, dim3(1), dim3(64), 0, s, o);
+  const int64_t items = axis == AXIS_ROW ? rows * cols / 16 : (rows / 16) * cols;
+  if (items == 0) return hipGetLastError();
+  int64_t grid = (items + kRhtThreads - 1) / kRhtThreads;
+  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (one atomic) per CU
+  grid = grid < cap ? grid : cap;
+  if (axis == AXIS_ROW)
+    hipLaunchKernelGGL(rht_amax_rows_kernel, dim3((unsigned)grid), dim3(kRhtThreads), 0, s,
+                       reinterpret_cast<const uint4*>(x), items, signs, o);
+  else
+    hipLaunchKernelGGL(rht_amax_cols_kernel, dim3((unsigned)grid), dim3(kRhtThreads), 0, s, x, rows,
+                       cols, signs, o);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- dequantize + inverse
+// A lane per block: x_hat = (q * D) * alpha (as the dequantize kernel), the
+// inverse transform in registers, 64 contiguous bytes out.
+template <int FMT>
+__global__ void __launch_bounds__(kThreads)
+dequantize_rht_kernel(const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
+                      int64_t nblocks, const float* __restrict__ amax, float sg, uint32_t signs,
+                      float4* __restrict__ out) {
+  const float alpha = outer_alpha(*amax, sg);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nblocks; i += stride) {
+    const uint2 w = ld_nt(codes + i);
+    const float D = decode_scale(FMT, scales[i]);
+    float q[16], v[16];
+    float qa[8], qb[8];
+    e2m1_unpack8(w.x, qa);
+    e2m1_unpack8(w.y, qb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      q[e] = qa[e];
+      q[8 + e] = qb[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = (q[e] * D) * alpha;
+    irht16(v, signs);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      st_nt(make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]), out + 4 * i + k);
+  }
+}
+
+hipError_t launch_dequantize_rht(const DequantizeArgs& a, uint32_t signs, hipStream_t s) {
+  const int64_t nblocks = a.rows * a.cols / 16;
+  int64_t grid = (nblocks + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  grid = grid < cap ? grid : cap;
+  if (a.fmt == FMT_UE5M3)
+    hipLaunchKernelGGL(dequantize_rht_kernel<FMT_UE5M3>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       reinterpret_cast<const uint2*>(a.codes), a.scales, nblocks, a.amax, a.sg,
+                       signs, reinterpret_cast<float4*>(a.out_f32));
+  else
+    hipLaunchKernelGGL(dequantize_rht_kernel<FMT_E4M3>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       reinterpret_cast<const uint2*>(a.codes), a.scales, nblocks, a.amax, a.sg,
+                       signs, reinterpret_cast<float4*>(a.out_f32));
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -27,7 +27,7 @@ def _declared():
 
 def test_library_loads_and_version():
     lib = N.lib()
-    assert lib.nvfp4_abi_version() == 4
+    assert lib.nvfp4_abi_version() == 5
 
 
 def test_every_declared_symbol_is_exported_and_bound():

@@ -547,6 +547,57 @@ def run_select(args, torch, np, nv, synth, dev, timer):
     return line
 
 
+def run_rht(args, torch, np, nv, synth, dev, timer):
+    """The random Hadamard transform around quantization on the 8192x4096
+    activation: transformed amax and quantization of column blocks (the
+    weight-gradient operand, the step) and of row blocks, and the
+    dequantize + inverse transform of the row-wise result."""
+    nsets = 8
+    xb = synth.make("activation")["x"]
+    rows, cols = xb.shape
+    n = rows * cols
+    x0 = to_dev(torch, np, xb, dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    ac = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    ar = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    oc = [{"codes": torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev),
+           "scales": torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev)} for _ in range(nsets)]
+    orow = [{"codes": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+             "scales": torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)} for _ in range(nsets)]
+    xh = [torch.empty((rows, cols), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    for i in range(nsets):
+        nv.rht_amax(xs[i], axis="col", sign_seed=5, out=ac[i])
+        nv.rht_amax(xs[i], axis="row", sign_seed=5, out=ar[i])
+        nv.quantize_rht(xs[i], ar[i], axis="row", sign_seed=5, out=orow[i])
+    gm = nv.default_global_max("e4m3", "4over6")
+    reps = max(args.steps, 40)
+    us = {
+        "rht_amax_col": timer.avg_us(lambda i: nv.rht_amax(xs[i % nsets], axis="col", sign_seed=5,
+                                                           out=ac[i % nsets]), reps, nsets),
+        "quantize_rht_col_4over6": timer.avg_us(lambda i: nv.quantize_rht(
+            xs[i % nsets], ac[i % nsets], axis="col", sign_seed=5, out=oc[i % nsets]), reps, nsets),
+        "rht_amax_row": timer.avg_us(lambda i: nv.rht_amax(xs[i % nsets], axis="row", sign_seed=5,
+                                                           out=ar[i % nsets]), reps, nsets),
+        "quantize_rht_row_4over6": timer.avg_us(lambda i: nv.quantize_rht(
+            xs[i % nsets], ar[i % nsets], axis="row", sign_seed=5, out=orow[i % nsets]), reps, nsets),
+        "dequantize_rht_f32": timer.avg_us(lambda i: nv.dequantize_rht(
+            orow[i % nsets]["codes"], orow[i % nsets]["scales"], ar[i % nsets], global_max=gm,
+            sign_seed=5, out=xh[i % nsets]), reps, nsets),
+    }
+    bpe = {"rht_amax_col": B_AMAX, "quantize_rht_col_4over6": B_QUANT, "rht_amax_row": B_AMAX,
+           "quantize_rht_row_4over6": B_QUANT, "dequantize_rht_f32": B_DEQ}
+    kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
+    ms_step = (us["rht_amax_col"] + us["quantize_rht_col_4over6"]) / 1e3
+    line = base_line("NVFP4 RHT + column-wise 4/6 quantize step GB/s at 8192x4096 bf16",
+                     n * (B_AMAX + B_QUANT) / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
+                     "activation 8192x4096 bf16 (seed 2): 16-point random Hadamard transform of "
+                     "column blocks (sign seed 5) -> transformed amax -> column-wise Four-Over-Six "
+                     "quantize (E4M3, FP8 max 256)",
+                     {"rows": rows, "cols": cols, "elements": n,
+                      "timing": "sum of per-kernel event averages"}, n)
+    return finish(line, kernels, args)
+
+
 def run_gradient(args, torch, np, nv, synth, dev, timer):
     log("generating the 16384x8192 gradient")
     xb = synth.make("gradient")["x"]
@@ -604,7 +655,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="activation",
                     choices=["activation", "weight-1k", "weight", "qat", "gradient",
-                             "activation-pertoken", "weight-2d", "requant", "select"])
+                             "activation-pertoken", "weight-2d", "requant", "select", "rht"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 256 MiB copy and each kernel of the workload twice (for PMC counters)")
@@ -638,6 +689,8 @@ def main():
         line = run_requant(args, torch, np, nv, synth, dev, timer)
     elif args.workload == "select":
         line = run_select(args, torch, np, nv, synth, dev, timer)
+    elif args.workload == "rht":
+        line = run_rht(args, torch, np, nv, synth, dev, timer)
     else:
         line = run_gradient(args, torch, np, nv, synth, dev, timer)
     if line is not None:

@@ -288,8 +288,12 @@ quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_b
 // MI355X; 4-byte pieces per tile, as an unstaged 64-row tile would write for
 // its scales, run at a fraction of the write bandwidth.
 // Loads the lane's chunks of the tile at rows r0.., strip c0.. (chunk
-// k = u * kThreads + lane: tile row k / 16, columns (k % 16) * 8 ..+8);
-// chunks outside the tensor read as zeros.
+// k = u * kThreads + lane: tile row k / 16, columns (k % 16) * 8 ..+8).  The
+// loads are unconditional, with addresses clamped into the tensor (cols % 8
+// == 0, so a chunk is whole or absent); chunks outside the tensor are zeroed
+// where they are used (tile_chunk).  The number of loads in flight is then
+// the same on every path, so waiting for the oldest tile never waits for the
+// newer ones.
 constexpr int kLoads = kSW * kTR / kChunk / kThreads;  // 2
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t rows,
                                           int64_t cols, int64_t r0, int64_t c0,
@@ -297,10 +301,18 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {
     const int k = u * kThreads + threadIdx.x;
-    const int64_t r = r0 + (k >> 4), c = c0 + (k & 15) * 8;
-    w[u] = (r < rows && c < cols) ? ld_nt(reinterpret_cast<const uint4*>(x + r * cols + c))
-                                  : make_uint4(0, 0, 0, 0);
+    int64_t r = r0 + (k >> 4), c = c0 + (k & 15) * 8;
+    r = r < rows ? r : rows - 1;
+    c = c < cols ? c : cols - 8;
+    w[u] = ld_nt(reinterpret_cast<const uint4*>(x + r * cols + c));
   }
+}
+
+__device__ __forceinline__ uint4 tile_chunk(const uint4 (&w)[kLoads], int u, int64_t rows,
+                                            int64_t cols, int64_t r0, int64_t c0) {
+  const int k = u * kThreads + threadIdx.x;
+  const bool ok = r0 + (k >> 4) < rows && c0 + (k & 15) * 8 < cols;
+  return ok ? w[u] : make_uint4(0, 0, 0, 0);
 }
 
 // Amax of 16x16 tile t from its 16 row-block values in LDS (NaN-propagating).
@@ -365,26 +377,27 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
     const int64_t tr0 = g * seg;
     const int64_t tr1 = tr0 + seg < tiles_r ? tr0 + seg : tiles_r;
     int64_t ct_lo = tr0, st_lo = tr0;  // first tile of the open stages
-    // the next tile's chunks are requested before the current one is processed
-    uint4 w[kLoads];
-    load_tile(x, rows, cols, tr0 * kTR, c0, w);
-    for (int64_t tr = tr0; tr < tr1; ++tr) {
+    // Two tiles are in flight ahead of the one being processed.  The three
+    // load buffers rotate by name (the walk is unrolled by three): copying a
+    // buffer whose loads are outstanding would make the copy wait for them.
+    // Past the end of the walk the last tile is requested again (unused).
+    auto step = [&](const uint4 (&w)[kLoads], uint4 (&ahead)[kLoads], int64_t tr) {
       const int64_t r0 = tr * kTR;
-      uint4 wn[kLoads];
-      if (tr + 1 < tr1) load_tile(x, rows, cols, r0 + kTR, c0, wn);
+      load_tile(x, rows, cols, (tr + 2 < tr1 ? tr + 2 : tr1 - 1) * kTR, c0, ahead);
       // ---- into LDS, row-major
 #pragma unroll
       for (int u = 0; u < kLoads; ++u) {
         const int k = u * kThreads + lane;
-        *reinterpret_cast<uint4*>(tile + (k >> 4) * kTilePitch + (k & 15) * 16) = w[u];
+        *reinterpret_cast<uint4*>(tile + (k >> 4) * kTilePitch + (k & 15) * 16) =
+            tile_chunk(w, u, rows, cols, r0, c0);
       }
-      __syncthreads();
+      lds_sync();
       if constexpr (TILE2D) {
         float xr[16];
         unpack16(*reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2),
                  *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2 + 16), xr);
         am[((rb_row >> 4) * 8 + (rb_col >> 4)) * 16 + (rb_row & 15)] = block_absmax(xr);
-        __syncthreads();
+        lds_sync();
       }
       // ---- row-wise block
       if constexpr (DO_ROW) {
@@ -428,7 +441,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
         st[cb_col * kStPitch + (int)(tr % kStTiles) * (kTR / 16) + (cb_row >> 4)] = (uint8_t)o.scale;
         if (r < rows && c < cols) n4 += o.four;
       }
-      __syncthreads();  // staged outputs complete; the tile may be rewritten
+      lds_sync();  // staged outputs complete; the tile may be rewritten
       // ---- flush closed stages
       if constexpr (DO_COL) {
         const bool last = tr + 1 == tr1;
@@ -441,12 +454,18 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
           st_lo = tr + 1;
         }
       }
-      // (the next tile writes the staging buffers only after its first barrier)
-      if (tr + 1 < tr1) {
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) w[u] = wn[u];
-      }
+    };
+    uint4 A[kLoads], B[kLoads], C[kLoads];
+    load_tile(x, rows, cols, tr0 * kTR, c0, A);
+    load_tile(x, rows, cols, (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0, B);
+    int64_t tr = tr0;
+    for (; tr + 3 <= tr1; tr += 3) {
+      step(A, C, tr);
+      step(B, A, tr + 1);
+      step(C, B, tr + 2);
     }
+    if (tr < tr1) step(A, C, tr);
+    if (tr + 1 < tr1) step(B, A, tr + 1);
   }
   if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
 }

@@ -40,7 +40,7 @@ TRAFFIC_FILE = os.path.join(PROFILE_DIR, "activation_8192x4096_traffic.json")
 # sources each activation-step kernel is built from (a change voids its PMC bytes)
 KERNEL_SOURCES = {
     "tensor_amax": ["amax.hip", "device.hpp", "common.hpp"],
-    "quantize_4over6": ["quantize.hip", "device.hpp", "common.hpp"],
+    "quantize_4over6": ["quantize.hip", "quantize_core.hpp", "device.hpp", "common.hpp"],
     "dequantize_f32_mse": ["dequantize.hip", "device.hpp", "common.hpp"],
 }
 METRIC = "NVFP4 4/6 quantize GB/s (Gelem/s) at 8192x4096 bf16; % of HBM peak"

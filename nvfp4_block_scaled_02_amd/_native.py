@@ -9,6 +9,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+ABI_VERSION = 5  # NVFP4_ABI_VERSION of include/nvfp4.h that these signatures follow
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 SCALE_E4M3, SCALE_UE5M3 = 0, 1
@@ -79,6 +80,10 @@ def lib():
         f = getattr(l, name)
         f.restype = res
         f.argtypes = args
+    if l.nvfp4_abi_version() != ABI_VERSION:
+        raise NativeError(
+            f"{LIB_PATH} has ABI version {l.nvfp4_abi_version()}, the binding expects "
+            f"{ABI_VERSION}; rebuild with `python -m nvfp4_block_scaled_02_amd.build`.")
     _lib = l
     return l
 

@@ -26,8 +26,10 @@ def _declared():
 
 
 def test_library_loads_and_version():
+    """The library, the binding and the header agree on the ABI version."""
     lib = N.lib()
-    assert lib.nvfp4_abi_version() == 5
+    hdr = int(re.search(r"#define NVFP4_ABI_VERSION (\d+)", open(HEADERS[0]).read()).group(1))
+    assert lib.nvfp4_abi_version() == N.ABI_VERSION == hdr
 
 
 def test_every_declared_symbol_is_exported_and_bound():

@@ -354,6 +354,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
                       unsigned long long* count4, int64_t seg, uint32_t rht_signs = 0) {
   static_assert(kSW * kTR / 16 == kThreads, "one row block and one column block per lane");
   static_assert(!(RHT && (DO_ROW || TILE2D)), "the transform applies to column blocks only here");
+  constexpr int kAhead = DO_ROW ? 2 : 1;
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kTilePitch];
   __shared__ uint32_t ct[DO_COL ? kSW * kCtPitch : 1];
@@ -377,13 +378,16 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
     const int64_t tr0 = g * seg;
     const int64_t tr1 = tr0 + seg < tiles_r ? tr0 + seg : tiles_r;
     int64_t ct_lo = tr0, st_lo = tr0;  // first tile of the open stages
-    // Two tiles are in flight ahead of the one being processed.  The three
-    // load buffers rotate by name (the walk is unrolled by three): copying a
-    // buffer whose loads are outstanding would make the copy wait for them.
-    // Past the end of the walk the last tile is requested again (unused).
+    // kAhead tiles are in flight ahead of the one being processed: two for
+    // the fused walk, one for the column-only walk (whose registers then fit
+    // five wavefronts per SIMD instead of four, measured 3.5% faster).  The
+    // load buffers rotate by name (the walk is unrolled by kAhead + 1):
+    // copying a buffer whose loads are outstanding would make the copy wait
+    // for them.  Past the end of the walk the last tile is requested again
+    // (unused).
     auto step = [&](const uint4 (&w)[kLoads], uint4 (&ahead)[kLoads], int64_t tr) {
       const int64_t r0 = tr * kTR;
-      load_tile(x, rows, cols, (tr + 2 < tr1 ? tr + 2 : tr1 - 1) * kTR, c0, ahead);
+      load_tile(x, rows, cols, (tr + kAhead < tr1 ? tr + kAhead : tr1 - 1) * kTR, c0, ahead);
       // ---- into LDS, row-major
 #pragma unroll
       for (int u = 0; u < kLoads; ++u) {
@@ -457,15 +461,23 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
     };
     uint4 A[kLoads], B[kLoads], C[kLoads];
     load_tile(x, rows, cols, tr0 * kTR, c0, A);
-    load_tile(x, rows, cols, (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0, B);
     int64_t tr = tr0;
-    for (; tr + 3 <= tr1; tr += 3) {
-      step(A, C, tr);
-      step(B, A, tr + 1);
-      step(C, B, tr + 2);
+    if constexpr (kAhead == 2) {
+      load_tile(x, rows, cols, (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0, B);
+      for (; tr + 3 <= tr1; tr += 3) {
+        step(A, C, tr);
+        step(B, A, tr + 1);
+        step(C, B, tr + 2);
+      }
+      if (tr < tr1) step(A, C, tr);
+      if (tr + 1 < tr1) step(B, A, tr + 1);
+    } else {
+      for (; tr + 2 <= tr1; tr += 2) {
+        step(A, B, tr);
+        step(B, A, tr + 1);
+      }
+      if (tr < tr1) step(A, B, tr);
     }
-    if (tr < tr1) step(A, C, tr);
-    if (tr + 1 < tr1) step(B, A, tr + 1);
   }
   if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
 }

@@ -98,7 +98,11 @@ constexpr int kRqPitch = kSW * 4;  // binary32 tile row pitch (bytes)
 __host__ __device__ constexpr int rq_col_off(int c) {
   return (c >> 4) * 64 + 16 * (((c >> 2) & 3) ^ ((c >> 5) & 3)) + 4 * (c & 3);
 }
-constexpr int kMxStTiles = 32;          // MXFP8 scales: 32 tiles of 64 rows = 64 bytes
+// MXFP8 scale bytes are staged for 8 tiles of 64 rows (16 bytes per column).
+// Staging them for 32 tiles (64-byte pieces) took 8.7 KiB of LDS, which held
+// the walk to 3 workgroups per CU; at 16 bytes 4 fit (33.5 -> 28.7 us at
+// 8192x4096, outputs identical), and the scale bytes are 1/32 of the output.
+constexpr int kMxStTiles = 8;
 constexpr int kMxStBytes = kMxStTiles * 2;
 constexpr int kMxStPitch = kMxStBytes + 4;
 

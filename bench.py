@@ -662,8 +662,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by rows with no exchange besides an amax all-reduce; "
-              "see the sharding note in the design document).", file=sys.stderr)
+              "(the path shards by rows, with an all-reduce of the outer amax as its "
+              "only exchange).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

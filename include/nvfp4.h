@@ -57,7 +57,7 @@ extern "C" {
 enum {
   NVFP4_OK = 0,
   NVFP4_ERR_INVALID = 1,     /* bad argument; nothing launched */
-  NVFP4_ERR_UNSUPPORTED = 2, /* valid request this build does not serve */
+  NVFP4_ERR_UNSUPPORTED = 2, /* valid request the library does not serve */
   NVFP4_ERR_HIP = 3          /* a HIP launch reported an error */
 };
 

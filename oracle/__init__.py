@@ -101,10 +101,12 @@ def _load():
     lib.or_requant_nvfp4_t.restype = ctypes.c_int
     lib.or_requant_nvfp4_t.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, _f32p,
                                        ctypes.c_float, ctypes.c_int, ctypes.c_float,
-                                       ctypes.c_float, ctypes.c_int, ctypes.c_uint64, _u8p, _u8p]
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_uint64, _i64, _u8p,
+                                       _u8p]
     lib.or_requant_mxfp8_t.restype = ctypes.c_int
     lib.or_requant_mxfp8_t.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, _f32p,
-                                       ctypes.c_float, ctypes.c_int, ctypes.c_uint64, _u8p, _u8p]
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_uint64, _i64, _u8p,
+                                       _u8p]
     lib.or_e4m3_code_sr.restype = ctypes.c_int
     lib.or_e4m3_code_sr.argtypes = [ctypes.c_float, ctypes.c_uint32]
     lib.or_mxfp8_quantize_sr.restype = ctypes.c_int
@@ -122,7 +124,7 @@ def _load():
     lib.or_quantize_rht.restype = ctypes.c_int
     lib.or_quantize_rht.argtypes = [_f32p, _i64, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
-                                    ctypes.c_int, _u8p, _u8p, _u64p]
+                                    ctypes.c_int, _i64, _u8p, _u8p, _u64p]
     lib.or_dequantize_rht.restype = ctypes.c_int
     lib.or_dequantize_rht.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                       ctypes.c_int, ctypes.c_uint64, _f32p]
@@ -430,11 +432,13 @@ def dequantized_amax(codes, scales, *, amax=None, row_amaxes=None, fmt=FMT_E4M3,
 
 def requant_t(codes, scales, *, amax=None, row_amaxes=None, fmt=FMT_E4M3, select=SELECT_4OVER6,
               global_max=None, target="nvfp4", dst_amax=None, dst_fmt=FMT_E4M3,
-              dst_global_max=None, seed=0):
+              dst_global_max=None, seed=0, col0=0):
     """Dequantize an NVFP4 tensor, transpose, re-quantize with stochastic
     rounding.  target "nvfp4": returns (codes_t [cols, rows/2], scales_t
     [cols, rows/16]) under outer amax dst_amax; "mxfp8": returns (elems_t
-    [cols, rows] E4M3 bytes, scales_t [cols, rows/32] E8M0 bytes)."""
+    [cols, rows] E4M3 bytes, scales_t [cols, rows/32] E8M0 bytes).  col0:
+    the source is the strip of columns col0.. of a wider tensor (SR indices
+    of the wider output)."""
     codes, scales, rows, cols, a, ra, sg, fmt = _source(codes, scales, amax, row_amaxes, fmt,
                                                          select, global_max)
     lib = _load()
@@ -445,12 +449,12 @@ def requant_t(codes, scales, *, amax=None, row_amaxes=None, fmt=FMT_E4M3, select
         st_ = np.empty((cols, rows // 16), np.uint8)
         st = lib.or_requant_nvfp4_t(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, a,
                                     _ptr(ra, _f32p), sg, fmt, float(dst_amax), dsg, dfmt,
-                                    int(seed), _ptr(ct, _u8p), _ptr(st_, _u8p))
+                                    int(seed), int(col0), _ptr(ct, _u8p), _ptr(st_, _u8p))
     elif target == "mxfp8":
         ct = np.empty((cols, rows), np.uint8)
         st_ = np.empty((cols, rows // 32), np.uint8)
         st = lib.or_requant_mxfp8_t(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, a,
-                                    _ptr(ra, _f32p), sg, fmt, int(seed), _ptr(ct, _u8p),
+                                    _ptr(ra, _f32p), sg, fmt, int(seed), int(col0), _ptr(ct, _u8p),
                                     _ptr(st_, _u8p))
     else:
         raise ValueError(f"unknown target {target!r}")
@@ -512,10 +516,12 @@ def rht_amax(x, *, axis=AXIS_ROW, sign_seed=0):
 
 
 def quantize_rht(x, amax, *, axis=AXIS_ROW, sign_seed=0, fmt=FMT_E4M3, select=SELECT_4OVER6,
-                 rounding=ROUND_RNE, seed=0, global_max=None):
+                 rounding=ROUND_RNE, seed=0, global_max=None, out_row0=0):
     """Quantization of the block-wise transformed tensor.  axis ROW: row-wise
-    layout; COL: the column-wise layout (of the transpose).  Returns (codes,
-    scales, count4)."""
+    layout; COL: the column-wise layout (of the transpose).  out_row0: the
+    first output row's position in a larger output (x a strip of a larger
+    tensor: its first row for ROW, its first column for COL), for the SR
+    indices.  Returns (codes, scales, count4)."""
     xf = as_f32(x)
     rows, cols = xf.shape
     fmt = _fmt(fmt)
@@ -525,7 +531,7 @@ def quantize_rht(x, amax, *, axis=AXIS_ROW, sign_seed=0, fmt=FMT_E4M3, select=SE
     scales = np.empty((R, C // 16), np.uint8)
     cnt = np.zeros(1, np.uint64)
     st = _load().or_quantize_rht(_ptr(xf, _f32p), rows, cols, float(amax), sg, fmt, int(select),
-                                 int(rounding), int(seed), int(sign_seed), int(axis),
+                                 int(rounding), int(seed), int(sign_seed), int(axis), int(out_row0),
                                  _ptr(codes, _u8p), _ptr(scales, _u8p), _ptr(cnt, _u64p))
     if st != 0:
         raise ValueError(f"oracle quantize_rht rejected the arguments (status {st})")

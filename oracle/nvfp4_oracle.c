@@ -583,19 +583,21 @@ float or_dequantized_amax(const uint8_t *codes, const uint8_t *scales, int64_t r
 
 /* NVFP4 target: X_hat^T [cols, rows] quantized row-wise (blocks of 16 source
  * rows of one column) with max->6 and SR, outer amax dst_amax with S_g =
- * dst_sg; SR index = the element's index in X_hat^T (c * rows + r).
- * rows % 16 == 0.  codes_t[cols, rows/2], scales_t[cols, rows/16]. */
+ * dst_sg; SR index = the element's index in X_hat^T ((out_row0 + c) * rows +
+ * r; out_row0 > 0 when the source is a strip of columns out_row0.. of a
+ * wider tensor).  rows % 16 == 0.  codes_t[cols, rows/2], scales_t[cols,
+ * rows/16]. */
 int or_requant_nvfp4_t(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
                        float amax, const float *row_amax, float sg, int fmt, float dst_amax,
-                       float dst_sg, int dst_fmt, uint64_t seed, uint8_t *codes_t,
-                       uint8_t *scales_t) {
+                       float dst_sg, int dst_fmt, uint64_t seed, int64_t out_row0,
+                       uint8_t *codes_t, uint8_t *scales_t) {
   if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return OR_EINVAL;
   float *x = dequant_source(codes, scales, rows, cols, amax, row_amax, sg, fmt);
   if (!x) return OR_EINVAL;
   float *t = transpose_f32(x, rows, cols);
   free(x);
-  int st = or_quantize(t, cols, rows, 0, dst_amax, dst_sg, dst_fmt, OR_SELECT_6, OR_ROUND_SR, seed,
-                       codes_t, scales_t, NULL, NULL, NULL);
+  int st = or_quantize(t, cols, rows, out_row0, dst_amax, dst_sg, dst_fmt, OR_SELECT_6, OR_ROUND_SR,
+                       seed, codes_t, scales_t, NULL, NULL, NULL);
   free(t);
   return st;
 }
@@ -695,17 +697,18 @@ int or_mxfp8_dequantize(const uint8_t *elems, const uint8_t *scales, int64_t row
 }
 
 /* MXFP8 target: X_hat^T [cols, rows] quantized to MXFP8 with SR along its
- * rows (blocks of 32 source rows of one column); rows % 32 == 0.
- * elems_t[cols, rows] (E4M3 bytes), scales_t[cols, rows/32] (E8M0). */
+ * rows (blocks of 32 source rows of one column); rows % 32 == 0; SR indices
+ * as for the NVFP4 target (out_row0 as there).  elems_t[cols, rows] (E4M3
+ * bytes), scales_t[cols, rows/32] (E8M0). */
 int or_requant_mxfp8_t(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
                        float amax, const float *row_amax, float sg, int fmt, uint64_t seed,
-                       uint8_t *elems_t, uint8_t *scales_t) {
+                       int64_t out_row0, uint8_t *elems_t, uint8_t *scales_t) {
   if (rows < 0 || cols < 0 || rows % 32 != 0 || cols % 16 != 0) return OR_EINVAL;
   float *x = dequant_source(codes, scales, rows, cols, amax, row_amax, sg, fmt);
   if (!x) return OR_EINVAL;
   float *t = transpose_f32(x, rows, cols);
   free(x);
-  int st = or_mxfp8_quantize_sr(t, cols, rows, 0, seed, elems_t, scales_t);
+  int st = or_mxfp8_quantize_sr(t, cols, rows, out_row0, seed, elems_t, scales_t);
   free(t);
   return st;
 }
@@ -938,21 +941,22 @@ float or_rht_amax(const float *x, int64_t rows, int64_t cols, int axis, uint64_t
 /* Quantization of the transformed tensor: axis 1 = row-wise (codes[rows,
  * cols/2], scales[rows, cols/16]), axis 2 = column-wise (the layout of the
  * transposed tensor, codes[cols, rows/2], scales[cols, rows/16]); every other
- * argument as or_quantize (SR indices in the output orientation). */
+ * argument as or_quantize (SR indices in the output orientation, whose first
+ * row is out_row0 of a larger output when x is a strip of a larger tensor). */
 int or_quantize_rht(const float *x, int64_t rows, int64_t cols, float amax, float sg, int fmt,
                     int select, int rounding, uint64_t seed, uint64_t sign_seed, int axis,
-                    uint8_t *codes, uint8_t *scales, uint64_t *count4) {
+                    int64_t out_row0, uint8_t *codes, uint8_t *scales, uint64_t *count4) {
   if (rows < 0 || cols < 0 || (axis != 1 && axis != 2)) return OR_EINVAL;
   if ((axis == 1 && cols % 16) || (axis == 2 && rows % 16)) return OR_EINVAL;
   float *y = rht_tensor(x, rows, cols, axis, or_rht_signs(sign_seed));
   int st;
   if (axis == 1) {
-    st = or_quantize(y, rows, cols, 0, amax, sg, fmt, select, rounding, seed, codes, scales, count4,
-                     NULL, NULL);
+    st = or_quantize(y, rows, cols, out_row0, amax, sg, fmt, select, rounding, seed, codes, scales,
+                     count4, NULL, NULL);
   } else {
     float *t = transpose_f32(y, rows, cols);
-    st = or_quantize(t, cols, rows, 0, amax, sg, fmt, select, rounding, seed, codes, scales, count4,
-                     NULL, NULL);
+    st = or_quantize(t, cols, rows, out_row0, amax, sg, fmt, select, rounding, seed, codes, scales,
+                     count4, NULL, NULL);
     free(t);
   }
   free(y);

@@ -12,7 +12,8 @@ past 2^32, and the last 128-column strip holds only 16 columns.
 
 The tensor amax is pinned by a planted maximum and a planted NaN past index
 2^32 (the property that holds at any size); the quantizers take a given
-(stale) outer amax, so no oracle input comes from the GPU.
+(stale) outer amax, so no oracle input comes from the GPU.  The
+re-quantization takes a seeded random NVFP4 source of the same shape.
 
 Bar: codes and scale bytes bit-exact; dequantized values bit-exact."""
 import numpy as np
@@ -153,3 +154,67 @@ def test_rowscaled_sr_past_2_32(big):
         _same(q.codes[r:r + 1].cpu().numpy(), rc, f"codes, row {r}")
     del q
     log("row-scaled SR past 2^32: ok")
+
+
+def _rand_u8(shape, lo, hi, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randint(lo, hi, shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+
+
+@pytest.mark.parametrize("target", ["mxfp8", "nvfp4"])
+def test_requant_past_2_32(target):
+    """Dequantize -> transpose -> SR re-quantize of a 65536x65552 NVFP4
+    tensor (seeded random codes and finite E4M3 scale bytes, given outer
+    amaxes): the oracle recomputes 16-column source strips, including the
+    last (output rows whose indices pass 2^32), with their output offset."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if torch.cuda.mem_get_info()[0] < 24 * 2 ** 30:
+        pytest.skip("needs 24 GiB of free device memory")
+    log(f"requant {target} 65536x65552")
+    codes = _rand_u8((ROWS, COLS // 2), 0, 256, 31)
+    scales = _rand_u8((ROWS, COLS // 16), 0x20, 0x60, 32)
+    amax = torch.tensor([100.0], dtype=torch.float32, device="cuda")
+    gm = O.default_global_max(O.FMT_E4M3, O.SELECT_4OVER6)
+    kw = {"dst_amax": torch.tensor([20.0], dtype=torch.float32, device="cuda")} if target == "nvfp4" else {}
+    out, out_s = nv.requantize_t(codes, scales, amax=amax, global_max=gm, target=target, seed=4242, **kw)
+    torch.cuda.synchronize()
+    for c0 in SAMPLE_COL0:
+        cs = np.ascontiguousarray(codes[:, c0 // 2:c0 // 2 + 8].cpu().numpy())
+        ss = np.ascontiguousarray(scales[:, c0 // 16:c0 // 16 + 1].cpu().numpy())
+        okw = {"dst_amax": 20.0} if target == "nvfp4" else {}
+        ro, rs = O.requant_t(cs, ss, amax=100.0, global_max=gm, target=target, seed=4242, col0=c0,
+                             **okw)
+        _same(out_s[c0:c0 + 16].cpu().numpy(), rs, f"{target} scales_t, strip {c0}")
+        _same(out[c0:c0 + 16].cpu().numpy(), ro, f"{target} out_t, strip {c0}")
+    del out, out_s, codes, scales
+    torch.cuda.empty_cache()
+    log(f"requant {target} past 2^32: ok")
+
+
+def test_rht_sr_past_2_32(big):
+    """The random Hadamard transform before SR quantization (UE5M3, max->6),
+    column blocks (the weight-gradient operand) and row blocks."""
+    x = big
+    amax = torch.tensor([A_STALE], dtype=torch.float32, device="cuda")
+    kw = dict(sign_seed=17, fmt="ue5m3", select="6", rounding="sr", seed=777)
+    okw = dict(sign_seed=17, fmt=O.FMT_UE5M3, select=O.SELECT_6, rounding=O.ROUND_SR, seed=777)
+    log("RHT column SR 65536x65552")
+    q = nv.quantize_rht(x, amax, axis="col", **kw)
+    torch.cuda.synchronize()
+    for c0 in SAMPLE_COL0:
+        rc, rs, _ = O.quantize_rht(_strip_host(x, c0), A_STALE, axis=O.AXIS_COL, out_row0=c0, **okw)
+        _same(q.scales[c0:c0 + 16].cpu().numpy(), rs, f"RHT column scales, strip {c0}")
+        _same(q.codes[c0:c0 + 16].cpu().numpy(), rc, f"RHT column codes, strip {c0}")
+    del q
+    log("RHT row SR 65536x65552")
+    q = nv.quantize_rht(x, amax, axis="row", **kw)
+    torch.cuda.synchronize()
+    xr = _rows_host(x, SAMPLE_ROWS)
+    for i, r in enumerate(SAMPLE_ROWS):
+        rc, rs, _ = O.quantize_rht(xr[i:i + 1], A_STALE, axis=O.AXIS_ROW, out_row0=r, **okw)
+        _same(q.scales[r:r + 1].cpu().numpy(), rs, f"RHT row scales, row {r}")
+        _same(q.codes[r:r + 1].cpu().numpy(), rc, f"RHT row codes, row {r}")
+    del q
+    log("RHT SR past 2^32: ok")

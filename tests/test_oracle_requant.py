@@ -277,3 +277,21 @@ def test_requant_rejects_ragged_rows():
     with pytest.raises(ValueError):
         O.requant_t(codes, scales, **src, target="mxfp8")        # 16 rows: not a multiple of 32
     O.requant_t(codes, scales, **src, target="nvfp4", dst_amax=1.0)
+
+
+def test_strip_with_offset_is_the_full_result_rows():
+    """A strip of source columns col0.. re-quantized with col0 gives exactly
+    the rows col0.. of the whole tensor's result (both targets): the SR
+    indices of a strip are those of the wider output."""
+    rng = np.random.default_rng(11)
+    rows, cols = 64, 48
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0x28, 0x50, (rows, cols // 16), dtype=np.uint8)
+    for target, kw in (("mxfp8", {}), ("nvfp4", {"dst_amax": 9.0})):
+        full = O.requant_t(codes, scales, amax=50.0, target=target, seed=5, **kw)
+        for c0 in (0, 16, 32):
+            part = O.requant_t(np.ascontiguousarray(codes[:, c0 // 2:c0 // 2 + 8]),
+                               np.ascontiguousarray(scales[:, c0 // 16:c0 // 16 + 1]),
+                               amax=50.0, target=target, seed=5, col0=c0, **kw)
+            for f, p in zip(full, part):
+                assert np.array_equal(f[c0:c0 + 16], p), (target, c0)

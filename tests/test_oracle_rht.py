@@ -138,3 +138,18 @@ def test_dequantize_rht_inverts_exact_values():
     c, s, _ = O.quantize_rht(x, A, sign_seed=21, select=O.SELECT_6, global_max=448.0)
     assert np.all(s == 0x48)
     assert np.array_equal(O.dequantize_rht(c, s, A, sign_seed=21, global_max=448.0), x)
+
+
+@pytest.mark.parametrize("axis", [O.AXIS_ROW, O.AXIS_COL])
+def test_strip_with_offset_is_the_full_result_rows(axis):
+    """Row or column strips quantized with out_row0 reproduce the rows
+    out_row0.. of the whole tensor's output (SR indices of the wider output)."""
+    x = _outlier_tensor(48, 64, 7)
+    A = O.rht_amax(x, axis=axis, sign_seed=3)
+    kw = dict(axis=axis, sign_seed=3, select=O.SELECT_6, rounding=O.ROUND_SR, seed=99)
+    full = O.quantize_rht(x, A, **kw)
+    for o in (0, 16, 32):
+        strip = x[o:o + 16] if axis == O.AXIS_ROW else x[:, o:o + 16]
+        part = O.quantize_rht(np.ascontiguousarray(strip), A, out_row0=o, **kw)
+        for f, p in zip(full[:2], part[:2]):
+            assert np.array_equal(f[o:o + 16], p), o

@@ -330,8 +330,8 @@ __device__ __forceinline__ float tile_amax(const float* am, int t) {
 // (workgroup b on XCD b mod 8) hold consecutive units: neighbouring strips
 // then share their row-wise cache lines inside one XCD's L2.
 //
-// Per tile: the lanes load it with coalesced 16-byte loads (issued one tile
-// ahead) and store it into LDS, row-major with a padded pitch
+// Per tile: the lanes load it with coalesced 16-byte loads (issued one or two
+// tiles ahead, see kAhead) and store it into LDS, row-major with a padded pitch
 // (conflict-free 16-byte writes and reads); after a barrier,
 // lane b quantizes row block b (tile row b / 8, columns (b % 8) * 16 ..+16)
 // from two 16-byte LDS reads, and column block b (tile column b % 128, rows

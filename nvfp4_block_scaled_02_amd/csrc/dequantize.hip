@@ -173,8 +173,10 @@ dequantize_rows_kernel(const uint16_t* __restrict__ codes, const uint8_t* __rest
 template <int FMT, bool F32, bool BF16, bool BSC, bool SSE>
 static hipError_t launch_dq(const DequantizeArgs& a, hipStream_t s) {
   constexpr int BLOCK = SSE ? 1024 : kThreads;
-  const int64_t cap = (int64_t)device_cu_count() * (SSE ? 1 : 8);
+  const int64_t cus = device_cu_count();
   if (a.row_scaled) {
+    // SSE: one 1024-lane workgroup per CU (88 registers: two do not fit)
+    const int64_t cap = cus * (SSE ? 1 : 8);
     const int64_t grid = a.rows < cap ? a.rows : cap;
     hipLaunchKernelGGL((dequantize_rows_kernel<FMT, F32, BF16, BSC, SSE, BLOCK>),
                        dim3((unsigned)grid), dim3(BLOCK), 0, s,
@@ -184,6 +186,9 @@ static hipError_t launch_dq(const DequantizeArgs& a, hipStream_t s) {
                        reinterpret_cast<const uint2*>(a.x_ref), a.sse);
     return hipGetLastError();
   }
+  // SSE: two 1024-lane workgroups per CU (8 wavefronts per SIMD; one atomic
+  // each): 39.5 us at 8192x4096 against 42.1 with one, four give 40.0
+  const int64_t cap = cus * (SSE ? 2 : 8);
   const int64_t nquads = a.rows * a.cols / 4;
   const int64_t per_wg = (int64_t)BLOCK * kDqUnroll;
   int64_t grid = (nquads + per_wg - 1) / per_wg;

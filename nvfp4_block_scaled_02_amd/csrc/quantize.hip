@@ -156,10 +156,11 @@ quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float
 }
 
 // The same with every block transformed by the 16-point random Hadamard
-// transform first (its butterfly needs more registers than the 64 that eight
-// wavefronts per SIMD allow).
+// transform first.  Its butterfly needs more registers than the 64 that
+// eight wavefronts per SIMD allow (the capped build spills); held to 72,
+// seven fit (2% faster than the uncapped 76).
 template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
-__global__ void __launch_bounds__(BLOCK)
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(7)))
 quantize_blocks_rht_kernel(const uint4* __restrict__ x, int64_t nblocks,
                            const float* __restrict__ amax, float sg, uint64_t seed, uint32_t key0,
                            uint2* __restrict__ codes, uint8_t* __restrict__ scales,

@@ -123,7 +123,7 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
     const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
     const BlockOut o = quantize_block<FMT, SELECT, ROUND, false, RHT>(reg[2 * l], reg[2 * l + 1],
                                                                       tab, ts, hb, rht_signs);
-    codes[bk] = make_uint2(o.c0, o.c1);
+    st_nt(make_uint2(o.c0, o.c1), codes + bk);
     scales[bk] = (uint8_t)o.scale;
     n4 += o.four;
   }
@@ -138,7 +138,7 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
     const BlockOut o = quantize_block<FMT, SELECT, ROUND, false, RHT>(reg[2 * l], reg[2 * l + 1],
                                                                       tab, ts, hb, rht_signs);
     if (bk < nblocks) {
-      codes[bk] = make_uint2(o.c0, o.c1);
+      st_nt(make_uint2(o.c0, o.c1), codes + bk);
       scales[bk] = (uint8_t)o.scale;
       n4 += o.four;
     }
@@ -203,7 +203,7 @@ quantize_rowscaled_kernel(const uint4* __restrict__ x, int64_t nblocks, int64_t 
     const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
     const BlockOut o = quantize_block<FMT, SELECT, ROUND, true>(reg[2 * l], reg[2 * l + 1], nullptr, ts, hb);
     if (ok) {
-      codes[bk] = make_uint2(o.c0, o.c1);
+      st_nt(make_uint2(o.c0, o.c1), codes + bk);
       scales[bk] = (uint8_t)o.scale;
       n4 += o.four;
     }
@@ -255,7 +255,7 @@ quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_b
       const int64_t ob = ob0 + g * 64;
       const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)ob * 16, key0);
       const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
-      codes[ob] = make_uint2(o.c0, o.c1);
+      st_nt(make_uint2(o.c0, o.c1), codes + ob);
       scales[ob] = (uint8_t)o.scale;
       n4 += o.four;
     }
@@ -269,7 +269,7 @@ quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_b
       const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)ob * 16, key0);
       const BlockOut o = quantize_block<FMT, SELECT, ROUND>(reg[2 * l], reg[2 * l + 1], tab, ts, hb);
       if (bk < row_blocks) {
-        codes[ob] = make_uint2(o.c0, o.c1);
+        st_nt(make_uint2(o.c0, o.c1), codes + ob);
         scales[ob] = (uint8_t)o.scale;
         n4 += o.four;
       }

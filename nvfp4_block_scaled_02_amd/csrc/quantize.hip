@@ -419,7 +419,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
           o = quantize_block<FMT, SELECT, ROUND>(wa, wb, tab, ts, hb);
         }
         if (r < rows && c < cols) {
-          *reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c >> 1)) = make_uint2(o.c0, o.c1);
+          st_nt(make_uint2(o.c0, o.c1), reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c >> 1)));
           scales[r * (cols >> 4) + (c >> 4)] = (uint8_t)o.scale;
           n4 += o.four;
         }

@@ -481,6 +481,9 @@ constexpr int kStPitch = kStBytes + 4;          // LDS pitch (bytes), padded
 // tile indices within one stage) of the strip at c0.  Only rows < rows and
 // columns < cols are written.  Consecutive lanes write consecutive words (or
 // bytes) of one column, so a wavefront store covers whole 64-byte pieces.
+// NT: non-temporal code stores (measured faster for the re-quantization's
+// walk, slower for the quantizer's column-wise walk).
+template <bool NT = false>
 __device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __restrict__ codes_t,
                                               int64_t rows, int64_t cols, int64_t c0,
                                               int64_t t_lo, int64_t t_hi) {
@@ -496,9 +499,11 @@ __device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __res
   for (int u = 0; u < kSW * kCtWords / kThreads; ++u) {
     const int j = u * kThreads + threadIdx.x;
     const int col = j / kCtWords, wd = j % kCtWords;
-    if (wd >= w_lo && wd < w_hi && c0 + col < cols)
-      *reinterpret_cast<uint32_t*>(codes_t + (c0 + col) * stride + (row0 >> 1) + wd * 4) =
-          ct[col * kCtPitch + wd];
+    if (wd >= w_lo && wd < w_hi && c0 + col < cols) {
+      uint32_t* p = reinterpret_cast<uint32_t*>(codes_t + (c0 + col) * stride + (row0 >> 1) + wd * 4);
+      if constexpr (NT) st_nt(ct[col * kCtPitch + wd], p);
+      else *p = ct[col * kCtPitch + wd];
+    }
   }
 }
 

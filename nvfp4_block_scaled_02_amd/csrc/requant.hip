@@ -256,7 +256,7 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
       const bool last = tr + 1 == tr1;
       if constexpr (NV) {
         if (last || (tr + 1) % kCtTiles == 0) {
-          flush_codes_t(ct, out_t, rows, cols, c0, ct_lo, tr + 1);
+          flush_codes_t<true>(ct, out_t, rows, cols, c0, ct_lo, tr + 1);
           ct_lo = tr + 1;
         }
         if (last || (tr + 1) % kStTiles == 0) {

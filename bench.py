@@ -92,8 +92,12 @@ class Timer:
         self.stream = torch.cuda.current_stream(dev)
 
     def avg_us(self, fn, reps, nsets):
+        """Average duration of fn(i) over `reps` back-to-back calls, after as
+        many untimed calls (at least one per buffer set): the GPU's clocks
+        settle within milliseconds of sustained load, and the first
+        milliseconds after an idle gap run slower."""
         torch = self.torch
-        for i in range(nsets):
+        for i in range(max(nsets, reps)):
             fn(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -652,7 +656,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="activation",
                     choices=["activation", "weight-1k", "weight", "qat", "gradient",
                              "activation-pertoken", "weight-2d", "requant", "select", "rht"])

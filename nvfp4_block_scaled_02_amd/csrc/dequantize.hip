@@ -43,13 +43,12 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
                   float4* __restrict__ out_f32, uint2* __restrict__ out_bf16,
                   float* __restrict__ block_scale, const uint2* __restrict__ x_ref,
                   double* sse) {
-  const float alpha = outer_alpha(*amax, sg);
   const bool lead4 = (threadIdx.x & 3) == 0;
   double acc = 0.0;
   const int64_t per_iter = (int64_t)gridDim.x * BLOCK * kDqUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * BLOCK * kDqUnroll; base < nquads; base += per_iter) {
-    uint32_t cw[kDqUnroll], sc[kDqUnroll];
-    uint2 xr[kDqUnroll];
+  uint32_t cw[kDqUnroll], sc[kDqUnroll];
+  uint2 xr[kDqUnroll];
+  auto load = [&](int64_t base) {
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
       const int64_t qd = base + u * BLOCK + threadIdx.x;
@@ -58,6 +57,14 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
       sc[u] = ok ? (uint32_t)scales[qd >> 2] : 0u;
       if (SSE) xr[u] = ok ? ld_nt(x_ref + qd) : make_uint2(0, 0);
     }
+  };
+  // The first trip's loads go out before the outer scale is read (two
+  // dependent scalar loads and a division), so their latency overlaps it;
+  // each later trip's loads are issued at the end of the one before.
+  int64_t base = (int64_t)blockIdx.x * BLOCK * kDqUnroll;
+  load(base);
+  const float alpha = outer_alpha(*amax, sg);
+  for (; base < nquads; base += per_iter) {
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
       const int64_t qd = base + u * BLOCK + threadIdx.x;
@@ -82,6 +89,7 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
         }
       }
     }
+    if (base + per_iter < nquads) load(base + per_iter);
   }
   if (SSE) {
     __shared__ double red[BLOCK / 64];

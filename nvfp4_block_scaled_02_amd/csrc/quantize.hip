@@ -105,19 +105,30 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
                                             unsigned long long* count4, uint32_t rht_signs) {
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint4 stage[BLOCK * 2];
-  const TensorScale ts = tensor_scale(*amax, sg);
-  build_table<FMT>(tab, ts.alpha);
-  __syncthreads();
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
   uint4* reg = stage + wv * 128;  // this wavefront's 2 KiB
   const int64_t nchunks = nblocks * 2;
   const int64_t nwhole = nblocks / 64;  // groups of 64 blocks
   const int64_t nwaves = (int64_t)gridDim.x * (BLOCK / 64);
-  uint32_t n4 = 0;
   int64_t g = (int64_t)blockIdx.x * (BLOCK / 64) + wv;
-  // whole groups, unchecked
+  // The first group's loads go out before the outer scale is read and the
+  // table built, so their latency overlaps that start-up instead of
+  // following it (every workgroup of the grid is resident from the start).
+  // The loads are unconditional (a wavefront without a whole group reads
+  // clamped addresses and ignores the data), and nothing before the loop
+  // waits on them: the table takes one entry per lane (BLOCK >= codes).
+  static_assert(BLOCK >= FmtTraits<FMT>::kCodes, "one table entry per lane");
+  const int64_t c0 = (g < nwhole ? g : 0) * 128 + l;
+  uint4 a = ld_nt(x + (c0 < nchunks ? c0 : nchunks - 1));
+  uint4 b = ld_nt(x + (c0 + 64 < nchunks ? c0 + 64 : nchunks - 1));
+  const TensorScale ts = tensor_scale(*amax, sg);
+  if (threadIdx.x < FmtTraits<FMT>::kCodes)
+    tab[threadIdx.x] = scale_entry(FMT, threadIdx.x, ts.alpha);
+  __syncthreads();
+  uint32_t n4 = 0;
+  // whole groups, unchecked; the next group's loads are issued after this
+  // group's stores (not before its arithmetic: that would cost registers)
   for (; g < nwhole; g += nwaves) {
-    const uint4 a = ld_nt(x + g * 128 + l), b = ld_nt(x + g * 128 + 64 + l);
     bounce_pair(reg, l, a, b);
     const int64_t bk = g * 64 + l;
     const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
@@ -126,6 +137,11 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
     st_nt(make_uint2(o.c0, o.c1), codes + bk);
     scales[bk] = (uint8_t)o.scale;
     n4 += o.four;
+    const int64_t gn = g + nwaves;
+    if (gn < nwhole) {
+      a = ld_nt(x + gn * 128 + l);
+      b = ld_nt(x + gn * 128 + 64 + l);
+    }
   }
   // the partial last group (nblocks % 64 blocks), if this wavefront owns it
   if (g == nwhole && nblocks % 64 != 0) {

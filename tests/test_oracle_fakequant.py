@@ -135,11 +135,18 @@ def test_tied_identity():
 
 
 def test_zero_scale_block():
-    x = np.zeros((1, 16), np.float32)
+    """A zero block scale has no reciprocal; the reading taken is inv = 0, so
+    every y = x * inv is a zero (inside the clamp range), every q is zero, the
+    forward output is zero for any x, the tied backward passes g through with
+    a zero scale gradient, and the dual backward gives zero everywhere
+    (r = s_post * inv = 0)."""
     g = np.ones((1, 16), np.float32)
     s = np.zeros(1, np.float32)
-    assert np.all(O.fakequant_fwd(x, s) == 0)
-    dx, ds = O.fakequant_bwd(x, g, s)
-    assert np.all(dx == 1) and ds[0] == 0
-    dx, dpre, dpost = O.fakequant_bwd(x, g, s, np.ones(1, np.float32))
-    assert np.all(dx == 0) and dpre[0] == 0 and dpost[0] == 0
+    for x in (np.zeros((1, 16), np.float32),
+              np.linspace(-3.0, 5.0, 16, dtype=np.float32).reshape(1, 16)):
+        assert np.all(O.fakequant_fwd(x, s) == 0)
+        assert np.all(O.fakequant_fwd(x, s, np.full(1, 2.0, np.float32)) == 0)
+        dx, ds = O.fakequant_bwd(x, g, s)
+        assert np.all(dx == 1) and ds[0] == 0
+        dx, dpre, dpost = O.fakequant_bwd(x, g, s, np.ones(1, np.float32))
+        assert np.all(dx == 0) and dpre[0] == 0 and dpost[0] == 0

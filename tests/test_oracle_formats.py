@@ -143,6 +143,23 @@ def test_fmix32_published_vectors(pages):
     assert O.fmix32(0) == int(v["seed0"], 16)
 
 
+def test_sr_hash_key_construction():
+    """The counter hash is fmix32 (pinned above to MurmurHash3's published
+    finalizer) applied to lo32(idx) ^ k, with the key
+    k = fmix32(lo32(seed) ^ fmix32(hi32(seed) ^ hi32(idx) ^ C)) and C the
+    32-bit golden-ratio constant floor(2^32 / phi).  The pages leave the
+    random source of stochastic rounding open; this pins the constant to its
+    published definition and each word of seed and index to its place."""
+    phi = (1 + 5 ** 0.5) / 2
+    C = int(2 ** 32 / phi)
+    assert C == 0x9E3779B9
+    M = 0xFFFFFFFF
+    for seed in (0, 1234, 0xDEADBEEF12345678, (7 << 32) | 3):
+        for idx in (0, 1, 15, 123456789, (1 << 32) + 5, (0xABCDE << 32) | 0x1234):
+            k = O.fmix32((seed & M) ^ O.fmix32((seed >> 32) ^ (idx >> 32) ^ C))
+            assert O.sr_hash(seed, idx) == O.fmix32((idx & M) ^ k), (seed, idx)
+
+
 def test_sr_hash_uniformity():
     n = 1 << 16
     u = np.array([O.sr_hash(1234, i) >> 8 for i in range(n)], np.float64) / 2 ** 24

@@ -334,6 +334,29 @@ def test_zero_tensor_and_zero_blocks():
     assert np.all(xh == 0)
 
 
+def test_reciprocal_overflow_of_tiny_amax():
+    """A tensor amax so small that 1 / (6 alpha) overflows binary32: the
+    per-tensor constant K_6 is then the largest finite float, not infinity
+    (the oracle's reading of an overflowing reciprocal), so a block holding the
+    tensor maximum A = 2^-123 gets the scale code nearest to fl(A * FLT_MAX)
+    = 31.999998 (E4M3 32 = 0x60) instead of saturating at 448, and a block
+    whose maximum is A / 4 gets the code nearest to 8 (0x50)."""
+    A = np.float32(2.0 ** -123)
+    alpha = A / np.float32(6.0 * 448.0)
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(1.0) / (np.float32(6.0) * alpha))
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = A
+    x[0, 16] = A / 4
+    kmax = np.finfo(np.float32).max
+    want = [O.scale_encode(E4M3, float(np.float32(A) * kmax)),
+            O.scale_encode(E4M3, float(np.float32(A / 4) * kmax))]
+    assert want == [0x60, 0x50]
+    for select in (O.SELECT_6, O.SELECT_4OVER6):
+        _, scales, _ = _q1(x, float(A), select=select, global_max=448.0)
+        assert list(scales[0]) == want, select
+
+
 def test_sr_rejected_with_four_over_six():
     with pytest.raises(ValueError):
         O.quantize(np.zeros((1, 16), np.float32), 1.0, select=O.SELECT_4OVER6, rounding=O.ROUND_SR)

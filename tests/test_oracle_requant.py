@@ -5,6 +5,8 @@ stochastic rounding to NVFP4 or MXFP8) against the page's worked example,
 unbiasedness, exact identities on representable values, and the MXFP8 block
 rules (OCP Microscaling: blocks of 32, power-of-two E8M0 scale, E4M3
 elements).  CPU only."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -253,6 +255,14 @@ def test_e4m3_sr_rule_counts_exactly():
             ups += v == hi
         # sampled u on an even grid: the up-fraction is p to the sample's resolution
         assert abs(ups / idx.size - p) <= 1.0 / idx.size + 1e-12
+        # the threshold itself: exactly the u >= 2^20 - floor(p * 2^20) round up,
+        # so the up-count over all 2^20 variates is floor(p * 2^20)
+        F = int(Fraction(y - lo) / Fraction(hi - lo) * 2 ** 20)
+        T = 2 ** 20 - F
+        if T <= 2 ** 20 - 1:
+            assert O.scale_decode(E4M3, O.e4m3_code_sr(y, T << 12) & 0x7F) == hi
+        if 1 <= T <= 2 ** 20:
+            assert O.scale_decode(E4M3, O.e4m3_code_sr(y, ((T - 1) << 12) | 0xFFF) & 0x7F) == lo
     assert O.e4m3_code_sr(-2.25, 0xFFFFFFFF) == 0x80 | 0x41   # on grid: sign kept, unchanged
     assert O.e4m3_code_sr(449.0, 0xFFFFFFFF) == 0x7E          # saturates, never NaN
 
@@ -270,6 +280,53 @@ def test_requant_nan_blocks():
     el, sc = O.requant_t(codes, scales, **src, target="mxfp8", seed=1)
     assert np.all(sc[32:48, 0] == 0xFF) and np.all(el[32:48, :] == 0)
     assert np.all(sc[:32] != 0xFF) and np.all(sc[48:] != 0xFF)
+
+
+def test_mxfp8_sr_index_and_scale():
+    """Each MXFP8 element is the E4M3 stochastic rounding of x * 2^-e, e the
+    block's E8M0 exponent, with the counter hash of its own index in the
+    output orientation ((row0 + r) * cols + c): every element of a block draws
+    its own variate."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((4, 64)) * 3.0).astype(np.float32)
+    el, sc = O.mxfp8_quantize_sr(x, seed=99, row0=3)
+    for r in range(4):
+        for c in range(64):
+            e = int(sc[r, c // 32]) - 127
+            y = float(np.float32(x[r, c]) * np.float32(2.0 ** -e))
+            assert el[r, c] == O.e4m3_code_sr(y, O.sr_hash(99, (3 + r) * 64 + c)), (r, c)
+
+
+def test_mxfp8_non_finite_blocks():
+    """A NaN or an infinity in a 32-element block has no power-of-two scale:
+    the block's E8M0 byte is the NaN code 0xFF and its elements are 0; the
+    other block of the row is unaffected."""
+    x = np.ones((2, 64), np.float32)
+    x[0, 5] = np.inf
+    x[1, 40] = np.nan
+    el, sc = O.mxfp8_quantize_sr(x, seed=1)
+    assert sc[0, 0] == 0xFF and np.all(el[0, :32] == 0) and sc[0, 1] != 0xFF
+    assert sc[1, 1] == 0xFF and np.all(el[1, 32:] == 0) and sc[1, 0] != 0xFF
+    assert np.all(np.isnan(O.mxfp8_dequantize(el, sc)[0, :32]))
+
+
+def test_dequantized_amax_is_the_max_of_the_dequantized_tensor():
+    """The outer scale of a re-quantization is max |x_hat| over the whole
+    dequantized tensor (the last row included), per-tensor or per-row source."""
+    for per_row in (False, True):
+        codes, scales, src = _random_source(32, 64, 5, per_row=per_row)
+        scales, codes = scales.copy(), codes.copy()
+        scales[31, 3] = 0x7E  # the largest block scale and code 6, in the last row's last block
+        codes[31, 24:32] = 0x77
+        if per_row:
+            xh = np.concatenate([O.dequantize(codes[r:r + 1], scales[r:r + 1], float(src["row_amaxes"][r]))
+                                 for r in range(32)])
+        else:
+            xh = O.dequantize(codes, scales, float(src["amax"]))
+        want = np.max(np.abs(xh))
+        if not per_row:  # the planted block holds the maximum
+            assert np.argmax(np.abs(xh).max(axis=1)) == 31
+        assert O.dequantized_amax(codes, scales, **src) == want
 
 
 def test_requant_rejects_ragged_rows():

@@ -62,6 +62,11 @@ def test_single_outlier_is_spread_evenly():
 
 
 def test_sign_vector_is_seeded():
+    # s_j = -1 iff the top bit of the counter hash (pinned in the formats
+    # tests) of index j under the sign seed is set
+    for seed in (0, 7, 1234, (5 << 32) | 9):
+        want = sum(1 << j for j in range(16) if O.sr_hash(seed, j) >> 31)
+        assert O.rht_signs(seed) == want
     m = [O.rht_signs(s) for s in range(200)]
     assert len(set(m)) > 190 and O.rht_signs(7) == O.rht_signs(7)
     neg = np.mean([bin(v).count("1") for v in m]) / 16

@@ -178,13 +178,6 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kRqPitch];
   __shared__ uint32_t ct[NV ? kSW * kCtPitch : 1];
   __shared__ uint8_t st[NV ? kSW * kStPitch : kSW * kMxStPitch];
-  TensorScale ts{};
-  if constexpr (NV) {
-    ts = tensor_scale(*dst_amax, dst_sg);
-    build_table<DST_FMT>(tab, ts.alpha);
-  }
-  const float alpha0 = ROWSC ? 0.0f : outer_alpha(*amax, sg);
-  __syncthreads();
   const int64_t tiles_r = (rows + kTR - 1) / kTR, tiles_c = (cols + kSW - 1) / kSW;
   const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
   const int64_t G = gridDim.x, b = blockIdx.x;
@@ -192,6 +185,25 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
   const int lane = threadIdx.x;
   const int cb_col = lane & (kSW - 1), cb_row = (lane / kSW) * kCB;  // this lane's column block
   const int col_off = rq_col_off(cb_col);
+  // MXFP8 target: the first unit's first two tiles are requested before the
+  // outer scale is read, so their latency overlaps that start-up (30.1 ->
+  // 28.9 us at 8192x4096).  The NVFP4 target, which also builds its code
+  // table there, ran 1.4% slower that way and keeps the plain order.
+  RqLoad<TARGET> A, B, C;
+  if (!NV && v < units) {
+    const int64_t g = v / tiles_c, c0 = (v - g * tiles_c) * kSW, tr0 = g * seg;
+    const int64_t tr1 = tr0 + seg < tiles_r ? tr0 + seg : tiles_r;
+    rq_load<TARGET, ROWSC>(A, codes, scales, row_amax, rows, cols, tr0 * kTR, c0);
+    rq_load<TARGET, ROWSC>(B, codes, scales, row_amax, rows, cols,
+                           (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0);
+  }
+  TensorScale ts{};
+  if constexpr (NV) {
+    ts = tensor_scale(*dst_amax, dst_sg);
+    build_table<DST_FMT>(tab, ts.alpha);
+  }
+  const float alpha0 = ROWSC ? 0.0f : outer_alpha(*amax, sg);
+  __syncthreads();
   for (int64_t unit = v; unit < units; unit += G) {
     const int64_t g = unit / tiles_c;
     const int64_t c0 = (unit - g * tiles_c) * kSW;
@@ -270,10 +282,11 @@ requant_t_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ 
         }
       }
     };
-    RqLoad<TARGET> A, B, C;
-    rq_load<TARGET, ROWSC>(A, codes, scales, row_amax, rows, cols, tr0 * kTR, c0);
-    rq_load<TARGET, ROWSC>(B, codes, scales, row_amax, rows, cols,
-                           (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0);
+    if (NV || unit != v) {  // MXFP8: the first unit's tiles were requested above
+      rq_load<TARGET, ROWSC>(A, codes, scales, row_amax, rows, cols, tr0 * kTR, c0);
+      rq_load<TARGET, ROWSC>(B, codes, scales, row_amax, rows, cols,
+                             (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0);
+    }
     int64_t tr = tr0;
     for (; tr + 3 <= tr1; tr += 3) {
       step(A, C, tr);

@@ -519,10 +519,10 @@ static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, B>), dim3((unsigned)grid),
                            dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg,
                            a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
-      } else {
-        // two 1024-thread workgroups per CU (8 wavefronts per SIMD, as with
-        // eight of 256): a quarter of the table builds, 16.57 -> 16.0 us at
-        // 8192x4096 (same-box A/B)
+      } else if (ngroups >= (int64_t)cus * 32) {
+        // enough groups to fill every CU: two 1024-thread workgroups per CU
+        // (8 wavefronts per SIMD, as with eight of 256) build a quarter of
+        // the tables, 16.57 -> 16.0 us at 8192x4096 (same-box A/B)
         constexpr int B = 1024;
         int64_t grid = (ngroups + B / 64 - 1) / (B / 64);
         const int64_t cap = (int64_t)cus * 2;
@@ -530,6 +530,15 @@ static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, B>), dim3((unsigned)grid),
                            dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg,
                            a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+      } else {
+        // small tensors: 256-thread workgroups spread the groups over more CUs
+        int64_t grid = (ngroups + kThreads / 64 - 1) / (kThreads / 64);
+        const int64_t cap = (int64_t)cus * 8;
+        grid = grid < cap ? grid : cap;
+        hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, kThreads>),
+                           dim3((unsigned)grid), dim3(kThreads), 0, s,
+                           reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg, a.seed, key0,
+                           reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
       }
     } else {
       // max->6 with round-to-nearest: the lane-pair stream (no count output)

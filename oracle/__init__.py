@@ -9,8 +9,10 @@ sources and the precision rules); this module only marshals numpy arrays.
 Inputs are bfloat16 bit patterns (``uint16``) or float32 arrays; bf16 is
 widened to float32 exactly (the bits shifted into the high half).
 
-Parity unpinned: the UE5M3 scale format (no outside definition exists on the
-pages; only its stated closed form is checked).
+The UE5M3 scale format is pinned to what the "UE5M3" blog fixes (unsigned,
+5 exponent and 3 mantissa bits, its emulation's bias and mantissa rounding);
+its subnormals, NaN code and largest code remain a reading (the E4M3FN
+conventions carried over).
 """
 import ctypes
 import os

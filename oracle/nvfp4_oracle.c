@@ -31,10 +31,13 @@
  * binary32 at the end.  Build: gcc -O2 -ffp-contract=off, no fast-math, so
  * every float operation rounds once and fmaf() is the only fused operation.
  *
- * Parity unpinned: the UE5M3 format itself.  The pages say only that it is
- * unsigned with 5 exponent and 3 mantissa bits ([UE] 数学推导); bias 15,
- * subnormals, 0xFF = NaN and the 114688 maximum are a reading (the E4M3FN
- * pattern carried over), checked here only against its own closed form.
+ * UE5M3 ([UE] 数学推导, 实现): unsigned, 5 exponent and 3 mantissa bits, and
+ * the emulation's bias 2^(5-1) - 1 = 15 with its top binade 2^16; the tests
+ * pin these against a minifloat built from those rules (the same
+ * construction reproduces torch's E4M3FN byte) and against the emulation's
+ * round-half-even mantissa rule over the normal range.  Still a reading:
+ * the subnormals below 2^-14, 0xFF = NaN and the 114688 maximum, which carry
+ * the E4M3FN conventions over (the emulation is not a format at its ends).
  */
 #include <float.h>
 #ifdef _OPENMP
@@ -118,8 +121,9 @@ int or_e2m1_code_sr(float y, uint32_t h) {
 /* Block-scale formats.  E4M3 is the OCP E4M3FN byte: bias 7, subnormals
  * m/8 * 2^-6, largest finite 0x7E = 448, 0x7F = NaN; this gives NVFP4 its
  * magnitude range 2^-10 .. 2688 = 6 * 448 ([E2E] Low-precision formats).
- * UE5M3 is unsigned with 5 exponent and 3 mantissa bits ([UE] 数学推导);
- * its bias, subnormals and NaN code are the reading stated in the header. */
+ * UE5M3 is unsigned with 5 exponent and 3 mantissa bits ([UE] 数学推导) and
+ * bias 15 ([UE] 实现, the emulation's 2^(E-1) - 1); its subnormals, NaN code
+ * and largest code are the reading stated in the header. */
 static int fmt_max_code(int fmt) { return fmt == OR_FMT_E4M3 ? 0x7E : 0xFE; }
 int or_scale_nan_code(int fmt) { return fmt == OR_FMT_E4M3 ? 0x7F : 0xFF; }
 

@@ -110,14 +110,106 @@ def test_e4m3_encode_saturates_above_max():
         assert O.scale_encode("e4m3", v) == 0x7E
 
 
-def test_ue5m3_closed_form():
-    # Parity unpinned: the pages define UE5M3 only as unsigned, 5 exponent and
-    # 3 mantissa bits.  These checks hold the stated reading to itself.
+def _minifloat_fn(code, ebits, mbits, signed):
+    """Decode one byte of an FN-style minifloat (no infinities; the all-ones
+    pattern is NaN; exponent field 0 holds the subnormals) with the bias
+    2^(ebits-1) - 1 that the "UE5M3" blog's emulation uses (实现).  Written
+    here independently of the oracle; for ebits=4, mbits=3, signed it is the
+    OCP E4M3FN byte (checked against torch below)."""
+    bias = 2 ** (ebits - 1) - 1
+    sign = -1.0 if (signed and code >> (ebits + mbits) & 1) else 1.0
+    body = code & ((1 << (ebits + mbits)) - 1)
+    if body == (1 << (ebits + mbits)) - 1:
+        return float("nan")
+    e, m = body >> mbits, body & ((1 << mbits) - 1)
+    if e == 0:
+        return sign * m / 2 ** mbits * 2.0 ** (1 - bias)
+    return sign * (1 + m / 2 ** mbits) * 2.0 ** (e - bias)
+
+
+def test_minifloat_construction_reproduces_torch_e4m3fn():
+    # the construction the UE5M3 pins rest on, checked on the one format a
+    # library defines: every E4M3FN byte
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([_minifloat_fn(c, 4, 3, True) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok].astype(np.float64))
+
+
+def test_ue5m3_is_unsigned_5_exponent_3_mantissa_bits():
+    """"UE5M3" blog (数学推导; 背景): the block scale is unsigned with 5
+    exponent and 3 mantissa bits.  The oracle's decode equals the same
+    construction with ebits=5, mbits=3 and no sign bit for every byte: bit 7
+    is an exponent bit (0x80 decodes to +2, not to -0), every binade holds 8
+    codes spaced by a 1/8 of its base, and the bias is 2^4 - 1 = 15."""
+    for c in range(256):
+        want = _minifloat_fn(c, 5, 3, False)
+        got = O.scale_decode("ue5m3", c)
+        if np.isnan(want):
+            assert np.isnan(got), c
+        else:
+            assert got == want, (c, got, want)
+    assert O.scale_decode("ue5m3", 0x80) == 2.0
+    vals = [O.scale_decode("ue5m3", c) for c in range(255)]
+    assert all(v >= 0 for v in vals)
+    assert all(b > a for a, b in zip(vals, vals[1:]))  # unsigned: code order = value order
+    for e in range(1, 31):  # 8 codes per binade, spaced base / 8
+        base = 2.0 ** (e - 15)
+        assert [vals[8 * e + m] for m in range(8)] == [base + m * base / 8 for m in range(8)]
+    # the top binade is 2^(2^5 - 1 - 15) = 2^16, the emulation's exponent ceiling
+    assert vals[0xF8] == 2.0 ** 16
+
+
+def test_ue5m3_rounding_matches_the_pages_mantissa_rule():
+    """The "UE5M3" blog's emulation (实现) rounds a positive scale within its
+    binade 2^e (e = floor(log2 s), clamped to [-bias, 2^5 - 1 - bias]) to 3
+    fractional mantissa bits, ties to even.  Over the normal range of the
+    format (2^-14 .. 114688) the oracle's encoder gives exactly that value;
+    below 2^-14 the format reading adds subnormals (step 2^-17) and at the top
+    it saturates at 0xFE, where the emulation is not a format (it carries past
+    the exponent field)."""
+    rng = np.random.default_rng(11)
+    s = np.concatenate([2.0 ** rng.uniform(-14, np.log2(114688.0), 4000),
+                        [2.0 ** -14, 1.0, 1.0625, 1.1875, 3.0, 448.0, 1000.0, 114688.0]])
+    s = s.astype(np.float32).astype(np.float64)
+    # exact ties (half way between two codes) and their neighbours
+    mids = np.array([(1 + (m + 0.5) / 8) * 2.0 ** e for e in (-10, 0, 7, 15) for m in range(7)])
+    s = np.concatenate([s, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9)]).astype(np.float32)
+    for v in s.astype(np.float64):
+        e = int(np.floor(np.log2(v)))
+        e = min(max(e, -15), 2 ** 5 - 1 - 15)
+        want = np.rint(v / 2.0 ** e * 8) / 8 * 2.0 ** e
+        if want > 114688.0:
+            want = 114688.0
+        got = O.scale_decode("ue5m3", O.scale_encode("ue5m3", float(v)))
+        assert got == want, (float(v), got, want)
+
+
+def test_ue5m3_range_is_wider_than_e4m3():
+    """"UE5M3" blog (直觉解释): one more exponent bit doubles the range the
+    scale can span, at the same 3 mantissa bits.  Against the torch-pinned
+    E4M3 byte: the largest value grows by 2^8 and the smallest by 2^-8, the
+    log2 span roughly doubles, and where both formats have normal binades
+    (2^-6 .. 448) they hold exactly the same values."""
+    ue = np.array([O.scale_decode("ue5m3", c) for c in range(255)])
+    e4 = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert ue.max() == 256 * e4.max()
+    assert ue[ue > 0].min() == e4[e4 > 0].min() / 256
+    span_ue = np.log2(ue.max() / ue[ue > 0].min())
+    span_e4 = np.log2(e4.max() / e4[e4 > 0].min())
+    assert 1.8 < span_ue / span_e4 < 2.2
+    lo, hi = 2.0 ** -6, 448.0
+    assert np.array_equal(ue[(ue >= lo) & (ue <= hi)], e4[(e4 >= lo) & (e4 <= hi)])
+
+
+def test_ue5m3_encode_closed_form():
+    # the format's own ends: subnormal step 2^-17, largest 0xFE, NaN 0xFF,
+    # saturation, and encode(decode(c)) = c
     vals = [O.scale_decode("ue5m3", c) for c in range(255)]
     assert vals[1] == 2.0 ** -17 and vals[8] == 2.0 ** -14
     assert vals[0xFE] == 114688.0 == 1.75 * 2 ** 16
     assert np.isnan(O.scale_decode("ue5m3", 0xFF))
-    assert all(b > a for a, b in zip(vals, vals[1:]))
     assert O.scale_encode("ue5m3", 1e9) == 0xFE
     for c in range(255):
         assert O.scale_encode("ue5m3", vals[c]) == c

@@ -28,11 +28,19 @@
  *  - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA/HIP
  *    tensors) unless stated; the caller owns every buffer; the library keeps
  *    no state between calls and allocates nothing.
- *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream) and never synchronizes.  Arguments are validated on the host
- *    before anything is launched; a non-zero status means nothing was
- *    launched (NVFP4_ERR_HIP: a launch was attempted and HIP reported an
- *    error).
+ *  - Every call is asynchronous on `stream` (NULL = the null stream) and
+ *    never synchronizes.
+ *  - Workspace: calls that combine one value per workgroup across the whole
+ *    launch (a maximum, a count, a sum) take `workspace`, NVFP4_WORKSPACE_BYTES
+ *    of device memory (16-byte aligned) that the caller zero-fills once before
+ *    its first use.  Each workgroup stores its value in its own slot and the
+ *    last one to finish combines the slots in a fixed order, in the same
+ *    launch; every call that runs to completion leaves the workspace's
+ *    counters zero again, so it is reused as is.  Calls that may run at the
+ *    same time (other streams) need workspaces of their own.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    non-zero status means nothing was launched (NVFP4_ERR_HIP: a launch was
+ *    attempted and HIP reported an error).
  *  - bfloat16 values travel as their 16-bit patterns (uint16_t).
  *  - Tensors are dense row-major [rows, cols].  Data pointers (x, codes,
  *    out_f32, out_bf16, grad tensors) must be 16-byte aligned; the row-wise
@@ -45,13 +53,18 @@
 #ifndef NVFP4_H
 #define NVFP4_H
 
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 5
+#define NVFP4_ABI_VERSION 6
+
+/* Size of a workspace (see the conventions above). */
+#define NVFP4_WORKSPACE_BYTES 66688
 
 /* Status codes. */
 enum {
@@ -62,12 +75,11 @@ enum {
 };
 
 /* Block-scale formats.  E4M3 = OCP E4M3FN (bias 7, max 448, 0x7F = NaN).
- * UE5M3 = unsigned, 5 exponent / 3 mantissa bits, read as bias 15 with
- * subnormals, max 0xFE = 114688, 0xFF = NaN (the pages fix only the field
- * widths). */
+ * UE5M3 = unsigned, 5 exponent / 3 mantissa bits, bias 15 ("UE5M3" blog,
+ * 数学推导 and the emulation in 实现), with subnormals, max 0xFE = 114688
+ * and 0xFF = NaN (the E4M3FN conventions carried over). */
 enum { NVFP4_SCALE_E4M3 = 0, NVFP4_SCALE_UE5M3 = 1 };
 
-/* Block-scale selection: every block max -> 6, or Four-Over-Six (MSE). */
 /* Block-scale selection ("Four Over Six" summaries: Methodologie, Key claims;
  * "Scale Learning" blog: the MSE scale sweep that initializes the scales). */
 enum {
@@ -90,37 +102,72 @@ enum { NVFP4_AXIS_ROW = 1, NVFP4_AXIS_COL = 2 };
 #define NVFP4_GLOBAL_MAX_E4M3_4OVER6 256.0f
 #define NVFP4_GLOBAL_MAX_UE5M3 114688.0f
 
-/*
- * nvfp4_tensor_amax -- current-tensor scaling: *amax_out = max_i |x_i| over
- * numel bf16 values ("UE5M3" blog, 数学推导).
- *   x         device, numel bf16 patterns, 16-byte aligned.
- *   numel     >= 0; 0 writes 0.
- *   amax_out  device, one float; overwritten (no need to clear it).
- * A NaN anywhere gives NaN; otherwise an infinity gives +inf.
- * Errors: x or amax_out NULL with numel > 0, or numel < 0 -> NVFP4_ERR_INVALID.
- */
-int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* stream);
+/* NVFP4_WORKSPACE_BYTES of the loaded library. */
+size_t nvfp4_workspace_bytes(void);
 
 /*
- * nvfp4_quantize -- NVFP4 quantization of a bf16 tensor x[rows, cols].
- *   amax            device float: the tensor amax A (fresh from
- *                   nvfp4_tensor_amax, or a stale/periodic value).  The outer
+ * nvfp4_tensor_amax -- current-tensor scaling: *amax_out = max_i |x_i| over
+ * numel bf16 values ("UE5M3" blog, 数学推导: the amax of the whole tensor
+ * recomputed at every step).  One launch.
+ *   x          device, numel bf16 patterns, 16-byte aligned.
+ *   numel      >= 0; 0 writes 0.
+ *   amax_out   device, one float; overwritten (no need to clear it).
+ *   workspace  a workspace (see above).
+ * A NaN anywhere gives NaN; otherwise an infinity gives +inf.
+ * Errors: x (numel > 0), amax_out or workspace NULL or misaligned, or
+ * numel < 0 -> NVFP4_ERR_INVALID.
+ */
+int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* workspace,
+                      hipStream_t stream);
+
+/*
+ * Arguments of the quantize calls: one struct, so that the outputs of the
+ * row-wise and column-wise layouts, the optional 4/6 count and its
+ * workspace travel together.
+ */
+typedef struct nvfp4_quant_args {
+  const uint16_t* x;            /* bf16 [rows, cols], row-major, 16-byte aligned */
+  int64_t rows, cols;
+  const float* amax;            /* device: the tensor amax A (one float), or for
+                                   nvfp4_quantize_rowscaled one amax per row */
+  float global_fp8_max;         /* S_g > 0, or 0 for the default (below) */
+  int scale_fmt;                /* NVFP4_SCALE_E4M3 or NVFP4_SCALE_UE5M3 */
+  int select;                   /* an NVFP4_SELECT_* rule */
+  int rounding;                 /* NVFP4_ROUND_RNE or NVFP4_ROUND_SR */
+  int axes;                     /* NVFP4_AXIS_ROW, NVFP4_AXIS_COL or both */
+  uint64_t seed;                /* stochastic rounding only */
+  uint8_t* codes;               /* ROW: [rows, cols/2], 16-byte aligned */
+  uint8_t* scales;              /* ROW: [rows, cols/16], 4-byte aligned */
+  uint8_t* codes_t;             /* COL: [cols, rows/2], 16-byte aligned */
+  uint8_t* scales_t;            /* COL: [cols, rows/16] */
+  unsigned long long* count4;   /* optional: += blocks that chose max->4 */
+  void* workspace;              /* required with count4 (see above), else unused */
+} nvfp4_quant_args;
+
+/*
+ * nvfp4_quantize -- NVFP4 quantization of a bf16 tensor x[rows, cols]: per
+ * 16-element block a scale = block amax / 6 encoded to E4M3 under the FP32
+ * outer scale, and every element rounded to the E2M1 grid ("End-to-End 4-Bit
+ * Training", Low-precision formats on Blackwell; "UE5M3" blog, 数学推导 for
+ * the UE5M3 scale); Four-Over-Six also encodes the block with its max
+ * mapped to 4 and keeps the lower-error result ("Four Over Six" notes,
+ * Method; gist.science summary, Methodologie); stochastic rounding for
+ * gradients ("UE5M3" blog, 数学推导; "End-to-End 4-Bit Training",
+ * Re-quantization with stochastic rounding); column-wise blocks for the
+ * transposed operand ("End-to-End 4-Bit Training", Block-scaled backward
+ * passes).  Fields of *args:
+ *   amax            the tensor amax A (fresh from nvfp4_tensor_amax, or a
+ *                   stale/periodic value, "UE5M3" blog, 数学推导).  The outer
  *                   scale is alpha = A / (6 * global_fp8_max) in binary32
  *                   (alpha = 1 if A = 0).
- *   global_fp8_max  S_g > 0, or 0 for the default: 448 (E4M3, max->6 and
- *                   the sweep), 256 (E4M3, the Four-Over-Six rules), 114688
- *                   (UE5M3).
- *   scale_fmt       NVFP4_SCALE_E4M3 or NVFP4_SCALE_UE5M3.
- *   select          an NVFP4_SELECT_* rule (below).
- *   rounding        NVFP4_ROUND_RNE or NVFP4_ROUND_SR (requires SELECT_6).
- *   axes            NVFP4_AXIS_ROW, NVFP4_AXIS_COL or both.
- *   seed            stochastic rounding only: the variate of the element at
- *                   index i of the OUTPUT orientation (r*cols + c row-wise,
- *                   c*rows + r column-wise) is the counter hash of (seed, i).
- *   codes, scales   ROW outputs: [rows, cols/2] and [rows, cols/16] bytes.
- *   codes_t, scales_t  COL outputs: [cols, rows/2] and [cols, rows/16].
- *   count4          optional device counter; += number of blocks (all axes)
- *                   that chose max->4.  The caller clears it.
+ *   global_fp8_max  0 selects the default: 448 (E4M3, max->6 and the
+ *                   sweep), 256 (E4M3, the Four-Over-Six rules; gist.science
+ *                   summary, Implementatiedetails), 114688 (UE5M3).
+ *   seed            the variate of the element at index i of the OUTPUT
+ *                   orientation (r*cols + c row-wise, c*rows + r column-wise)
+ *                   is the counter hash of (seed, i).
+ *   count4          += number of blocks (all axes) that chose max->4; the
+ *                   caller clears it.  Needs workspace.
  * Per block (binary32, in this order): a = max|x_i|; for Q in {6, 4}:
  * s_raw = a * K_Q with K_Q = 1/(Q*alpha); code = nearest scale code (ties to
  * even, saturating); y_i = x_i * (1/(D[code]*alpha)); E2M1 code of y_i (RNE,
@@ -130,45 +177,51 @@ int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* s
  * additions), SELECT_4OVER6_MAXERR the largest |d_i|.  SELECT_SWEEP encodes
  * the block with every finite scale code (ascending) and keeps the one with
  * the strictly smallest SSE (ties keep the smaller code): the MSE scale sweep
- * that initializes scale learning; it does not touch count4.
+ * that initializes scale learning ("Scale Learning" blog); it does not touch
+ * count4.
  * A negative or non-finite *amax: every scale byte = the NaN code (0x7F E4M3,
  * 0xFF UE5M3), every element code 0.  A NaN element with a usable amax: same
  * for its block.
- * Errors (NVFP4_ERR_INVALID): x/amax NULL; rows or cols < 0; ROW with
- * cols % 16 != 0 or codes/scales NULL; COL with rows % 16 != 0 or
+ * Errors (NVFP4_ERR_INVALID): args, x or amax NULL; rows or cols < 0; ROW
+ * with cols % 16 != 0 or codes/scales NULL; COL with rows % 16 != 0 or
  * codes_t/scales_t NULL; unknown enum; axes == 0; SR with any select but
- * SELECT_6;
- * global_fp8_max negative or non-finite; misaligned pointers.
- * rows == 0 or cols == 0: nothing to do, NVFP4_OK.
+ * SELECT_6; global_fp8_max negative or non-finite; count4 without workspace;
+ * misaligned pointers.  rows == 0 or cols == 0: nothing to do, NVFP4_OK.
  */
-int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                   float global_fp8_max, int scale_fmt, int select, int rounding, int axes,
-                   uint64_t seed, uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
-                   uint8_t* scales_t, unsigned long long* count4, void* stream);
+int nvfp4_quantize(const nvfp4_quant_args* args, hipStream_t stream);
 
 /*
  * nvfp4_dequantize -- x_hat = q * D[scale code] * alpha, correctly rounded
- * to binary32 ("End-to-End 4-Bit Training", "Low-precision formats on
- * Blackwell"); a NaN scale code gives NaN.
+ * to binary32: the FP4 value times the FP8 block scale times the FP32 outer
+ * scale ("End-to-End 4-Bit Training", Low-precision formats on Blackwell);
+ * a NaN scale code gives NaN.  Optionally, in the same pass, the squared
+ * error against the original tensor, whose mean is the per-tensor MSE and
+ * whose square root over ||x|| is the relative error the "UE5M3" blog
+ * suggests monitoring (调试指南).
  *   codes, scales   [rows, cols/2], [rows, cols/16] as nvfp4_quantize writes.
- *   amax, global_fp8_max, scale_fmt   as given to nvfp4_quantize (here
- *                   global_fp8_max must be > 0: the value actually used).
+ *   amax, global_fp8_max, scale_fmt   as given to nvfp4_quantize; here
+ *                   global_fp8_max must be > 0 (the value actually used:
+ *                   its default depends on the selection rule, which a
+ *                   dequantization does not know).
  *   out_f32         optional [rows, cols] float.
  *   out_bf16        optional [rows, cols] bf16: round-to-nearest-even of the
  *                   binary32 value.
  *   block_scale_out optional [rows, cols/16] float: D * alpha per block (the
  *                   binary32 effective scale; the scale-learning init).
  *   x_ref, sse_out  optional pair: x_ref [rows, cols] bf16 input; *sse_out
- *                   (device double) += sum (x - x_hat)^2 in binary64.  The
- *                   caller clears *sse_out.  Per-tensor MSE = SSE / numel.
+ *                   (device double) = sum (x - x_hat)^2, the residual and
+ *                   the sum in binary64, combined in a fixed order (the same
+ *                   on every run).  Needs workspace.
+ *   workspace       required with sse_out (see above), else unused.
  * Errors (NVFP4_ERR_INVALID): codes/scales/amax NULL; rows or cols < 0;
  * cols % 16 != 0; unknown format; global_fp8_max <= 0 or non-finite; exactly
- * one of x_ref / sse_out given; misaligned pointers.
+ * one of x_ref / sse_out given; sse_out without workspace; misaligned
+ * pointers.
  */
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      const float* amax, float global_fp8_max, int scale_fmt, float* out_f32,
                      uint16_t* out_bf16, float* block_scale_out, const uint16_t* x_ref,
-                     double* sse_out, void* stream);
+                     double* sse_out, void* workspace, hipStream_t stream);
 
 /*
  * nvfp4_fakequant_fwd -- scale-learning fake quantization ("Scale Learning",
@@ -183,7 +236,7 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
  * pointers -> NVFP4_ERR_INVALID.
  */
 int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
-                        const float* s_post, float* xq_out, void* stream);
+                        const float* s_post, float* xq_out, hipStream_t stream);
 
 /*
  * nvfp4_fakequant_bwd -- straight-through backward of nvfp4_fakequant_fwd
@@ -208,7 +261,7 @@ int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const flo
  */
 int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
                         const float* s_pre, const float* s_post, float* grad_x,
-                        float* grad_s_pre, float* grad_s_post, void* stream);
+                        float* grad_s_pre, float* grad_s_post, hipStream_t stream);
 
 /*
  * nvfp4_fakequant_fwd_amax / nvfp4_fakequant_bwd_amax -- the same with the
@@ -221,10 +274,10 @@ int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, i
  * nvfp4_fakequant_fwd / nvfp4_fakequant_bwd with a_* in place of s_*.
  */
 int nvfp4_fakequant_fwd_amax(const uint16_t* x, int64_t rows, int64_t cols, const float* a_pre,
-                             const float* a_post, float* xq_out, void* stream);
+                             const float* a_post, float* xq_out, hipStream_t stream);
 int nvfp4_fakequant_bwd_amax(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
                              const float* a_pre, const float* a_post, float* grad_x,
-                             float* grad_a_pre, float* grad_a_post, void* stream);
+                             float* grad_a_pre, float* grad_a_post, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * Per-row outer scales ("End-to-End 4-Bit Training", Recipe details:
@@ -242,21 +295,19 @@ int nvfp4_fakequant_bwd_amax(const uint16_t* x, const float* grad_xq, int64_t ro
  * Errors: NULL pointers with rows > 0, misalignment, cols % 16 != 0 ->
  * NVFP4_ERR_INVALID.
  */
-int nvfp4_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* row_amax, void* stream);
+int nvfp4_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* row_amax, hipStream_t stream);
 
 /*
  * nvfp4_quantize_rowscaled -- row-wise NVFP4 quantization with per-row
  * outer scales (as nvfp4_quantize with axes = ROW, A_r in place of A).
- *   row_amax  [rows] float on the device (from nvfp4_row_amax, or stale).
- *   Other arguments and errors as nvfp4_quantize; codes / scales / count4 as
- *   there.  A row whose amax is negative or non-finite gets the NaN scale
- *   code in every block and element code 0.  SR uses the row-major element
- *   index r * cols + c.
+ *   args->amax  [rows] float on the device (from nvfp4_row_amax, or stale).
+ *   args->axes  must be NVFP4_AXIS_ROW.
+ *   Other fields and errors as nvfp4_quantize; codes / scales / count4 /
+ *   workspace as there.  A row whose amax is negative or non-finite gets the
+ *   NaN scale code in every block and element code 0.  SR uses the
+ *   row-major element index r * cols + c.
  */
-int nvfp4_quantize_rowscaled(const uint16_t* x, int64_t rows, int64_t cols, const float* row_amax,
-                             float global_fp8_max, int scale_fmt, int select, int rounding,
-                             uint64_t seed, uint8_t* codes, uint8_t* scales,
-                             unsigned long long* count4, void* stream);
+int nvfp4_quantize_rowscaled(const nvfp4_quant_args* args, hipStream_t stream);
 
 /*
  * nvfp4_dequantize_rowscaled -- nvfp4_dequantize with per-row outer scales:
@@ -267,7 +318,7 @@ int nvfp4_dequantize_rowscaled(const uint8_t* codes, const uint8_t* scales, int6
                                int64_t cols, const float* row_amax, float global_fp8_max,
                                int scale_fmt, float* out_f32, uint16_t* out_bf16,
                                float* block_scale_out, const uint16_t* x_ref, double* sse_out,
-                               void* stream);
+                               void* workspace, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * nvfp4_quantize_2d -- 16x16 tile scales ("End-to-End 4-Bit Training",
@@ -275,21 +326,22 @@ int nvfp4_dequantize_rowscaled(const uint8_t* codes, const uint8_t* scales, int6
  * the tile's amax, shared by the tile's 16 row blocks and 16 column blocks,
  * so the column-wise codes are bit for bit the transpose of the row-wise ones.
  * Max->6 and round-to-nearest-even (the weights path).  Per-tensor outer
- * scale from *amax as in nvfp4_quantize.
+ * scale from args->amax as in nvfp4_quantize.  Fields of *args:
  *   x          [rows, cols] bf16, rows % 16 == 0, cols % 16 == 0.
+ *   select, rounding  must be NVFP4_SELECT_6 and NVFP4_ROUND_RNE.
+ *   axes       NVFP4_AXIS_ROW, or ROW | COL for the transposed layout too.
  *   codes      [rows, cols/2], scales [rows, cols/16] (every row block holds
  *              its tile's code); 16- and 4-byte aligned.
- *   codes_t    [cols, rows/2], scales_t [cols, rows/16]: the layout of X^T;
- *              both NULL to skip, else codes_t 16-byte aligned.
+ *   codes_t    [cols, rows/2], scales_t [cols, rows/16]: the layout of X^T
+ *              (with COL); codes_t 16-byte aligned.
+ *   count4, workspace  unused.
  * NaN rules: a non-finite or negative amax -> NaN scale code everywhere and
  * codes 0; a tile holding a NaN element -> its scale is the NaN code and its
  * codes 0.
  * Errors: NULL / misaligned outputs, shape not a multiple of 16, unknown
- * scale_fmt, only one of codes_t / scales_t -> NVFP4_ERR_INVALID.
+ * scale_fmt, another select / rounding, axes without ROW -> NVFP4_ERR_INVALID.
  */
-int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                      float global_fp8_max, int scale_fmt, uint8_t* codes, uint8_t* scales,
-                      uint8_t* codes_t, uint8_t* scales_t, void* stream);
+int nvfp4_quantize_2d(const nvfp4_quant_args* args, hipStream_t stream);
 
 /*
  * Re-quantization for the backward pass ("End-to-End 4-Bit Training",
@@ -311,14 +363,15 @@ enum { NVFP4_TARGET_NVFP4 = 0, NVFP4_TARGET_MXFP8 = 1 };
 /*
  * nvfp4_dequantized_amax -- *amax_out = max |x_hat| over the tensor (the
  * current amax of the dequantized tensor, for the outer scale of an NVFP4
- * re-quantization); NaN if any x_hat is NaN.  amax_out 4-byte aligned.
+ * re-quantization); NaN if any x_hat is NaN.  amax_out 4-byte aligned;
+ * workspace as for nvfp4_tensor_amax.  One launch.
  * Errors: NULL or misaligned pointers, both or neither of amax / row_amax,
  * cols % 16 != 0, unknown scale_fmt, global_fp8_max not > 0 ->
  * NVFP4_ERR_INVALID.
  */
 int nvfp4_dequantized_amax(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                            const float* amax, const float* row_amax, float global_fp8_max,
-                           int scale_fmt, float* amax_out, void* stream);
+                           int scale_fmt, float* amax_out, void* workspace, hipStream_t stream);
 
 /*
  * nvfp4_requantize_t -- quantize X_hat^T ([cols, rows], row-major) with
@@ -349,7 +402,7 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows
                        const float* amax, const float* row_amax, float global_fp8_max,
                        int scale_fmt, int target, const float* dst_amax, float dst_global_fp8_max,
                        int dst_scale_fmt, uint64_t seed, uint8_t* out_t, uint8_t* out_scales_t,
-                       void* stream);
+                       hipStream_t stream);
 
 /*
  * 16-point random Hadamard transform around quantization ("Four Over Six"
@@ -368,12 +421,13 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows
  * nvfp4_rht_amax -- *amax_out = max |y| over the transformed tensor (the
  * outer amax for nvfp4_quantize_rht; NaN if any element is NaN).  x [rows,
  * cols] bf16; ROW: cols % 16 == 0, x 16-byte aligned; COL: rows % 16 == 0.
+ * workspace as for nvfp4_tensor_amax.  One launch.
  *
  * nvfp4_quantize_rht -- nvfp4_quantize of the transformed tensor, along one
- * axis: ROW writes codes [rows, cols/2] and scales [rows, cols/16]; COL
- * writes the column-wise layout (of the transpose), codes [cols, rows/2] and
- * scales [cols, rows/16].  amax, global_fp8_max, scale_fmt, select,
- * rounding, seed and count4 as nvfp4_quantize (SR indices in the output
+ * axis (args->axes = NVFP4_AXIS_ROW or NVFP4_AXIS_COL, not both): ROW writes
+ * codes [rows, cols/2] and scales [rows, cols/16]; COL writes the column-wise
+ * layout (of the transpose) into codes_t [cols, rows/2] and scales_t [cols,
+ * rows/16].  Other fields as nvfp4_quantize (SR indices in the output
  * orientation).
  *
  * nvfp4_dequantize_rht -- x_hat of an NVFP4 tensor [rows, cols] (as
@@ -385,14 +439,11 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows
  * NVFP4_ERR_INVALID.
  */
 int nvfp4_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint64_t sign_seed,
-                   float* amax_out, void* stream);
-int nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                       float global_fp8_max, int scale_fmt, int select, int rounding, int axis,
-                       uint64_t seed, uint64_t sign_seed, uint8_t* codes, uint8_t* scales,
-                       unsigned long long* count4, void* stream);
+                   float* amax_out, void* workspace, hipStream_t stream);
+int nvfp4_quantize_rht(const nvfp4_quant_args* args, uint64_t sign_seed, hipStream_t stream);
 int nvfp4_dequantize_rht(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                          const float* amax, float global_fp8_max, int scale_fmt,
-                         uint64_t sign_seed, float* out_f32, void* stream);
+                         uint64_t sign_seed, float* out_f32, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(int status);

@@ -7,9 +7,9 @@ does not load the library; the first call does, and raises if it is not built.
 from .api import (Quantized, default_global_max, dequantize, dequantize_rowscaled,
                   dequantize_rht, dequantized_amax, fakequant_bwd, fakequant_fwd, quantize,
                   quantize_2d, quantize_rht, quantize_rowscaled, requantize_t, rht_amax, row_amax,
-                  tensor_amax)
+                  tensor_amax, workspace)
 
 __all__ = ["Quantized", "default_global_max", "dequantize", "dequantize_rowscaled",
            "dequantize_rht", "dequantized_amax", "fakequant_bwd", "fakequant_fwd", "quantize",
            "quantize_2d", "quantize_rht", "quantize_rowscaled", "requantize_t", "rht_amax",
-           "row_amax", "tensor_amax"]
+           "row_amax", "tensor_amax", "workspace"]

@@ -4,20 +4,15 @@
 // HBM-bound (2 bytes read per element).  One 1024-thread workgroup per CU;
 // each lane streams 16-byte chunks with non-temporal loads, four in flight,
 // folding them with packed 16-bit integer max on the sign-cleared patterns
-// (integer order = magnitude order; NaN > inf > finite).  The workgroup
-// reduces through cross-lane shuffles and LDS, and at most one integer
-// atomicMax per workgroup lands the result as the float whose bits are
-// (pattern << 16): same-address atomics (and coherent reads) serialize, at
-// several nanoseconds each on MI355X, so the grid is kept to one workgroup
-// per CU.  A one-lane kernel clears the result first.
+// (integer order = magnitude order; NaN > inf > finite).  The workgroups'
+// maxima meet in the caller's workspace (grid_reduce.hpp): the last
+// workgroup to finish writes the float whose bits are (pattern << 16).  One
+// launch, nothing to clear beforehand.
 #include "common.hpp"
 #include "device.hpp"
+#include "grid_reduce.hpp"
 
 namespace nvfp4 {
-
-__global__ void __launch_bounds__(64) amax_init_kernel(uint32_t* out) {
-  if (threadIdx.x == 0) out[0] = 0u;
-}
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   // butterfly over the 64 lanes with ds_swizzle-free cross-lane moves
@@ -33,7 +28,8 @@ constexpr int kAmaxThreads = 1024;
 
 __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const uint4* __restrict__ x, int64_t nchunks,
                                                         const uint16_t* __restrict__ tail,
-                                                        int ntail, uint32_t* out) {
+                                                        int ntail, float* __restrict__ out,
+                                                        uint8_t* __restrict__ ws) {
   uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
   int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
@@ -56,20 +52,8 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const uint4* __restr
     uint32_t v = tail[threadIdx.x] & 0x7FFFu;
     m = m > v ? m : v;
   }
-  m = wave_max_u32(m);
-  __shared__ uint32_t red[kAmaxThreads / 64];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-    for (int w2 = 1; w2 < kAmaxThreads / 64; ++w2) r = r > red[w2] ? r : red[w2];
-    // The running maximum only grows, so a workgroup whose maximum it
-    // already covers skips its atomic; the coherent read costs less than a
-    // same-address atomic.  A stale read is smaller and only costs the atomic.
-    const uint32_t cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((r << 16) > cur) atomicMax(out, r << 16);
-  }
+  uint32_t r;
+  if (grid_reduce<MaxU32, kAmaxThreads>(ws, m, &r)) out[0] = __uint_as_float(r << 16);
 }
 
 // Per-row amax (per-token outer scales, "End-to-End 4-Bit Training", Recipe
@@ -116,19 +100,18 @@ hipError_t launch_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float*
   return hipGetLastError();
 }
 
-hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipStream_t s) {
-  uint32_t* o = reinterpret_cast<uint32_t*>(out);
-  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(64), 0, s, o);
-  if (numel == 0) return hipGetLastError();
+hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, uint8_t* ws,
+                              hipStream_t s) {
   const int64_t nchunks = numel / kChunk;
   const int ntail = (int)(numel - nchunks * kChunk);
-  // one workgroup per CU (fewer if the tensor is small)
+  // one workgroup per CU (fewer if the tensor is small); an empty tensor
+  // runs one workgroup, which writes 0
   const int64_t want = (nchunks + (int64_t)kAmaxThreads * kAmaxUnroll - 1) / ((int64_t)kAmaxThreads * kAmaxUnroll);
-  const int64_t cap = (int64_t)device_cu_count();
+  const int64_t cap = (int64_t)device_cu_count() < kSlots ? (int64_t)device_cu_count() : kSlots;
   int64_t grid = want < cap ? want : cap;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(kAmaxThreads), 0, s,
-                     reinterpret_cast<const uint4*>(x), nchunks, x + nchunks * kChunk, ntail, o);
+                     reinterpret_cast<const uint4*>(x), nchunks, x + nchunks * kChunk, ntail, out, ws);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 #include "../../include/nvfp4_testing.h"
 #include "common.hpp"
 #include "device.hpp"
+#include "grid_reduce.hpp"
 
 namespace nvfp4 {
 
@@ -105,6 +106,10 @@ const char* nvfp4_status_string(int status) {
   }
 }
 
+static_assert(NVFP4_WORKSPACE_BYTES == kWorkspaceBytes, "header and kernels agree on the workspace");
+
+size_t nvfp4_workspace_bytes(void) { return kWorkspaceBytes; }
+
 static float resolve_sg(float global_fp8_max, int scale_fmt, int select) {
   if (global_fp8_max != 0.0f) return global_fp8_max;
   if (scale_fmt == NVFP4_SCALE_UE5M3) return NVFP4_GLOBAL_MAX_UE5M3;
@@ -112,137 +117,146 @@ static float resolve_sg(float global_fp8_max, int scale_fmt, int select) {
              ? NVFP4_GLOBAL_MAX_E4M3_4OVER6 : NVFP4_GLOBAL_MAX_E4M3;
 }
 
-int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* stream) {
-  if (numel < 0 || !amax_out) return NVFP4_ERR_INVALID;
+static bool ws_ok(const void* ws) { return ws != nullptr && aligned16(ws); }
+
+int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* workspace,
+                      hipStream_t stream) {
+  if (numel < 0 || !amax_out || !ws_ok(workspace)) return NVFP4_ERR_INVALID;
   if (numel > 0 && (!x || !aligned16(x))) return NVFP4_ERR_INVALID;
   if (((uintptr_t)amax_out & 3u) != 0) return NVFP4_ERR_INVALID;
-  return status_of(launch_tensor_amax(x, numel, amax_out, (hipStream_t)stream));
+  return status_of(launch_tensor_amax(x, numel, amax_out, static_cast<uint8_t*>(workspace), stream));
 }
 
-int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                   float global_fp8_max, int scale_fmt, int select, int rounding, int axes,
-                   uint64_t seed, uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
-                   uint8_t* scales_t, unsigned long long* count4, void* stream) {
-  if (!x || !amax || !size_ok(rows, cols)) return NVFP4_ERR_INVALID;
-  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (select < NVFP4_SELECT_6 || select > NVFP4_SELECT_SWEEP) return NVFP4_ERR_INVALID;
-  if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
-  if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
-  if (axes != NVFP4_AXIS_ROW && axes != NVFP4_AXIS_COL && axes != (NVFP4_AXIS_ROW | NVFP4_AXIS_COL))
+// Checks shared by the quantize calls; fills the kernel-side arguments.
+static int quant_common(const nvfp4_quant_args* p, QuantizeArgs& a) {
+  if (!p || !p->x || !p->amax || !size_ok(p->rows, p->cols)) return NVFP4_ERR_INVALID;
+  if (p->scale_fmt != NVFP4_SCALE_E4M3 && p->scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (p->select < NVFP4_SELECT_6 || p->select > NVFP4_SELECT_SWEEP) return NVFP4_ERR_INVALID;
+  if (p->rounding != NVFP4_ROUND_RNE && p->rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
+  if (p->rounding == NVFP4_ROUND_SR && p->select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
+  if (p->axes != NVFP4_AXIS_ROW && p->axes != NVFP4_AXIS_COL &&
+      p->axes != (NVFP4_AXIS_ROW | NVFP4_AXIS_COL))
     return NVFP4_ERR_INVALID;
-  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
-  if (axes & NVFP4_AXIS_ROW) {
-    if (cols % 16 != 0 || !codes || !scales || !aligned16(codes) || ((uintptr_t)scales & 3u))
+  if (!(p->global_fp8_max >= 0.0f) || isinf(p->global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (p->axes & NVFP4_AXIS_ROW) {
+    if (p->cols % 16 != 0 || !p->codes || !p->scales || !aligned16(p->codes) ||
+        ((uintptr_t)p->scales & 3u))
       return NVFP4_ERR_INVALID;
   }
-  if (axes & NVFP4_AXIS_COL) {
-    if (rows % 16 != 0 || cols % 8 != 0 || !codes_t || !scales_t || !aligned16(codes_t))
+  if (p->axes & NVFP4_AXIS_COL) {
+    if (p->rows % 16 != 0 || p->cols % 8 != 0 || !p->codes_t || !p->scales_t || !aligned16(p->codes_t))
       return NVFP4_ERR_INVALID;
   }
-  if (!aligned16(x) || ((uintptr_t)amax & 3u) || ((uintptr_t)count4 & 7u)) return NVFP4_ERR_INVALID;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!aligned16(p->x) || ((uintptr_t)p->amax & 3u) || ((uintptr_t)p->count4 & 7u))
+    return NVFP4_ERR_INVALID;
+  if (p->count4 && !ws_ok(p->workspace)) return NVFP4_ERR_INVALID;
+  a.x = p->x; a.rows = p->rows; a.cols = p->cols; a.amax = p->amax;
+  a.sg = resolve_sg(p->global_fp8_max, p->scale_fmt, p->select);
+  a.fmt = p->scale_fmt; a.select = p->select; a.rounding = p->rounding; a.axes = p->axes;
+  a.seed = p->seed;
+  a.codes = (p->axes & NVFP4_AXIS_ROW) ? p->codes : nullptr;
+  a.scales = (p->axes & NVFP4_AXIS_ROW) ? p->scales : nullptr;
+  a.codes_t = (p->axes & NVFP4_AXIS_COL) ? p->codes_t : nullptr;
+  a.scales_t = (p->axes & NVFP4_AXIS_COL) ? p->scales_t : nullptr;
+  a.count4 = p->count4;
+  a.ws = p->count4 ? static_cast<uint8_t*>(p->workspace) : nullptr;
+  return NVFP4_OK;
+}
+
+int nvfp4_quantize(const nvfp4_quant_args* args, hipStream_t stream) {
   QuantizeArgs a;
-  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax;
-  a.sg = resolve_sg(global_fp8_max, scale_fmt, select);
-  a.fmt = scale_fmt; a.select = select; a.rounding = rounding; a.axes = axes; a.seed = seed;
-  a.codes = codes; a.scales = scales; a.codes_t = codes_t; a.scales_t = scales_t;
-  a.count4 = count4;
-  return status_of(launch_quantize(a, (hipStream_t)stream));
+  const int st = quant_common(args, a);
+  if (st != NVFP4_OK) return st;
+  if (a.rows == 0 || a.cols == 0) return NVFP4_OK;
+  return status_of(launch_quantize(a, stream));
+}
+
+static int dq_common(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     const float* amax, float global_fp8_max, int scale_fmt, float* out_f32,
+                     uint16_t* out_bf16, float* block_scale_out, const uint16_t* x_ref,
+                     double* sse_out, void* workspace, bool row_scaled, DequantizeArgs& a) {
+  if (!codes || !scales || !amax || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
+  if ((x_ref == nullptr) != (sse_out == nullptr)) return NVFP4_ERR_INVALID;
+  if (sse_out && !ws_ok(workspace)) return NVFP4_ERR_INVALID;
+  if (!aligned16(codes) || !aligned16(out_f32) || !aligned16(out_bf16) || !aligned16(x_ref))
+    return NVFP4_ERR_INVALID;
+  if (((uintptr_t)amax & 3u) || ((uintptr_t)block_scale_out & 3u) || ((uintptr_t)sse_out & 7u))
+    return NVFP4_ERR_INVALID;
+  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = amax;
+  a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32; a.out_bf16 = out_bf16;
+  a.block_scale = block_scale_out; a.x_ref = x_ref; a.sse = sse_out;
+  a.ws = sse_out ? static_cast<uint8_t*>(workspace) : nullptr; a.row_scaled = row_scaled;
+  return NVFP4_OK;
 }
 
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      const float* amax, float global_fp8_max, int scale_fmt, float* out_f32,
                      uint16_t* out_bf16, float* block_scale_out, const uint16_t* x_ref,
-                     double* sse_out, void* stream) {
-  if (!codes || !scales || !amax || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
-  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
-  if ((x_ref == nullptr) != (sse_out == nullptr)) return NVFP4_ERR_INVALID;
-  if (!aligned16(codes) || !aligned16(out_f32) || !aligned16(out_bf16) || !aligned16(x_ref))
-    return NVFP4_ERR_INVALID;
-  if (((uintptr_t)amax & 3u) || ((uintptr_t)block_scale_out & 3u) || ((uintptr_t)sse_out & 7u))
-    return NVFP4_ERR_INVALID;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
+                     double* sse_out, void* workspace, hipStream_t stream) {
   DequantizeArgs a;
-  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = amax;
-  a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32; a.out_bf16 = out_bf16;
-  a.block_scale = block_scale_out; a.x_ref = x_ref; a.sse = sse_out; a.row_scaled = false;
-  return status_of(launch_dequantize(a, (hipStream_t)stream));
+  const int st = dq_common(codes, scales, rows, cols, amax, global_fp8_max, scale_fmt, out_f32,
+                           out_bf16, block_scale_out, x_ref, sse_out, workspace, false, a);
+  if (st != NVFP4_OK) return st;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  return status_of(launch_dequantize(a, stream));
 }
 
-int nvfp4_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* row_amax, void* stream) {
+int nvfp4_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* row_amax, hipStream_t stream) {
   if (!size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
   if (rows > 0 && (!x || !row_amax || !aligned16(x) || ((uintptr_t)row_amax & 3u)))
     return NVFP4_ERR_INVALID;
   if (rows == 0) return NVFP4_OK;
-  return status_of(launch_row_amax(x, rows, cols, row_amax, (hipStream_t)stream));
+  return status_of(launch_row_amax(x, rows, cols, row_amax, stream));
 }
 
-int nvfp4_quantize_rowscaled(const uint16_t* x, int64_t rows, int64_t cols, const float* row_amax,
-                             float global_fp8_max, int scale_fmt, int select, int rounding,
-                             uint64_t seed, uint8_t* codes, uint8_t* scales,
-                             unsigned long long* count4, void* stream) {
-  if (!x || !row_amax || !size_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_INVALID;
-  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (select < NVFP4_SELECT_6 || select > NVFP4_SELECT_SWEEP) return NVFP4_ERR_INVALID;
-  if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
-  if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
-  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
-  if (!codes || !scales || !aligned16(codes) || ((uintptr_t)scales & 3u)) return NVFP4_ERR_INVALID;
-  if (!aligned16(x) || ((uintptr_t)row_amax & 3u) || ((uintptr_t)count4 & 7u))
-    return NVFP4_ERR_INVALID;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
+int nvfp4_quantize_rowscaled(const nvfp4_quant_args* args, hipStream_t stream) {
+  if (!args || args->axes != NVFP4_AXIS_ROW) return NVFP4_ERR_INVALID;
   QuantizeArgs a;
-  a.x = x; a.rows = rows; a.cols = cols; a.amax = row_amax;
-  a.sg = resolve_sg(global_fp8_max, scale_fmt, select);
-  a.fmt = scale_fmt; a.select = select; a.rounding = rounding; a.axes = AXIS_ROW; a.seed = seed;
-  a.codes = codes; a.scales = scales; a.codes_t = nullptr; a.scales_t = nullptr;
-  a.count4 = count4;
-  return status_of(launch_quantize_rowscaled(a, (hipStream_t)stream));
+  const int st = quant_common(args, a);
+  if (st != NVFP4_OK) return st;
+  if (a.rows == 0 || a.cols == 0) return NVFP4_OK;
+  return status_of(launch_quantize_rowscaled(a, stream));
 }
 
 int nvfp4_dequantize_rowscaled(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                int64_t cols, const float* row_amax, float global_fp8_max,
                                int scale_fmt, float* out_f32, uint16_t* out_bf16,
                                float* block_scale_out, const uint16_t* x_ref, double* sse_out,
-                               void* stream) {
-  if (!codes || !scales || !row_amax || !size_ok(rows, cols) || cols % 16 != 0)
-    return NVFP4_ERR_INVALID;
-  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (!(global_fp8_max > 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
-  if ((x_ref == nullptr) != (sse_out == nullptr)) return NVFP4_ERR_INVALID;
-  if (!aligned16(codes) || !aligned16(out_f32) || !aligned16(out_bf16) || !aligned16(x_ref))
-    return NVFP4_ERR_INVALID;
-  if (((uintptr_t)row_amax & 3u) || ((uintptr_t)block_scale_out & 3u) || ((uintptr_t)sse_out & 7u))
-    return NVFP4_ERR_INVALID;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
+                               void* workspace, hipStream_t stream) {
   DequantizeArgs a;
-  a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = row_amax;
-  a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32; a.out_bf16 = out_bf16;
-  a.block_scale = block_scale_out; a.x_ref = x_ref; a.sse = sse_out; a.row_scaled = true;
-  return status_of(launch_dequantize(a, (hipStream_t)stream));
+  const int st = dq_common(codes, scales, rows, cols, row_amax, global_fp8_max, scale_fmt, out_f32,
+                           out_bf16, block_scale_out, x_ref, sse_out, workspace, true, a);
+  if (st != NVFP4_OK) return st;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  return status_of(launch_dequantize(a, stream));
 }
 
-int nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                      float global_fp8_max, int scale_fmt, uint8_t* codes, uint8_t* scales,
-                      uint8_t* codes_t, uint8_t* scales_t, void* stream) {
-  if (!x || !amax || !size_ok(rows, cols) || rows % 16 != 0 || cols % 16 != 0)
+int nvfp4_quantize_2d(const nvfp4_quant_args* args, hipStream_t stream) {
+  if (!args) return NVFP4_ERR_INVALID;
+  const nvfp4_quant_args* p = args;
+  if (!p->x || !p->amax || !size_ok(p->rows, p->cols) || p->rows % 16 != 0 || p->cols % 16 != 0)
     return NVFP4_ERR_INVALID;
-  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
-  if (!codes || !scales || !aligned16(codes) || ((uintptr_t)scales & 3u)) return NVFP4_ERR_INVALID;
-  if ((codes_t == nullptr) != (scales_t == nullptr)) return NVFP4_ERR_INVALID;
-  if (codes_t && !aligned16(codes_t)) return NVFP4_ERR_INVALID;
-  if (!aligned16(x) || ((uintptr_t)amax & 3u)) return NVFP4_ERR_INVALID;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (p->scale_fmt != NVFP4_SCALE_E4M3 && p->scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
+  if (p->select != NVFP4_SELECT_6 || p->rounding != NVFP4_ROUND_RNE) return NVFP4_ERR_INVALID;
+  if (p->axes != NVFP4_AXIS_ROW && p->axes != (NVFP4_AXIS_ROW | NVFP4_AXIS_COL)) return NVFP4_ERR_INVALID;
+  if (!(p->global_fp8_max >= 0.0f) || isinf(p->global_fp8_max)) return NVFP4_ERR_INVALID;
+  if (!p->codes || !p->scales || !aligned16(p->codes) || ((uintptr_t)p->scales & 3u))
+    return NVFP4_ERR_INVALID;
+  const bool both = p->axes & NVFP4_AXIS_COL;
+  if (both && (!p->codes_t || !p->scales_t || !aligned16(p->codes_t))) return NVFP4_ERR_INVALID;
+  if (!aligned16(p->x) || ((uintptr_t)p->amax & 3u)) return NVFP4_ERR_INVALID;
+  if (p->rows == 0 || p->cols == 0) return NVFP4_OK;
   QuantizeArgs a;
-  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax;
-  a.sg = resolve_sg(global_fp8_max, scale_fmt, NVFP4_SELECT_6);
-  a.fmt = scale_fmt; a.select = SELECT_6; a.rounding = ROUND_RNE;
-  a.axes = codes_t ? (AXIS_ROW | AXIS_COL) : AXIS_ROW; a.seed = 0;
-  a.codes = codes; a.scales = scales; a.codes_t = codes_t; a.scales_t = scales_t;
-  a.count4 = nullptr;
-  return status_of(launch_quantize_2d(a, (hipStream_t)stream));
+  a.x = p->x; a.rows = p->rows; a.cols = p->cols; a.amax = p->amax;
+  a.sg = resolve_sg(p->global_fp8_max, p->scale_fmt, NVFP4_SELECT_6);
+  a.fmt = p->scale_fmt; a.select = SELECT_6; a.rounding = ROUND_RNE;
+  a.axes = both ? (AXIS_ROW | AXIS_COL) : AXIS_ROW; a.seed = 0;
+  a.codes = p->codes; a.scales = p->scales;
+  a.codes_t = both ? p->codes_t : nullptr; a.scales_t = both ? p->scales_t : nullptr;
+  a.count4 = nullptr; a.ws = nullptr;
+  return status_of(launch_quantize_2d(a, stream));
 }
 
 static int rq_source(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
@@ -260,21 +274,21 @@ static int rq_source(const uint8_t* codes, const uint8_t* scales, int64_t rows, 
 
 int nvfp4_dequantized_amax(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                            const float* amax, const float* row_amax, float global_fp8_max,
-                           int scale_fmt, float* amax_out, void* stream) {
+                           int scale_fmt, float* amax_out, void* workspace, hipStream_t stream) {
   const int st = rq_source(codes, scales, rows, cols, amax, row_amax, global_fp8_max, scale_fmt);
   if (st != NVFP4_OK) return st;
-  if (!amax_out || ((uintptr_t)amax_out & 3u)) return NVFP4_ERR_INVALID;
+  if (!amax_out || ((uintptr_t)amax_out & 3u) || !ws_ok(workspace)) return NVFP4_ERR_INVALID;
   RequantArgs a = {};
   a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols;
   a.amax = amax; a.row_amax = row_amax; a.sg = global_fp8_max; a.fmt = scale_fmt;
-  return status_of(launch_dequantized_amax(a, amax_out, (hipStream_t)stream));
+  return status_of(launch_dequantized_amax(a, amax_out, static_cast<uint8_t*>(workspace), stream));
 }
 
 int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                        const float* amax, const float* row_amax, float global_fp8_max,
                        int scale_fmt, int target, const float* dst_amax, float dst_global_fp8_max,
                        int dst_scale_fmt, uint64_t seed, uint8_t* out_t, uint8_t* out_scales_t,
-                       void* stream) {
+                       hipStream_t stream) {
   const int st = rq_source(codes, scales, rows, cols, amax, row_amax, global_fp8_max, scale_fmt);
   if (st != NVFP4_OK) return st;
   if (!out_t || !out_scales_t || !aligned16(out_t)) return NVFP4_ERR_INVALID;
@@ -299,7 +313,7 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, int64_t rows
   } else {
     a.dst_amax = nullptr; a.dst_fmt = FMT_E4M3; a.dst_sg = 0.0f;
   }
-  return status_of(launch_requant_t(a, (hipStream_t)stream));
+  return status_of(launch_requant_t(a, stream));
 }
 
 // ---------------------------------------------------------------- random Hadamard transform
@@ -314,8 +328,9 @@ static uint32_t rht_signs(uint64_t sign_seed) {
 }
 
 int nvfp4_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint64_t sign_seed,
-                   float* amax_out, void* stream) {
+                   float* amax_out, void* workspace, hipStream_t stream) {
   if (!x || !amax_out || !size_ok(rows, cols) || ((uintptr_t)amax_out & 3u)) return NVFP4_ERR_INVALID;
+  if (!ws_ok(workspace)) return NVFP4_ERR_INVALID;
   if (axis == NVFP4_AXIS_ROW) {
     if (cols % 16 != 0 || !aligned16(x)) return NVFP4_ERR_INVALID;
   } else if (axis == NVFP4_AXIS_COL) {
@@ -324,45 +339,21 @@ int nvfp4_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint
     return NVFP4_ERR_INVALID;
   }
   return status_of(launch_rht_amax(x, rows, cols, axis, rht_signs(sign_seed), amax_out,
-                                   (hipStream_t)stream));
+                                   static_cast<uint8_t*>(workspace), stream));
 }
 
-int nvfp4_quantize_rht(const uint16_t* x, int64_t rows, int64_t cols, const float* amax,
-                       float global_fp8_max, int scale_fmt, int select, int rounding, int axis,
-                       uint64_t seed, uint64_t sign_seed, uint8_t* codes, uint8_t* scales,
-                       unsigned long long* count4, void* stream) {
-  if (!x || !amax || !codes || !scales || !size_ok(rows, cols)) return NVFP4_ERR_INVALID;
-  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
-  if (select < NVFP4_SELECT_6 || select > NVFP4_SELECT_SWEEP) return NVFP4_ERR_INVALID;
-  if (rounding != NVFP4_ROUND_RNE && rounding != NVFP4_ROUND_SR) return NVFP4_ERR_INVALID;
-  if (rounding == NVFP4_ROUND_SR && select != NVFP4_SELECT_6) return NVFP4_ERR_INVALID;
-  if (!(global_fp8_max >= 0.0f) || isinf(global_fp8_max)) return NVFP4_ERR_INVALID;
-  if (axis == NVFP4_AXIS_ROW) {
-    if (cols % 16 != 0) return NVFP4_ERR_INVALID;
-  } else if (axis == NVFP4_AXIS_COL) {
-    if (rows % 16 != 0 || cols % 8 != 0) return NVFP4_ERR_INVALID;
-  } else {
-    return NVFP4_ERR_INVALID;
-  }
-  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 3u) || ((uintptr_t)amax & 3u) ||
-      ((uintptr_t)count4 & 7u))
-    return NVFP4_ERR_INVALID;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
+int nvfp4_quantize_rht(const nvfp4_quant_args* args, uint64_t sign_seed, hipStream_t stream) {
+  if (!args || (args->axes != NVFP4_AXIS_ROW && args->axes != NVFP4_AXIS_COL)) return NVFP4_ERR_INVALID;
   QuantizeArgs a;
-  a.x = x; a.rows = rows; a.cols = cols; a.amax = amax;
-  a.sg = resolve_sg(global_fp8_max, scale_fmt, select);
-  a.fmt = scale_fmt; a.select = select; a.rounding = rounding; a.axes = axis; a.seed = seed;
-  a.codes = axis == NVFP4_AXIS_ROW ? codes : nullptr;
-  a.scales = axis == NVFP4_AXIS_ROW ? scales : nullptr;
-  a.codes_t = axis == NVFP4_AXIS_COL ? codes : nullptr;
-  a.scales_t = axis == NVFP4_AXIS_COL ? scales : nullptr;
-  a.count4 = count4;
-  return status_of(launch_quantize_rht(a, rht_signs(sign_seed), (hipStream_t)stream));
+  const int st = quant_common(args, a);
+  if (st != NVFP4_OK) return st;
+  if (a.rows == 0 || a.cols == 0) return NVFP4_OK;
+  return status_of(launch_quantize_rht(a, rht_signs(sign_seed), stream));
 }
 
 int nvfp4_dequantize_rht(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                          const float* amax, float global_fp8_max, int scale_fmt,
-                         uint64_t sign_seed, float* out_f32, void* stream) {
+                         uint64_t sign_seed, float* out_f32, hipStream_t stream) {
   if (!codes || !scales || !amax || !out_f32 || !size_ok(rows, cols) || cols % 16 != 0)
     return NVFP4_ERR_INVALID;
   if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
@@ -373,7 +364,7 @@ int nvfp4_dequantize_rht(const uint8_t* codes, const uint8_t* scales, int64_t ro
   DequantizeArgs a = {};
   a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols; a.amax = amax;
   a.sg = global_fp8_max; a.fmt = scale_fmt; a.out_f32 = out_f32;
-  return status_of(launch_dequantize_rht(a, rht_signs(sign_seed), (hipStream_t)stream));
+  return status_of(launch_dequantize_rht(a, rht_signs(sign_seed), stream));
 }
 
 static int fq_common(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre) {
@@ -383,7 +374,7 @@ static int fq_common(const uint16_t* x, int64_t rows, int64_t cols, const float*
 }
 
 static int fq_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
-                  const float* s_post, float* xq_out, bool amax_param, void* stream) {
+                  const float* s_post, float* xq_out, bool amax_param, hipStream_t stream) {
   int st = fq_common(x, rows, cols, s_pre);
   if (st != NVFP4_OK) return st;
   if (!xq_out || !aligned16(xq_out) || ((uintptr_t)s_post & 3u)) return NVFP4_ERR_INVALID;
@@ -391,12 +382,12 @@ static int fq_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_
   FakeQuantArgs a = {};
   a.x = x; a.rows = rows; a.cols = cols; a.s_pre = s_pre; a.s_post = s_post; a.xq = xq_out;
   a.amax_param = amax_param;
-  return status_of(launch_fakequant_fwd(a, (hipStream_t)stream));
+  return status_of(launch_fakequant_fwd(a, stream));
 }
 
 static int fq_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
                   const float* s_pre, const float* s_post, float* grad_x, float* grad_s_pre,
-                  float* grad_s_post, bool amax_param, void* stream) {
+                  float* grad_s_post, bool amax_param, hipStream_t stream) {
   int st = fq_common(x, rows, cols, s_pre);
   if (st != NVFP4_OK) return st;
   if (!grad_xq || !grad_x || !grad_s_pre) return NVFP4_ERR_INVALID;
@@ -408,77 +399,77 @@ static int fq_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t
   FakeQuantArgs a = {};
   a.x = x; a.g = grad_xq; a.rows = rows; a.cols = cols; a.s_pre = s_pre; a.s_post = s_post;
   a.dx = grad_x; a.ds_pre = grad_s_pre; a.ds_post = grad_s_post; a.amax_param = amax_param;
-  return status_of(launch_fakequant_bwd(a, (hipStream_t)stream));
+  return status_of(launch_fakequant_bwd(a, stream));
 }
 
 int nvfp4_fakequant_fwd(const uint16_t* x, int64_t rows, int64_t cols, const float* s_pre,
-                        const float* s_post, float* xq_out, void* stream) {
+                        const float* s_post, float* xq_out, hipStream_t stream) {
   return fq_fwd(x, rows, cols, s_pre, s_post, xq_out, false, stream);
 }
 
 int nvfp4_fakequant_bwd(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
                         const float* s_pre, const float* s_post, float* grad_x,
-                        float* grad_s_pre, float* grad_s_post, void* stream) {
+                        float* grad_s_pre, float* grad_s_post, hipStream_t stream) {
   return fq_bwd(x, grad_xq, rows, cols, s_pre, s_post, grad_x, grad_s_pre, grad_s_post, false,
                 stream);
 }
 
 int nvfp4_fakequant_fwd_amax(const uint16_t* x, int64_t rows, int64_t cols, const float* a_pre,
-                             const float* a_post, float* xq_out, void* stream) {
+                             const float* a_post, float* xq_out, hipStream_t stream) {
   return fq_fwd(x, rows, cols, a_pre, a_post, xq_out, true, stream);
 }
 
 int nvfp4_fakequant_bwd_amax(const uint16_t* x, const float* grad_xq, int64_t rows, int64_t cols,
                              const float* a_pre, const float* a_post, float* grad_x,
-                             float* grad_a_pre, float* grad_a_post, void* stream) {
+                             float* grad_a_pre, float* grad_a_post, hipStream_t stream) {
   return fq_bwd(x, grad_xq, rows, cols, a_pre, a_post, grad_x, grad_a_pre, grad_a_post, true,
                 stream);
 }
 
 // ---------------------------------------------------------------- test hooks
-int nvfp4_test_e2m1_rne_range(uint32_t first, int64_t n, uint8_t* codes, void* stream) {
+int nvfp4_test_e2m1_rne_range(uint32_t first, int64_t n, uint8_t* codes, hipStream_t stream) {
   if (n < 0 || n > (INT64_C(1) << 32) || (uint64_t)first + (uint64_t)n > (UINT64_C(1) << 32) ||
       (n > 0 && !codes))
     return NVFP4_ERR_INVALID;
   if (n == 0) return NVFP4_OK;
   hipLaunchKernelGGL(test_e2m1_range_kernel, dim3(test_grid(n)), dim3(256), 0,
-                     (hipStream_t)stream, first, n, codes);
+                     stream, first, n, codes);
   return status_of(hipGetLastError());
 }
 
-int nvfp4_test_e2m1_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, void* stream) {
+int nvfp4_test_e2m1_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, hipStream_t stream) {
   if (n < 0 || n % 8 != 0 || (n > 0 && (!y || !h || !codes))) return NVFP4_ERR_INVALID;
   if (n == 0) return NVFP4_OK;
   hipLaunchKernelGGL(test_e2m1_sr_kernel, dim3(test_grid(n / 8)), dim3(256), 0,
-                     (hipStream_t)stream, y, h, n, codes);
+                     stream, y, h, n, codes);
   return status_of(hipGetLastError());
 }
 
 int nvfp4_test_scale_encode_range(int fmt, uint32_t first, int64_t n, uint8_t* codes,
-                                  void* stream) {
+                                  hipStream_t stream) {
   if (fmt != NVFP4_SCALE_E4M3 && fmt != NVFP4_SCALE_UE5M3) return NVFP4_ERR_INVALID;
   if (n < 0 || (uint64_t)first + (uint64_t)n > (UINT64_C(1) << 31) || (n > 0 && !codes))
     return NVFP4_ERR_INVALID;
   if (n == 0) return NVFP4_OK;
   if (fmt == NVFP4_SCALE_E4M3)
     hipLaunchKernelGGL(test_scale_range_kernel<FMT_E4M3>, dim3(test_grid(n)), dim3(256), 0,
-                       (hipStream_t)stream, first, n, codes);
+                       stream, first, n, codes);
   else
     hipLaunchKernelGGL(test_scale_range_kernel<FMT_UE5M3>, dim3(test_grid(n)), dim3(256), 0,
-                       (hipStream_t)stream, first, n, codes);
+                       stream, first, n, codes);
   return status_of(hipGetLastError());
 }
 
-int nvfp4_test_e4m3_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, void* stream) {
+int nvfp4_test_e4m3_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes, hipStream_t stream) {
   if (n < 0 || n % 4 != 0 || (n > 0 && (!y || !h || !codes))) return NVFP4_ERR_INVALID;
   if (n == 0) return NVFP4_OK;
-  return status_of(launch_test_e4m3_sr(y, h, n, codes, (hipStream_t)stream));
+  return status_of(launch_test_e4m3_sr(y, h, n, codes, stream));
 }
 
-int nvfp4_test_sr_hash(uint64_t seed, uint64_t idx0, int64_t n, uint32_t* out, void* stream) {
+int nvfp4_test_sr_hash(uint64_t seed, uint64_t idx0, int64_t n, uint32_t* out, hipStream_t stream) {
   if (n < 0 || (n > 0 && !out)) return NVFP4_ERR_INVALID;
   if (n == 0) return NVFP4_OK;
-  hipLaunchKernelGGL(test_sr_hash_kernel, dim3(test_grid(n)), dim3(256), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(test_sr_hash_kernel, dim3(test_grid(n)), dim3(256), 0, stream,
                      seed, idx0, n, sr_key(seed, 0u), out);
   return status_of(hipGetLastError());
 }

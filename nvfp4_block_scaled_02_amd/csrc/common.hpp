@@ -30,6 +30,7 @@ struct QuantizeArgs {
   uint64_t seed;
   uint8_t *codes, *scales, *codes_t, *scales_t;
   unsigned long long* count4;
+  uint8_t* ws;  // workspace of the count's grid reduction (with count4)
 };
 
 struct DequantizeArgs {
@@ -43,6 +44,7 @@ struct DequantizeArgs {
   float* block_scale;
   const uint16_t* x_ref;
   double* sse;
+  uint8_t* ws;      // workspace of the error report's grid reduction (with sse)
   bool row_scaled;  // amax points to one amax per row (per-row outer scales)
 };
 
@@ -74,7 +76,10 @@ struct RequantArgs {
 };
 
 // Launchers (one translation unit each); return the hipError_t of the launch.
-hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, hipStream_t s);
+// Launchers taking `ws` reduce one value per workgroup in that workspace
+// (grid_reduce.hpp: kWorkspaceBytes, counters zero on entry and on exit).
+hipError_t launch_tensor_amax(const uint16_t* x, int64_t numel, float* out, uint8_t* ws,
+                              hipStream_t s);
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
 hipError_t launch_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* out, hipStream_t s);
 // a.amax = one amax per row
@@ -87,12 +92,12 @@ hipError_t launch_dequantize(const DequantizeArgs& a, hipStream_t s);
 hipError_t launch_quantize_rht(const QuantizeArgs& a, uint32_t signs, hipStream_t s);
 // amax of the transformed tensor (axis ROW or COL), and dequantize + inverse
 hipError_t launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint32_t signs,
-                           float* out, hipStream_t s);
+                           float* out, uint8_t* ws, hipStream_t s);
 hipError_t launch_dequantize_rht(const DequantizeArgs& a, uint32_t signs, hipStream_t s);
 hipError_t launch_fakequant_fwd(const FakeQuantArgs& a, hipStream_t s);
 hipError_t launch_fakequant_bwd(const FakeQuantArgs& a, hipStream_t s);
 hipError_t launch_requant_t(const RequantArgs& a, hipStream_t s);
-hipError_t launch_dequantized_amax(const RequantArgs& a, float* out, hipStream_t s);
+hipError_t launch_dequantized_amax(const RequantArgs& a, float* out, uint8_t* ws, hipStream_t s);
 // test hook: E4M3 SR element bytes through the re-quantizer's packing routine
 hipError_t launch_test_e4m3_sr(const float* y, const uint32_t* h, int64_t n, uint8_t* codes,
                                hipStream_t s);

@@ -10,6 +10,7 @@
 // plus 2 B read with the error report.
 #include "common.hpp"
 #include "device.hpp"
+#include "grid_reduce.hpp"
 
 namespace nvfp4 {
 
@@ -18,17 +19,13 @@ namespace nvfp4 {
 // float4 store per lane for binary32 output); 4 lanes share a block's scale
 // byte.  Outputs use non-temporal stores.
 //
-// Error report: the residual x - x_hat is taken in binary32 (exact whenever
-// x_hat is within a factor 2 of x, which holds for every unclipped nonzero
-// code), squared and summed in binary64; one binary64 atomic add per
-// workgroup.  Same-address atomics serialize, so the reporting variant runs
-// one 1024-thread workgroup per CU.
+// Error report: the residual x - x_hat is taken in binary64 (exact unless x
+// is more than 2^29 times x_hat, i.e. a block scale saturated far below its
+// data), squared and accumulated in binary64 per
+// lane in a fixed order; the workgroups' sums meet in the caller's workspace
+// and the last workgroup adds them in index order (grid_reduce.hpp), so the
+// report is the same on every run of a launch shape.
 constexpr int kDqUnroll = 4;
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
   const uint32_t b = __float_as_uint(v);
@@ -42,7 +39,7 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
                   int64_t nquads, const float* __restrict__ amax, float sg,
                   float4* __restrict__ out_f32, uint2* __restrict__ out_bf16,
                   float* __restrict__ block_scale, const uint2* __restrict__ x_ref,
-                  double* sse) {
+                  double* sse, uint8_t* ws) {
   const bool lead4 = (threadIdx.x & 3) == 0;
   double acc = 0.0;
   const int64_t per_iter = (int64_t)gridDim.x * BLOCK * kDqUnroll;
@@ -84,23 +81,16 @@ dequantize_kernel(const uint16_t* __restrict__ codes, const uint8_t* __restrict_
         const float xs[4] = {bf16_lo(xr[u].x), bf16_hi(xr[u].x), bf16_lo(xr[u].y), bf16_hi(xr[u].y)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const double d = (double)(xs[i] - v[i]);
+          const double d = (double)xs[i] - (double)v[i];
           acc = __builtin_fma(d, d, acc);
         }
       }
     }
     if (base + per_iter < nquads) load(base + per_iter);
   }
-  if (SSE) {
-    __shared__ double red[BLOCK / 64];
-    acc = wave_sum_f64(acc);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double t = 0.0;
-      for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
-      unsafeAtomicAdd(sse, t);
-    }
+  if constexpr (SSE) {
+    double total;
+    if (grid_reduce<SumF64, BLOCK>(ws, acc, &total)) *sse = total;
   }
 }
 
@@ -115,7 +105,7 @@ dequantize_rows_kernel(const uint16_t* __restrict__ codes, const uint8_t* __rest
                        int64_t rows, int64_t qpr, const float* __restrict__ row_amax, float sg,
                        float4* __restrict__ out_f32, uint2* __restrict__ out_bf16,
                        float* __restrict__ block_scale, const uint2* __restrict__ x_ref,
-                       double* sse) {
+                       double* sse, uint8_t* ws) {
   const bool lead4 = (threadIdx.x & 3) == 0;
   const int64_t G = gridDim.x;
   double acc = 0.0;
@@ -158,23 +148,16 @@ dequantize_rows_kernel(const uint16_t* __restrict__ codes, const uint8_t* __rest
           const float xs[4] = {bf16_lo(xr[u].x), bf16_hi(xr[u].x), bf16_lo(xr[u].y), bf16_hi(xr[u].y)};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const double d = (double)(xs[i] - v[i]);
+            const double d = (double)xs[i] - (double)v[i];
             acc = __builtin_fma(d, d, acc);
           }
         }
       }
     }
   }
-  if (SSE) {
-    __shared__ double red[BLOCK / 64];
-    acc = wave_sum_f64(acc);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double t = 0.0;
-      for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
-      unsafeAtomicAdd(sse, t);
-    }
+  if constexpr (SSE) {
+    double total;
+    if (grid_reduce<SumF64, BLOCK>(ws, acc, &total)) *sse = total;
   }
 }
 
@@ -184,19 +167,21 @@ static hipError_t launch_dq(const DequantizeArgs& a, hipStream_t s) {
   const int64_t cus = device_cu_count();
   if (a.row_scaled) {
     // SSE: one 1024-lane workgroup per CU (88 registers: two do not fit)
-    const int64_t cap = cus * (SSE ? 1 : 8);
+    int64_t cap = cus * (SSE ? 1 : 8);
+    cap = cap < kSlots ? cap : kSlots;
     const int64_t grid = a.rows < cap ? a.rows : cap;
     hipLaunchKernelGGL((dequantize_rows_kernel<FMT, F32, BF16, BSC, SSE, BLOCK>),
                        dim3((unsigned)grid), dim3(BLOCK), 0, s,
                        reinterpret_cast<const uint16_t*>(a.codes), a.scales, a.rows, a.cols / 4,
                        a.amax, a.sg, reinterpret_cast<float4*>(a.out_f32),
                        reinterpret_cast<uint2*>(a.out_bf16), a.block_scale,
-                       reinterpret_cast<const uint2*>(a.x_ref), a.sse);
+                       reinterpret_cast<const uint2*>(a.x_ref), a.sse, a.ws);
     return hipGetLastError();
   }
-  // SSE: two 1024-lane workgroups per CU (8 wavefronts per SIMD; one atomic
-  // each): 39.5 us at 8192x4096 against 42.1 with one, four give 40.0
-  const int64_t cap = cus * (SSE ? 2 : 8);
+  // SSE: two 1024-lane workgroups per CU (8 wavefronts per SIMD): 39.5 us
+  // at 8192x4096 against 42.1 with one, four give 40.0
+  int64_t cap = cus * (SSE ? 2 : 8);
+  cap = cap < kSlots ? cap : kSlots;
   const int64_t nquads = a.rows * a.cols / 4;
   const int64_t per_wg = (int64_t)BLOCK * kDqUnroll;
   int64_t grid = (nquads + per_wg - 1) / per_wg;
@@ -205,7 +190,7 @@ static hipError_t launch_dq(const DequantizeArgs& a, hipStream_t s) {
                      dim3(BLOCK), 0, s, reinterpret_cast<const uint16_t*>(a.codes), a.scales,
                      nquads, a.amax, a.sg, reinterpret_cast<float4*>(a.out_f32),
                      reinterpret_cast<uint2*>(a.out_bf16), a.block_scale,
-                     reinterpret_cast<const uint2*>(a.x_ref), a.sse);
+                     reinterpret_cast<const uint2*>(a.x_ref), a.sse, a.ws);
   return hipGetLastError();
 }
 

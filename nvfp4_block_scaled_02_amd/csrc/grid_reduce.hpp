@@ -1,0 +1,141 @@
+// grid_reduce.hpp -- one value per workgroup combined across the grid in a
+// fixed order, in the same launch, with no clearing kernel and no
+// floating-point atomics.
+//
+// Every workgroup stores its value into its own 8-byte slot of a workspace
+// and then arrives at one of kGroups counters (workgroup b at counter b mod
+// kGroups, each counter on its own 128-byte line, so that same-address
+// atomics queue kGroups ways in parallel instead of all on one address).  The
+// last workgroup of a counter resets it and arrives at a top counter; the
+// last workgroup at the top counter resets that one too and combines slots 0,
+// 1, ..., G-1.  The combination is a fixed shape (a strided sequential pass
+// per lane, a fixed butterfly per wavefront, wavefronts in index order), so a
+// floating-point sum depends only on G and the workgroup size, not on the
+// order in which workgroups finished.
+//
+// Workspace contract: kWorkspaceBytes of device memory whose counters are
+// zero before a launch; every launch that runs to completion leaves them
+// zero.  Launches that use one workspace must not overlap.
+//
+// Ordering: the arrivals are agent-scope acquire-release read-modify-writes,
+// so a workgroup's slot store happens-before the last workgroup's reads of
+// it (HIP memory model; on gfx950 the release writes back and the acquire
+// invalidates this XCD's L2 as needed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kSlots = 8192;                 // largest grid a reducing launch may use
+constexpr int kGroups = 8;                   // arrival counters below the top counter
+constexpr int kCtrStride = 32;               // uint32 words between counters (128 bytes)
+constexpr size_t kCtrOffset = (size_t)kSlots * 8;
+constexpr size_t kWorkspaceBytes = kCtrOffset + (size_t)(kGroups + 1) * kCtrStride * 4;
+
+// Called by exactly one thread of every workgroup of the grid, once.  Returns
+// true in the last workgroup to arrive; in it every slot [0, gridDim.x) holds
+// its workgroup's value.
+__device__ __forceinline__ bool grid_arrive(uint8_t* ws, uint64_t value) {
+  const uint32_t G = gridDim.x, b = blockIdx.x;
+  uint64_t* slots = reinterpret_cast<uint64_t*>(ws);
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + kCtrOffset);
+  __hip_atomic_store(&slots[b], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t grp = b % kGroups;
+  const uint32_t gsize = G / kGroups + (grp < G % kGroups ? 1u : 0u);
+  const uint32_t ngroups = G < (uint32_t)kGroups ? G : (uint32_t)kGroups;
+  uint32_t* gc = ctr + grp * kCtrStride;
+  if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != gsize - 1)
+    return false;
+  // every member of this group has arrived: no further update in this launch
+  __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t* top = ctr + kGroups * kCtrStride;
+  if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1)
+    return false;
+  __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+__device__ __forceinline__ uint64_t slot_load(const uint8_t* ws, uint32_t i) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(ws) + i, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The combinations: an identity, a binary operation, and the slot encoding.
+struct SumU64 {
+  typedef uint64_t T;
+  static __device__ T identity() { return 0; }
+  static __device__ T op(T a, T b) { return a + b; }
+  static __device__ uint64_t to_bits(T v) { return v; }
+  static __device__ T from_bits(uint64_t v) { return v; }
+};
+struct MaxU32 {
+  typedef uint32_t T;
+  static __device__ T identity() { return 0; }
+  static __device__ T op(T a, T b) { return a > b ? a : b; }
+  static __device__ uint64_t to_bits(T v) { return v; }
+  static __device__ T from_bits(uint64_t v) { return (uint32_t)v; }
+};
+struct SumF64 {
+  typedef double T;
+  static __device__ T identity() { return 0.0; }
+  static __device__ T op(T a, T b) { return a + b; }
+  static __device__ uint64_t to_bits(T v) { return __builtin_bit_cast(uint64_t, v); }
+  static __device__ T from_bits(uint64_t v) { return __builtin_bit_cast(double, v); }
+};
+
+template <class R>
+__device__ __forceinline__ typename R::T wave_reduce(typename R::T v) {
+  typedef typename R::T T;
+  for (int off = 32; off >= 1; off >>= 1) {
+    T o;
+    if constexpr (sizeof(T) == 8) {
+      const uint64_t u = __builtin_bit_cast(uint64_t, v);
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)u, off, 64);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(u >> 32), off, 64);
+      o = __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    } else {
+      o = __builtin_bit_cast(T, __shfl_xor(__builtin_bit_cast(int, v), off, 64));
+    }
+    v = R::op(v, o);
+  }
+  return v;
+}
+
+// Every thread of every workgroup calls this once with its own value (all
+// threads must reach it: it holds workgroup barriers).  The workgroup's
+// values are combined (fixed butterfly, wavefronts in order), the grid's
+// workgroup values are combined by the last workgroup, and true is returned
+// to thread 0 of that workgroup with the grid total in *total.
+template <class R, int BLOCK>
+__device__ __forceinline__ bool grid_reduce(uint8_t* ws, typename R::T v, typename R::T* total) {
+  typedef typename R::T T;
+  static_assert(BLOCK % 64 == 0 && BLOCK <= 1024, "whole wavefronts");
+  __shared__ T red[BLOCK / 64];
+  __shared__ bool last;
+  v = wave_reduce<R>(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    T t = red[0];
+    for (int i = 1; i < BLOCK / 64; ++i) t = R::op(t, red[i]);
+    last = grid_arrive(ws, R::to_bits(t));
+  }
+  __syncthreads();
+  if (!last) return false;
+  // the last workgroup: lane t takes slots t, t + BLOCK, ... in order
+  T acc = R::identity();
+  for (uint32_t i = threadIdx.x; i < gridDim.x; i += BLOCK) acc = R::op(acc, R::from_bits(slot_load(ws, i)));
+  acc = wave_reduce<R>(acc);
+  __syncthreads();  // red[] is reused
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x != 0) return false;
+  T t = red[0];
+  for (int i = 1; i < BLOCK / 64; ++i) t = R::op(t, red[i]);
+  *total = t;
+  return true;
+}
+
+}  // namespace nvfp4

@@ -39,7 +39,7 @@ template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
 __global__ void __launch_bounds__(BLOCK)
 quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* __restrict__ amax,
                      float sg, uint64_t seed, uint32_t key0, uint32_t* __restrict__ codes,
-                     uint8_t* __restrict__ scales, unsigned long long* count4) {
+                     uint8_t* __restrict__ scales, unsigned long long* count4, uint8_t* ws) {
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   const TensorScale ts = tensor_scale(*amax, sg);
   build_table<FMT>(tab, ts.alpha);
@@ -83,7 +83,7 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
       }
     }
   }
-  if (is_four_six(SELECT) && count4) flush_count<BLOCK>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<BLOCK>(count4, n4, ws);
 }
 
 
@@ -102,7 +102,8 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
                                             const float* __restrict__ amax, float sg, uint64_t seed,
                                             uint32_t key0, uint2* __restrict__ codes,
                                             uint8_t* __restrict__ scales,
-                                            unsigned long long* count4, uint32_t rht_signs) {
+                                            unsigned long long* count4, uint8_t* ws,
+                                            uint32_t rht_signs) {
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint4 stage[BLOCK * 2];
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -159,16 +160,16 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
       n4 += o.four;
     }
   }
-  if (is_four_six(SELECT) && count4) flush_count<BLOCK>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<BLOCK>(count4, n4, ws);
 }
 
 template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8)))
 quantize_blocks_kernel(const uint4* __restrict__ x, int64_t nblocks, const float* __restrict__ amax,
                        float sg, uint64_t seed, uint32_t key0, uint2* __restrict__ codes,
-                       uint8_t* __restrict__ scales, unsigned long long* count4) {
+                       uint8_t* __restrict__ scales, unsigned long long* count4, uint8_t* ws) {
   blocks_body<FMT, SELECT, ROUND, WIDE, BLOCK, false>(x, nblocks, amax, sg, seed, key0, codes,
-                                                      scales, count4, 0u);
+                                                      scales, count4, ws, 0u);
 }
 
 // The same with every block transformed by the 16-point random Hadamard
@@ -180,9 +181,9 @@ __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(7)))
 quantize_blocks_rht_kernel(const uint4* __restrict__ x, int64_t nblocks,
                            const float* __restrict__ amax, float sg, uint64_t seed, uint32_t key0,
                            uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-                           unsigned long long* count4, uint32_t rht_signs) {
+                           unsigned long long* count4, uint8_t* ws, uint32_t rht_signs) {
   blocks_body<FMT, SELECT, ROUND, WIDE, BLOCK, true>(x, nblocks, amax, sg, seed, key0, codes,
-                                                     scales, count4, rht_signs);
+                                                     scales, count4, ws, rht_signs);
 }
 
 // ---------------------------------------------------------------- per-row outer scales
@@ -197,7 +198,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8
 quantize_rowscaled_kernel(const uint4* __restrict__ x, int64_t nblocks, int64_t row_blocks,
                           const float* __restrict__ row_amax, float sg, uint64_t seed,
                           uint32_t key0, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-                          unsigned long long* count4) {
+                          unsigned long long* count4, uint8_t* ws) {
   __shared__ __attribute__((aligned(16))) uint4 stage[kThreads * 2];
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
   uint4* reg = stage + wv * 128;
@@ -224,7 +225,7 @@ quantize_rowscaled_kernel(const uint4* __restrict__ x, int64_t nblocks, int64_t 
       n4 += o.four;
     }
   }
-  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4, ws);
 }
 
 // Long rows (at least 64 blocks): a wavefront owns whole rows.  Per row it
@@ -237,7 +238,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8
 quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_blocks,
                         const float* __restrict__ row_amax, float sg, uint64_t seed,
                         uint32_t key0, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-                        unsigned long long* count4) {
+                        unsigned long long* count4, uint8_t* ws) {
   constexpr int kTab = (FmtTraits<FMT>::kCodes + 63) / 64 * 64;
   __shared__ __attribute__((aligned(16))) uint4 stage[kThreads * 2];
   __shared__ f32x2 tabs[kThreads / 64][kTab];
@@ -291,7 +292,7 @@ quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_b
       }
     }
   }
-  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4, ws);
 }
 
 // ---------------------------------------------------------------- column-wise
@@ -368,7 +369,8 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
                       const float* __restrict__ amax, float sg, uint64_t seed, uint32_t key0,
                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                       uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
-                      unsigned long long* count4, int64_t seg, uint32_t rht_signs = 0) {
+                      unsigned long long* count4, uint8_t* ws, int64_t seg,
+                      uint32_t rht_signs = 0) {
   static_assert(kSW * kTR / 16 == kThreads, "one row block and one column block per lane");
   static_assert(!(RHT && (DO_ROW || TILE2D)), "the transform applies to column blocks only here");
   constexpr int kAhead = DO_ROW ? 2 : 1;
@@ -496,78 +498,77 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
       if (tr < tr1) step(A, B, tr);
     }
   }
-  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4);
+  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4, ws);
 }
 
 // ---------------------------------------------------------------- dispatch
+// Grids never exceed the workspace's kSlots (a counting launch reduces one
+// value per workgroup there); every launch below is far smaller on MI355X.
+static int64_t cap_grid(int64_t grid, int64_t cap) {
+  grid = grid < cap ? grid : cap;
+  grid = grid < kSlots ? grid : kSlots;
+  return grid < 1 ? 1 : grid;
+}
+
+// Strip-walker launch: as many workgroups as the GPU holds at once, each
+// walking a strip over `seg` tiles.
+template <auto KERN>
+static void walker_shape(const QuantizeArgs& a, int64_t& grid, int64_t& seg) {
+  const int64_t tiles_r = (a.rows + kTR - 1) / kTR, tiles_c = (a.cols + kSW - 1) / kSW;
+  const int64_t target = (int64_t)device_cu_count() * resident_per_cu<KERN>();
+  seg = (tiles_r * tiles_c + target - 1) / target;
+  seg = seg < 1 ? 1 : (seg > tiles_r ? tiles_r : seg);
+  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
+  grid = cap_grid(units, target);
+}
 
 template <int FMT, int SELECT, int ROUND, bool WIDE>
 static hipError_t launch_typed(const QuantizeArgs& a, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int cus = device_cu_count();
-  const bool counting = is_four_six(a.select) && a.count4 != nullptr;
   if (a.axes == AXIS_ROW) {
     if constexpr (SELECT != SELECT_6 || ROUND == ROUND_SR) {
       // one lane per block: these paths are bound by per-block arithmetic
       const int64_t nblocks = a.rows * a.cols / 16;
       const int64_t ngroups = (nblocks + 63) / 64;
-      if (counting) {
-        // one 1024-thread workgroup per CU: at most one atomic per CU
-        constexpr int B = 1024;
-        int64_t grid = (ngroups + B / 64 - 1) / (B / 64);
-        grid = grid < cus ? grid : cus;
-        hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, B>), dim3((unsigned)grid),
-                           dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg,
-                           a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
-      } else if (ngroups >= (int64_t)cus * 32) {
+      if (ngroups >= (int64_t)cus * 32) {
         // enough groups to fill every CU: two 1024-thread workgroups per CU
         // (8 wavefronts per SIMD, as with eight of 256) build a quarter of
         // the tables, 16.57 -> 16.0 us at 8192x4096 (same-box A/B)
         constexpr int B = 1024;
-        int64_t grid = (ngroups + B / 64 - 1) / (B / 64);
-        const int64_t cap = (int64_t)cus * 2;
-        grid = grid < cap ? grid : cap;
+        const int64_t grid = cap_grid((ngroups + B / 64 - 1) / (B / 64), (int64_t)cus * 2);
         hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, B>), dim3((unsigned)grid),
                            dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg,
-                           a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+                           a.seed, key0, reinterpret_cast<uint2*>(a.codes), a.scales, a.count4, a.ws);
       } else {
         // small tensors: 256-thread workgroups spread the groups over more CUs
-        int64_t grid = (ngroups + kThreads / 64 - 1) / (kThreads / 64);
-        const int64_t cap = (int64_t)cus * 8;
-        grid = grid < cap ? grid : cap;
+        const int64_t grid = cap_grid((ngroups + kThreads / 64 - 1) / (kThreads / 64), (int64_t)cus * 8);
         hipLaunchKernelGGL((quantize_blocks_kernel<FMT, SELECT, ROUND, WIDE, kThreads>),
                            dim3((unsigned)grid), dim3(kThreads), 0, s,
                            reinterpret_cast<const uint4*>(a.x), nblocks, a.amax, a.sg, a.seed, key0,
-                           reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+                           reinterpret_cast<uint2*>(a.codes), a.scales, a.count4, a.ws);
       }
     } else {
       // max->6 with round-to-nearest: the lane-pair stream (no count output)
       const int64_t nchunks = a.rows * a.cols / kChunk;
-      int64_t grid = (nchunks + (int64_t)kThreads * kRowUnroll - 1) / ((int64_t)kThreads * kRowUnroll);
-      const int64_t cap = (int64_t)cus * 8;
-      grid = grid < cap ? grid : cap;
+      const int64_t grid = cap_grid((nchunks + (int64_t)kThreads * kRowUnroll - 1) / ((int64_t)kThreads * kRowUnroll),
+                                    (int64_t)cus * 8);
       hipLaunchKernelGGL((quantize_rows_kernel<FMT, SELECT, ROUND, WIDE, kThreads>),
                          dim3((unsigned)grid), dim3(kThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.x), nchunks, a.amax, a.sg, a.seed, key0,
-                         reinterpret_cast<uint32_t*>(a.codes), a.scales, a.count4);
+                         reinterpret_cast<uint32_t*>(a.codes), a.scales, a.count4, a.ws);
     }
     return hipGetLastError();
   }
   constexpr auto kFused = quantize_tiles_kernel<FMT, SELECT, ROUND, WIDE, true>;
   constexpr auto kCol = quantize_tiles_kernel<FMT, SELECT, ROUND, WIDE, false>;
   const bool fused = a.axes == (AXIS_ROW | AXIS_COL);
-  const auto kern = fused ? kFused : kCol;
-  // as many workgroups as the GPU holds at once (fewer when counting: one
-  // atomic each), each walking a strip over `seg` tiles
-  const int64_t tiles_r = (a.rows + kTR - 1) / kTR, tiles_c = (a.cols + kSW - 1) / kSW;
-  const int64_t target =
-      (int64_t)cus * (counting ? 2 : (fused ? resident_per_cu<kFused>() : resident_per_cu<kCol>()));
-  int64_t seg = (tiles_r * tiles_c + target - 1) / target;
-  seg = seg < 1 ? 1 : (seg > tiles_r ? tiles_r : seg);
-  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
-  const int64_t grid = units < target ? units : target;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows, a.cols, a.amax,
-                     a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t, a.count4, seg, 0u);
+  int64_t grid, seg;
+  if (fused) walker_shape<kFused>(a, grid, seg);
+  else walker_shape<kCol>(a, grid, seg);
+  hipLaunchKernelGGL(fused ? kFused : kCol, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows,
+                     a.cols, a.amax, a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t,
+                     a.count4, a.ws, seg, 0u);
   return hipGetLastError();
 }
 
@@ -592,28 +593,24 @@ template <int FMT, int SELECT, int ROUND, bool WIDE>
 static hipError_t launch_rowscaled_typed(const QuantizeArgs& a, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int64_t cus = device_cu_count();
-  const bool counting = is_four_six(a.select) && a.count4 != nullptr;
   const int64_t nblocks = a.rows * a.cols / 16;
   const int64_t row_blocks = a.cols / 16;
-  const int64_t cap = counting ? cus : cus * 8;  // counting: one atomic per workgroup
   // A wavefront per row when its groups are mostly full (at least 3/4 of
   // the lanes busy), else one lane per block over the flat block stream.
   if (row_blocks % 64 == 0 || row_blocks >= 192) {
-    int64_t grid = (a.rows + kThreads / 64 - 1) / (kThreads / 64);
-    grid = grid < cap ? grid : cap;
+    const int64_t grid = cap_grid((a.rows + kThreads / 64 - 1) / (kThreads / 64), cus * 8);
     hipLaunchKernelGGL((quantize_rowwave_kernel<FMT, SELECT, ROUND, WIDE>), dim3((unsigned)grid),
                        dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), a.rows,
                        row_blocks, a.amax, a.sg, a.seed, key0,
-                       reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+                       reinterpret_cast<uint2*>(a.codes), a.scales, a.count4, a.ws);
     return hipGetLastError();
   }
   const int64_t ngroups = (nblocks + 63) / 64;
-  int64_t grid = (ngroups + kThreads / 64 - 1) / (kThreads / 64);
-  grid = grid < cap ? grid : cap;
+  const int64_t grid = cap_grid((ngroups + kThreads / 64 - 1) / (kThreads / 64), cus * 8);
   hipLaunchKernelGGL((quantize_rowscaled_kernel<FMT, SELECT, ROUND, WIDE>), dim3((unsigned)grid),
                      dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), nblocks,
                      a.cols / 16, a.amax, a.sg, a.seed, key0,
-                     reinterpret_cast<uint2*>(a.codes), a.scales, a.count4);
+                     reinterpret_cast<uint2*>(a.codes), a.scales, a.count4, a.ws);
   return hipGetLastError();
 }
 
@@ -645,30 +642,23 @@ template <int FMT, int SELECT, int ROUND, bool WIDE>
 static hipError_t launch_rht_typed(const QuantizeArgs& a, uint32_t signs, hipStream_t s) {
   const uint32_t key0 = sr_key(a.seed, 0u);
   const int cus = device_cu_count();
-  const bool counting = is_four_six(a.select) && a.count4 != nullptr;
   if (a.axes == AXIS_ROW) {
     const int64_t nblocks = a.rows * a.cols / 16;
     const int64_t ngroups = (nblocks + 63) / 64;
     constexpr int B = kThreads;
-    int64_t grid = (ngroups + B / 64 - 1) / (B / 64);
-    const int64_t cap = counting ? (int64_t)cus * 2 : (int64_t)cus * 8;
-    grid = grid < cap ? grid : cap;
+    const int64_t grid = cap_grid((ngroups + B / 64 - 1) / (B / 64), (int64_t)cus * 8);
     hipLaunchKernelGGL((quantize_blocks_rht_kernel<FMT, SELECT, ROUND, WIDE, B>),
                        dim3((unsigned)grid), dim3(B), 0, s, reinterpret_cast<const uint4*>(a.x),
                        nblocks, a.amax, a.sg, a.seed, key0, reinterpret_cast<uint2*>(a.codes),
-                       a.scales, a.count4, signs);
+                       a.scales, a.count4, a.ws, signs);
     return hipGetLastError();
   }
   constexpr auto kern = quantize_tiles_kernel<FMT, SELECT, ROUND, WIDE, false, true, false, true>;
-  const int64_t tiles_r = (a.rows + kTR - 1) / kTR, tiles_c = (a.cols + kSW - 1) / kSW;
-  const int64_t target = (int64_t)cus * (counting ? 2 : resident_per_cu<kern>());
-  int64_t seg = (tiles_r * tiles_c + target - 1) / target;
-  seg = seg < 1 ? 1 : (seg > tiles_r ? tiles_r : seg);
-  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
-  const int64_t grid = units < target ? units : target;
+  int64_t grid, seg;
+  walker_shape<kern>(a, grid, seg);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows, a.cols, a.amax,
-                     a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t, a.count4, seg,
-                     signs);
+                     a.sg, a.seed, key0, a.codes, a.scales, a.codes_t, a.scales_t, a.count4, a.ws,
+                     seg, signs);
   return hipGetLastError();
 }
 
@@ -697,16 +687,12 @@ static hipError_t launch_2d_fmt(const QuantizeArgs& a, hipStream_t s) {
   constexpr auto kBoth = quantize_tiles_kernel<FMT, SELECT_6, ROUND_RNE, false, true, true, true>;
   constexpr auto kRow = quantize_tiles_kernel<FMT, SELECT_6, ROUND_RNE, false, true, false, true>;
   const bool both = a.axes == (AXIS_ROW | AXIS_COL);
-  const int64_t tiles_r = (a.rows + kTR - 1) / kTR, tiles_c = (a.cols + kSW - 1) / kSW;
-  const int64_t target =
-      (int64_t)device_cu_count() * (both ? resident_per_cu<kBoth>() : resident_per_cu<kRow>());
-  int64_t seg = (tiles_r * tiles_c + target - 1) / target;
-  seg = seg < 1 ? 1 : (seg > tiles_r ? tiles_r : seg);
-  const int64_t units = ((tiles_r + seg - 1) / seg) * tiles_c;
-  const int64_t grid = units < target ? units : target;
+  int64_t grid, seg;
+  if (both) walker_shape<kBoth>(a, grid, seg);
+  else walker_shape<kRow>(a, grid, seg);
   hipLaunchKernelGGL(both ? kBoth : kRow, dim3((unsigned)grid), dim3(kThreads), 0, s, a.x, a.rows,
                      a.cols, a.amax, a.sg, a.seed, 0u, a.codes, a.scales, a.codes_t, a.scales_t,
-                     nullptr, seg, 0u);
+                     nullptr, nullptr, seg, 0u);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 
 #include "common.hpp"
 #include "device.hpp"
+#include "grid_reduce.hpp"
 
 namespace nvfp4 {
 
@@ -413,20 +414,14 @@ __device__ __forceinline__ uint32_t hash_base(uint64_t seed, uint64_t idx0, uint
   return (uint32_t)idx0 ^ key;
 }
 
-// Adds the per-lane 4/6 counts of the workgroup to *count4 (one atomic).
-// Same-address device atomics serialize (about 8 ns each on MI355X), so the
-// launchers keep the grid of a counting launch to about one workgroup per CU.
+// Adds the grid's per-lane 4/6 counts to *count4: the workgroups' sums meet
+// in the workspace (grid_reduce.hpp) and the last workgroup adds the total
+// with one atomic, so a counting launch keeps the launch shape of a
+// non-counting one.  Every workgroup of the grid must call it.
 template <int BLOCK>
-__device__ __forceinline__ void flush_count(unsigned long long* count4, uint32_t n4) {
-  __shared__ uint32_t red[BLOCK / 64];
-  for (int off = 32; off >= 1; off >>= 1) n4 += (uint32_t)__shfl_xor((int)n4, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = n4;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long t = 0;
-    for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
-    if (t) atomicAdd(count4, t);
-  }
+__device__ __forceinline__ void flush_count(unsigned long long* count4, uint32_t n4, uint8_t* ws) {
+  uint64_t total;
+  if (grid_reduce<SumU64, BLOCK>(ws, (uint64_t)n4, &total) && total != 0) atomicAdd(count4, total);
 }
 
 // Writes the wavefront's 128 chunks (lane l: chunks l and 64 + l) to its LDS

@@ -14,6 +14,7 @@
 // pieces per output row: NVFP4 codes and scales and MXFP8 scales through LDS
 // staging, MXFP8 elements as the two 32-byte halves of each 64-row tile
 // column, written together by the two lanes that own them.
+#include "grid_reduce.hpp"
 #include "quantize_core.hpp"
 
 namespace nvfp4 {
@@ -328,19 +329,11 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 constexpr int kDqaUnroll = 4;
 constexpr int kDqaThreads = 1024;
 
-// Workgroup maximum of m, folded into *out by one atomic (skipped when the
-// running maximum already covers it).
-__device__ __forceinline__ void dq_amax_flush(uint32_t m, uint32_t* out) {
-  for (int off = 32; off >= 1; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  __shared__ uint32_t red[kDqaThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-    for (int w2 = 1; w2 < (int)(blockDim.x >> 6); ++w2) r = umax(r, red[w2]);
-    const uint32_t cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (r > cur) atomicMax(out, r);
-  }
+// The grid maximum of the per-lane values m written to *out by the last
+// workgroup (grid_reduce.hpp).
+__device__ __forceinline__ void dq_amax_flush(uint32_t m, float* out, uint8_t* ws) {
+  uint32_t r;
+  if (grid_reduce<MaxU32, kDqaThreads>(ws, m, &r)) out[0] = __uint_as_float(r);
 }
 
 // Per-tensor alpha: a lane takes two blocks (a 16-byte chunk of codes, two
@@ -349,7 +342,7 @@ template <int FMT>
 __global__ void __launch_bounds__(kDqaThreads)
 dq_amax_kernel(const uint4* __restrict__ codes, const uint16_t* __restrict__ scales, int64_t npairs,
                int64_t nblocks, const float* __restrict__ amax, float sg,
-               uint32_t* __restrict__ out) {
+               float* __restrict__ out, uint8_t* __restrict__ ws) {
   uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * kDqaThreads;
   int64_t i = (int64_t)blockIdx.x * kDqaThreads + threadIdx.x;
@@ -375,8 +368,9 @@ dq_amax_kernel(const uint4* __restrict__ codes, const uint16_t* __restrict__ sca
   if ((nblocks & 1) && blockIdx.x == 0 && threadIdx.x == 0)  // the block after the last pair
     m = umax(m, qd_bits<FMT>(reinterpret_cast<const uint2*>(codes)[nblocks - 1],
                              reinterpret_cast<const uint8_t*>(scales)[nblocks - 1]));
-  const float alpha = outer_alpha(*amax, sg);
-  dq_amax_flush(__float_as_uint(__uint_as_float(m) * alpha) & 0x7FFFFFFFu, out);
+  // an empty tensor (nblocks = 0, amax possibly absent) reduces to 0
+  const float alpha = nblocks ? outer_alpha(*amax, sg) : 0.0f;
+  dq_amax_flush(__float_as_uint(__uint_as_float(m) * alpha) & 0x7FFFFFFFu, out, ws);
 }
 
 // Per-row alpha_r: a wavefront per row (its lanes over the row's blocks,
@@ -385,7 +379,7 @@ template <int FMT>
 __global__ void __launch_bounds__(kDqaThreads)
 dq_amax_rows_kernel(const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
                     int64_t rows, int64_t row_blocks, const float* __restrict__ row_amax, float sg,
-                    uint32_t* __restrict__ out) {
+                    float* __restrict__ out, uint8_t* __restrict__ ws) {
   const int l = threadIdx.x & 63;
   const int64_t nwaves = (int64_t)gridDim.x * (kDqaThreads / 64);
   uint32_t best = 0;
@@ -410,11 +404,7 @@ dq_amax_rows_kernel(const uint2* __restrict__ codes, const uint8_t* __restrict__
     const float v = __uint_as_float(m) * outer_alpha(row_amax[r], sg);
     best = umax(best, __float_as_uint(v) & 0x7FFFFFFFu);
   }
-  dq_amax_flush(best, out);
-}
-
-__global__ void __launch_bounds__(64) dq_amax_init_kernel(uint32_t* out) {
-  if (threadIdx.x == 0) out[0] = 0u;
+  dq_amax_flush(best, out, ws);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -456,25 +446,24 @@ hipError_t launch_requant_t(const RequantArgs& a, hipStream_t s) {
   return rowsc ? launch_rq_src<FMT_E4M3, true>(a, s) : launch_rq_src<FMT_E4M3, false>(a, s);
 }
 
-hipError_t launch_dequantized_amax(const RequantArgs& a, float* out, hipStream_t s) {
-  uint32_t* o = reinterpret_cast<uint32_t*>(out);
-  hipLaunchKernelGGL(dq_amax_init_kernel, dim3(1), dim3(64), 0, s, o);
+hipError_t launch_dequantized_amax(const RequantArgs& a, float* out, uint8_t* ws, hipStream_t s) {
   const int64_t nblocks = a.rows * a.cols / 16;
-  if (nblocks == 0) return hipGetLastError();
-  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (one atomic) per CU
+  int64_t cap = (int64_t)device_cu_count();  // one workgroup per CU at most
+  cap = cap < kSlots ? cap : kSlots;
   const dim3 bd(kDqaThreads);
-  if (a.row_amax != nullptr) {
+  if (a.row_amax != nullptr && nblocks > 0) {
     int64_t grid = (a.rows + kDqaThreads / 64 - 1) / (kDqaThreads / 64);
     grid = grid < cap ? grid : cap;
     const uint2* c = reinterpret_cast<const uint2*>(a.codes);
     if (a.fmt == FMT_UE5M3)
       hipLaunchKernelGGL(dq_amax_rows_kernel<FMT_UE5M3>, dim3((unsigned)grid), bd, 0, s, c, a.scales,
-                         a.rows, a.cols / 16, a.row_amax, a.sg, o);
+                         a.rows, a.cols / 16, a.row_amax, a.sg, out, ws);
     else
       hipLaunchKernelGGL(dq_amax_rows_kernel<FMT_E4M3>, dim3((unsigned)grid), bd, 0, s, c, a.scales,
-                         a.rows, a.cols / 16, a.row_amax, a.sg, o);
+                         a.rows, a.cols / 16, a.row_amax, a.sg, out, ws);
     return hipGetLastError();
   }
+  // per-tensor alpha, or an empty tensor (one workgroup writes 0)
   const int64_t npairs = nblocks / 2;
   int64_t grid = (npairs + (int64_t)kDqaThreads * kDqaUnroll - 1) / ((int64_t)kDqaThreads * kDqaUnroll);
   grid = grid < cap ? grid : cap;
@@ -483,10 +472,10 @@ hipError_t launch_dequantized_amax(const RequantArgs& a, float* out, hipStream_t
   const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.scales);
   if (a.fmt == FMT_UE5M3)
     hipLaunchKernelGGL(dq_amax_kernel<FMT_UE5M3>, dim3((unsigned)grid), bd, 0, s, c, sc, npairs,
-                       nblocks, a.amax, a.sg, o);
+                       nblocks, a.amax, a.sg, out, ws);
   else
     hipLaunchKernelGGL(dq_amax_kernel<FMT_E4M3>, dim3((unsigned)grid), bd, 0, s, c, sc, npairs,
-                       nblocks, a.amax, a.sg, o);
+                       nblocks, a.amax, a.sg, out, ws);
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 // its quantization), and dequantization followed by the inverse transform.
 // The quantization of the transformed tensor itself is in quantize.hip (the
 // transform runs in registers inside the block quantizers).
+#include "grid_reduce.hpp"
 #include "quantize_core.hpp"
 
 namespace nvfp4 {
@@ -13,22 +14,11 @@ namespace nvfp4 {
 constexpr int kRhtThreads = 1024;
 constexpr int kRhtUnroll = 2;
 
-// Workgroup maximum of m folded into *out (one atomic, skipped when the
-// running maximum already covers it).
-__device__ __forceinline__ void rht_amax_flush(uint32_t m, uint32_t* out) {
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
-    m = m > o ? m : o;
-  }
-  __shared__ uint32_t red[kRhtThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-    for (int w = 1; w < kRhtThreads / 64; ++w) r = r > red[w] ? r : red[w];
-    const uint32_t cur = __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (r > cur) atomicMax(out, r);
-  }
+// The grid maximum of the per-lane maxima m (sign-cleared binary32 patterns)
+// written to *out by the last workgroup (grid_reduce.hpp).
+__device__ __forceinline__ void rht_amax_flush(uint32_t m, float* out, uint8_t* ws) {
+  uint32_t r;
+  if (grid_reduce<MaxU32, kRhtThreads>(ws, m, &r)) out[0] = __uint_as_float(r);
 }
 
 // Largest sign-cleared binary32 pattern of a transformed block (NaN beats
@@ -46,7 +36,7 @@ __device__ __forceinline__ uint32_t block_max_bits(const float (&y)[16]) {
 // Row blocks: a lane transforms whole blocks (two 16-byte chunks).
 __global__ void __launch_bounds__(kRhtThreads)
 rht_amax_rows_kernel(const uint4* __restrict__ x, int64_t nblocks, uint32_t signs,
-                     uint32_t* __restrict__ out) {
+                     float* __restrict__ out, uint8_t* __restrict__ ws) {
   uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * kRhtThreads;
   int64_t i = (int64_t)blockIdx.x * kRhtThreads + threadIdx.x;
@@ -73,7 +63,7 @@ rht_amax_rows_kernel(const uint4* __restrict__ x, int64_t nblocks, uint32_t sign
     const uint32_t v = block_max_bits(y);
     m = m > v ? m : v;
   }
-  rht_amax_flush(m, out);
+  rht_amax_flush(m, out, ws);
 }
 
 // Column blocks: a lane transforms the 16 values of one column in one group
@@ -82,7 +72,7 @@ rht_amax_rows_kernel(const uint4* __restrict__ x, int64_t nblocks, uint32_t sign
 // column (16 loads of one bf16).
 __global__ void __launch_bounds__(kRhtThreads)
 rht_amax_cols4_kernel(const uint2* __restrict__ x, int64_t rows, int64_t quads, uint32_t signs,
-                      uint32_t* __restrict__ out) {
+                      float* __restrict__ out, uint8_t* __restrict__ ws) {
   uint32_t m = 0;
   const int64_t items = (rows / 16) * quads;
   const bool narrow = (items >> 32) == 0;
@@ -107,12 +97,12 @@ rht_amax_cols4_kernel(const uint2* __restrict__ x, int64_t rows, int64_t quads, 
       m = m > b ? m : b;
     }
   }
-  rht_amax_flush(m, out);
+  rht_amax_flush(m, out, ws);
 }
 
 __global__ void __launch_bounds__(kRhtThreads)
 rht_amax_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t signs,
-                     uint32_t* __restrict__ out) {
+                     float* __restrict__ out, uint8_t* __restrict__ ws) {
   uint32_t m = 0;
   const int64_t items = (rows / 16) * cols;
   const bool narrow = (items >> 32) == 0;
@@ -128,34 +118,31 @@ rht_amax_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
     const uint32_t v = block_max_bits(y);
     m = m > v ? m : v;
   }
-  rht_amax_flush(m, out);
-}
-
-__global__ void __launch_bounds__(64) rht_amax_init_kernel(uint32_t* out) {
-  if (threadIdx.x == 0) out[0] = 0u;
+  rht_amax_flush(m, out, ws);
 }
 
 hipError_t launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, int axis, uint32_t signs,
-                           float* out, hipStream_t s) {
-  uint32_t* o = reinterpret_cast<uint32_t*>(out);
-  hipLaunchKernelGGL(rht_amax_init_kernel, dim3(1), dim3(64), 0, s, o);
+                           float* out, uint8_t* ws, hipStream_t s) {
   const int64_t items = axis == AXIS_ROW ? rows * cols / 16 : (rows / 16) * cols;
-  if (items == 0) return hipGetLastError();
+  // one workgroup per CU at most (an empty tensor runs one, which writes 0)
+  int64_t cap = (int64_t)device_cu_count();
+  cap = cap < kSlots ? cap : kSlots;
   int64_t grid = (items + kRhtThreads - 1) / kRhtThreads;
-  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (one atomic) per CU
   grid = grid < cap ? grid : cap;
+  if (grid < 1) grid = 1;
   if (axis == AXIS_ROW) {
     hipLaunchKernelGGL(rht_amax_rows_kernel, dim3((unsigned)grid), dim3(kRhtThreads), 0, s,
-                       reinterpret_cast<const uint4*>(x), items, signs, o);
+                       reinterpret_cast<const uint4*>(x), items, signs, out, ws);
   } else if (cols % 4 == 0 && ((uintptr_t)x & 7u) == 0) {
     const int64_t quads = cols / 4;
     int64_t g4 = ((rows / 16) * quads + kRhtThreads - 1) / kRhtThreads;
     g4 = g4 < cap ? g4 : cap;
+    if (g4 < 1) g4 = 1;
     hipLaunchKernelGGL(rht_amax_cols4_kernel, dim3((unsigned)g4), dim3(kRhtThreads), 0, s,
-                       reinterpret_cast<const uint2*>(x), rows, quads, signs, o);
+                       reinterpret_cast<const uint2*>(x), rows, quads, signs, out, ws);
   } else {
     hipLaunchKernelGGL(rht_amax_cols_kernel, dim3((unsigned)grid), dim3(kRhtThreads), 0, s, x, rows,
-                       cols, signs, o);
+                       cols, signs, out, ws);
   }
   return hipGetLastError();
 }

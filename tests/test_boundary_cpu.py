@@ -49,13 +49,19 @@ def test_status_strings():
         assert lib.nvfp4_status_string(s) == text
 
 
-def _q(**kw):
+def _qargs(**kw):
     a = dict(x=FAKE, rows=16, cols=32, amax=FAKE, gmax=0.0, fmt=0, select=1, rnd=0, axes=1,
-             seed=0, codes=FAKE, scales=FAKE, codes_t=FAKE, scales_t=FAKE, count4=None)
+             seed=0, codes=FAKE, scales=FAKE, codes_t=FAKE, scales_t=FAKE, count4=None, ws=None)
     a.update(kw)
-    return N.lib().nvfp4_quantize(a["x"], a["rows"], a["cols"], a["amax"], a["gmax"], a["fmt"],
-                                  a["select"], a["rnd"], a["axes"], a["seed"], a["codes"],
-                                  a["scales"], a["codes_t"], a["scales_t"], a["count4"], None)
+    return N.QuantArgs(x=a["x"], rows=a["rows"], cols=a["cols"], amax=a["amax"],
+                       global_fp8_max=a["gmax"], scale_fmt=a["fmt"], select=a["select"],
+                       rounding=a["rnd"], axes=a["axes"], seed=a["seed"], codes=a["codes"],
+                       scales=a["scales"], codes_t=a["codes_t"], scales_t=a["scales_t"],
+                       count4=a["count4"], workspace=a["ws"])
+
+
+def _q(**kw):
+    return N.lib().nvfp4_quantize(_qargs(**kw), None)
 
 
 @pytest.mark.parametrize("kw", [
@@ -65,32 +71,71 @@ def _q(**kw):
     dict(gmax=-1.0), dict(gmax=float("inf")), dict(gmax=float("nan")),
     dict(codes=None), dict(scales=None), dict(axes=2, rows=24), dict(axes=2, codes_t=None),
     dict(axes=3, scales_t=None), dict(axes=2, cols=20, rows=16), dict(x=FAKE_ODD),
-    dict(codes=FAKE_ODD), dict(scales=FAKE + 2), dict(count4=FAKE_ODD),
+    dict(codes=FAKE_ODD), dict(scales=FAKE + 2), dict(count4=FAKE_ODD, ws=FAKE),
     dict(rows=1 << 40, cols=1 << 40),
+    # the 4/6 count needs a workspace, 16-byte aligned
+    dict(count4=FAKE), dict(count4=FAKE, ws=FAKE_ODD),
 ])
 def test_quantize_rejects(kw):
     assert _q(**kw) == N.ERR_INVALID
+
+
+def test_quantize_rejects_null_args():
+    assert N.lib().nvfp4_quantize(None, None) == N.ERR_INVALID
 
 
 def test_quantize_empty_is_ok_without_launch():
     assert _q(rows=0) == N.OK
     assert _q(cols=0) == N.OK
     assert _q(rows=0, axes=3) == N.OK
+    assert _q(rows=0, count4=FAKE, ws=FAKE) == N.OK
+
+
+def test_quant_args_layout_matches_the_header(tmp_path):
+    """ctypes' QuantArgs has the C layout of nvfp4_quant_args: a host program
+    built from the header prints every field's offset and the size."""
+    fields = [f for f, _ in N.QuantArgs._fields_]
+    c_name = {"global_fp8_max": "global_fp8_max"}
+    src = tmp_path / "layout.c"
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "nvfp4.h"', "int main(void) {"]
+    for f in fields:
+        lines.append(f'  printf("%zu\\n", offsetof(nvfp4_quant_args, {c_name.get(f, f)}));')
+    lines += ['  printf("%zu\\n", sizeof(nvfp4_quant_args));', "  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    r = subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include",
+                        "-I/opt/rocm/include", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip(f"cannot build a host program against the HIP headers: {r.stderr[:200]}")
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [getattr(N.QuantArgs, f).offset for f in fields] + [ctypes.sizeof(N.QuantArgs)]
+    assert got == want
+
+
+def test_workspace_size_agrees():
+    hdr = open(HEADERS[0]).read()
+    n = int(re.search(r"#define NVFP4_WORKSPACE_BYTES (\d+)", hdr).group(1))
+    assert N.lib().nvfp4_workspace_bytes() == N.WORKSPACE_BYTES == n
 
 
 def _dq(**kw):
     a = dict(codes=FAKE, scales=FAKE, rows=16, cols=32, amax=FAKE, gmax=448.0, fmt=0,
-             f32=FAKE, b16=None, bs=None, xref=None, sse=None)
+             f32=FAKE, b16=None, bs=None, xref=None, sse=None, ws=None)
     a.update(kw)
     return N.lib().nvfp4_dequantize(a["codes"], a["scales"], a["rows"], a["cols"], a["amax"],
                                     a["gmax"], a["fmt"], a["f32"], a["b16"], a["bs"], a["xref"],
-                                    a["sse"], None)
+                                    a["sse"], a["ws"], None)
 
 
 @pytest.mark.parametrize("kw", [
     dict(codes=None), dict(scales=None), dict(amax=None), dict(cols=8), dict(rows=-2),
-    dict(fmt=5), dict(gmax=0.0), dict(gmax=-3.0), dict(xref=FAKE), dict(sse=FAKE),
-    dict(f32=FAKE_ODD), dict(sse=FAKE_ODD, xref=FAKE),
+    dict(fmt=5), dict(gmax=0.0), dict(gmax=-3.0), dict(xref=FAKE, ws=FAKE), dict(sse=FAKE, ws=FAKE),
+    dict(f32=FAKE_ODD), dict(sse=FAKE_ODD, xref=FAKE, ws=FAKE),
+    # the error report needs a workspace, 16-byte aligned
+    dict(sse=FAKE, xref=FAKE), dict(sse=FAKE, xref=FAKE, ws=FAKE_ODD),
 ])
 def test_dequantize_rejects(kw):
     assert _dq(**kw) == N.ERR_INVALID
@@ -98,14 +143,17 @@ def test_dequantize_rejects(kw):
 
 def test_dequantize_empty_ok():
     assert _dq(rows=0) == N.OK
+    assert _dq(rows=0, sse=FAKE, xref=FAKE, ws=FAKE) == N.OK
 
 
 def test_amax_rejects():
     lib = N.lib()
-    assert lib.nvfp4_tensor_amax(FAKE, -1, FAKE, None) == N.ERR_INVALID
-    assert lib.nvfp4_tensor_amax(None, 16, FAKE, None) == N.ERR_INVALID
-    assert lib.nvfp4_tensor_amax(FAKE, 16, None, None) == N.ERR_INVALID
-    assert lib.nvfp4_tensor_amax(FAKE_ODD, 16, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE, -1, FAKE, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(None, 16, FAKE, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE, 16, None, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE_ODD, 16, FAKE, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE, 16, FAKE, None, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE, 16, FAKE, FAKE_ODD, None) == N.ERR_INVALID
 
 
 def test_fakequant_rejects():
@@ -137,19 +185,17 @@ def test_row_amax_rejects():
 
 
 def _qrs(**kw):
-    a = dict(x=FAKE, rows=16, cols=32, ra=FAKE, gmax=0.0, fmt=0, select=1, rnd=0, seed=0,
-             codes=FAKE, scales=FAKE, count4=None)
-    a.update(kw)
-    return N.lib().nvfp4_quantize_rowscaled(a["x"], a["rows"], a["cols"], a["ra"], a["gmax"],
-                                            a["fmt"], a["select"], a["rnd"], a["seed"],
-                                            a["codes"], a["scales"], a["count4"], None)
+    kw.setdefault("ra", FAKE)
+    kw["amax"] = kw.pop("ra")
+    return N.lib().nvfp4_quantize_rowscaled(_qargs(**kw), None)
 
 
 @pytest.mark.parametrize("kw", [
     dict(x=None), dict(ra=None), dict(rows=-1), dict(cols=24), dict(fmt=2), dict(select=5),
     dict(rnd=2), dict(rnd=1, select=1), dict(rnd=1, select=4), dict(gmax=-1.0), dict(gmax=float("nan")),
     dict(codes=None), dict(scales=None), dict(codes=FAKE_ODD), dict(scales=FAKE + 2),
-    dict(x=FAKE_ODD), dict(ra=FAKE + 2), dict(count4=FAKE_ODD),
+    dict(x=FAKE_ODD), dict(ra=FAKE + 2), dict(count4=FAKE_ODD, ws=FAKE), dict(count4=FAKE),
+    dict(axes=2), dict(axes=3),
 ])
 def test_quantize_rowscaled_rejects(kw):
     assert _qrs(**kw) == N.ERR_INVALID
@@ -161,34 +207,32 @@ def test_quantize_rowscaled_empty_ok():
 
 def _dqrs(**kw):
     a = dict(codes=FAKE, scales=FAKE, rows=16, cols=32, ra=FAKE, gmax=448.0, fmt=0,
-             f32=FAKE, b16=None, bs=None, xref=None, sse=None)
+             f32=FAKE, b16=None, bs=None, xref=None, sse=None, ws=None)
     a.update(kw)
     return N.lib().nvfp4_dequantize_rowscaled(a["codes"], a["scales"], a["rows"], a["cols"],
                                               a["ra"], a["gmax"], a["fmt"], a["f32"], a["b16"],
-                                              a["bs"], a["xref"], a["sse"], None)
+                                              a["bs"], a["xref"], a["sse"], a["ws"], None)
 
 
 @pytest.mark.parametrize("kw", [
     dict(codes=None), dict(ra=None), dict(cols=8), dict(fmt=3), dict(gmax=0.0),
-    dict(xref=FAKE), dict(f32=FAKE_ODD), dict(ra=FAKE + 2),
+    dict(xref=FAKE, ws=FAKE), dict(f32=FAKE_ODD), dict(ra=FAKE + 2), dict(xref=FAKE, sse=FAKE),
 ])
 def test_dequantize_rowscaled_rejects(kw):
     assert _dqrs(**kw) == N.ERR_INVALID
 
 
 def _q2d(**kw):
-    a = dict(x=FAKE, rows=32, cols=32, amax=FAKE, gmax=0.0, fmt=0, codes=FAKE, scales=FAKE,
-             codes_t=FAKE, scales_t=FAKE)
+    a = dict(rows=32, cols=32, select=0, axes=3)
     a.update(kw)
-    return N.lib().nvfp4_quantize_2d(a["x"], a["rows"], a["cols"], a["amax"], a["gmax"],
-                                     a["fmt"], a["codes"], a["scales"], a["codes_t"],
-                                     a["scales_t"], None)
+    return N.lib().nvfp4_quantize_2d(_qargs(**a), None)
 
 
 @pytest.mark.parametrize("kw", [
     dict(x=None), dict(amax=None), dict(rows=24), dict(cols=8), dict(fmt=2), dict(gmax=-2.0),
     dict(codes=None), dict(scales=None), dict(codes_t=None), dict(scales_t=None),
     dict(codes_t=FAKE_ODD), dict(codes=FAKE_ODD), dict(x=FAKE_ODD), dict(amax=FAKE + 2),
+    dict(select=1), dict(rnd=1), dict(axes=2),
 ])
 def test_quantize_2d_rejects(kw):
     assert _q2d(**kw) == N.ERR_INVALID
@@ -196,7 +240,7 @@ def test_quantize_2d_rejects(kw):
 
 def test_quantize_2d_empty_ok():
     assert _q2d(rows=0) == N.OK
-    assert _q2d(codes_t=None, scales_t=None, rows=0) == N.OK
+    assert _q2d(codes_t=None, scales_t=None, rows=0, axes=1) == N.OK
 
 
 def _rq(**kw):
@@ -228,15 +272,30 @@ def test_requantize_t_empty_ok():
 
 @pytest.mark.parametrize("kw", [
     dict(codes=None), dict(amax=None), dict(ra=FAKE), dict(cols=8), dict(fmt=4), dict(gmax=-1.0),
-    dict(out=None), dict(out=FAKE + 1),
+    dict(out=None), dict(out=FAKE + 1), dict(ws=None), dict(ws=FAKE_ODD),
 ])
 def test_dequantized_amax_rejects(kw):
     a = dict(codes=FAKE, scales=FAKE, rows=16, cols=32, amax=FAKE, ra=None, gmax=448.0, fmt=0,
-             out=FAKE)
+             out=FAKE, ws=FAKE)
     a.update(kw)
     assert N.lib().nvfp4_dequantized_amax(a["codes"], a["scales"], a["rows"], a["cols"],
                                           a["amax"], a["ra"], a["gmax"], a["fmt"], a["out"],
-                                          None) == N.ERR_INVALID
+                                          a["ws"], None) == N.ERR_INVALID
+
+
+def test_rht_calls_reject():
+    lib = N.lib()
+    f = lib.nvfp4_rht_amax
+    assert f(FAKE, 16, 32, 1, 0, FAKE, None, None) == N.ERR_INVALID  # no workspace
+    assert f(FAKE, 16, 32, 3, 0, FAKE, FAKE, None) == N.ERR_INVALID  # one axis only
+    assert f(FAKE, 16, 24, 1, 0, FAKE, FAKE, None) == N.ERR_INVALID
+    assert f(FAKE, 24, 32, 2, 0, FAKE, FAKE, None) == N.ERR_INVALID
+    q = lib.nvfp4_quantize_rht
+    assert q(_qargs(axes=3), 0, None) == N.ERR_INVALID
+    assert q(_qargs(axes=2, rows=24), 0, None) == N.ERR_INVALID
+    assert q(_qargs(count4=FAKE), 0, None) == N.ERR_INVALID
+    assert q(None, 0, None) == N.ERR_INVALID
+    assert q(_qargs(rows=0), 0, None) == N.OK
 
 
 @pytest.mark.parametrize("entry", ["nvfp4_fakequant_fwd_amax", "nvfp4_fakequant_bwd_amax"])

@@ -20,7 +20,16 @@ from nvfp4_block_scaled_02_amd import synth  # noqa: E402
 FMTS = {"e4m3": O.FMT_E4M3, "ue5m3": O.FMT_UE5M3}
 SELS = {"6": O.SELECT_6, "4over6": O.SELECT_4OVER6}
 RNDS = {"rne": O.ROUND_RNE, "sr": O.ROUND_SR}
-SSE_REL = 1e-6
+# The error report: both sides take each residual x - x_hat in binary64 the
+# same way and sum n non-negative terms in binary64, the oracle in index order
+# and the device in its fixed blocked order.  Any order of summing n
+# non-negative terms is within (n - 1) u of the exact sum (u = 2^-53), and the
+# oracle rounds each square once more than the device's fma: the two reports
+# differ by at most 3 n u relative.
+
+
+def sse_rel(n):
+    return 3.0 * n * 2.0 ** -53
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -158,7 +167,7 @@ def test_dequantize_rowscaled(rows, cols):
     _same(xh16.cpu().view(torch.int16).numpy().view(np.uint16), ref16, "x_hat bf16")
     _same(bs.cpu().numpy().view(np.uint32), rbs.view(np.uint32), "block scales")
     rsse = O.sse(O.as_f32(xb), ref)
-    assert abs(float(sse.item()) - rsse) <= SSE_REL * rsse
+    assert abs(float(sse.item()) - rsse) <= sse_rel(xb.size) * rsse
 
 
 # ---------------------------------------------------------------- 16x16 tile scales

@@ -121,6 +121,22 @@ int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* w
                       hipStream_t stream);
 
 /*
+ * nvfp4_tensor_amax_noalloc -- nvfp4_tensor_amax without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workgroups' maxima meet in a static array the library holds on each GPU
+ * (NVFP4_WORKSPACE_BYTES per GPU, kept until the process ends); the call
+ * allocates nothing.  Every call on one GPU shares that array, so calls that
+ * overlap on one GPU (several streams) race; calls in one stream do not.
+ * Arguments and result as nvfp4_tensor_amax; any numel.  Errors: as
+ * nvfp4_tensor_amax, plus NVFP4_ERR_UNSUPPORTED on a GPU with more than 8192
+ * compute units (more workgroups than the array has slots) and
+ * NVFP4_ERR_HIP if the array's device address cannot be obtained.
+ */
+int nvfp4_tensor_amax_noalloc(const uint16_t* x, int64_t numel, float* amax_out,
+                              hipStream_t stream);
+
+/*
  * Arguments of the quantize calls: one struct, so that the outputs of the
  * row-wise and column-wise layouts, the optional 4/6 count and its
  * workspace travel together.

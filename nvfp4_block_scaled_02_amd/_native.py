@@ -45,6 +45,7 @@ SIGNATURES = {
     "nvfp4_status_string": (ctypes.c_char_p, [_int]),
     "nvfp4_workspace_bytes": (ctypes.c_size_t, []),
     "nvfp4_tensor_amax": (_int, [_vp, _i64, _vp, _vp, _vp]),
+    "nvfp4_tensor_amax_noalloc": (_int, [_vp, _i64, _vp, _vp]),
     "nvfp4_quantize": (_int, [_qa, _vp]),
     "nvfp4_dequantize": (_int, [_vp, _vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp]),

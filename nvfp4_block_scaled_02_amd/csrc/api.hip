@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/nvfp4.h"
 #include "../../include/nvfp4_testing.h"
@@ -88,6 +89,36 @@ static unsigned test_grid(int64_t n) {
   return (unsigned)(g < 1 ? 1 : (g < cap ? g : cap));
 }
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of nvfp4_tensor_amax_noalloc: one array per GPU, in the
+// library's own device memory (it is zero at load, like every static object,
+// and every call that completes leaves its counters zero again).  Host code
+// never uses the array's name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<uint8_t*> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, or nullptr.
+static uint8_t* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+      return nullptr;
+    p = static_cast<uint8_t*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -125,6 +156,18 @@ int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* w
   if (numel > 0 && (!x || !aligned16(x))) return NVFP4_ERR_INVALID;
   if (((uintptr_t)amax_out & 3u) != 0) return NVFP4_ERR_INVALID;
   return status_of(launch_tensor_amax(x, numel, amax_out, static_cast<uint8_t*>(workspace), stream));
+}
+
+int nvfp4_tensor_amax_noalloc(const uint16_t* x, int64_t numel, float* amax_out,
+                              hipStream_t stream) {
+  if (numel < 0 || !amax_out) return NVFP4_ERR_INVALID;
+  if (numel > 0 && (!x || !aligned16(x))) return NVFP4_ERR_INVALID;
+  if (((uintptr_t)amax_out & 3u) != 0) return NVFP4_ERR_INVALID;
+  // the kernel's grid (one workgroup per CU at most) must fit the scratch's slots
+  if (device_cu_count() > kSlots) return NVFP4_ERR_UNSUPPORTED;
+  uint8_t* ws = scratch_of_current_device();
+  if (!ws) return NVFP4_ERR_HIP;
+  return status_of(launch_tensor_amax(x, numel, amax_out, ws, stream));
 }
 
 // Checks shared by the quantize calls; fills the kernel-side arguments.

@@ -12,6 +12,7 @@ the 4/6 count, the squared-error report) need a workspace: by default one
 zero-filled buffer per (device, stream) is created on first use and reused
 (every call leaves it zeroed); ``workspace=`` passes another one.
 """
+import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
@@ -89,16 +90,43 @@ def _ws(given: Optional[torch.Tensor], dev):
     return given
 
 
+class Launch:
+    """One entry point with its arguments checked once: each call issues the
+    launch again on `stream` (default: the current stream of the device)
+    without re-checking anything.  It keeps its tensors alive.  For loops
+    that launch the same call many times (serving, graph capture, timing)."""
+
+    def __init__(self, entry: str, args: tuple, device, keep):
+        self._fn = getattr(N.lib(), entry)
+        self._entry = entry
+        self._args = args
+        self._device = device
+        self._keep = keep
+
+    def __call__(self, stream=None):
+        s = stream if stream is not None else _stream(self._device)
+        st = self._fn(*self._args, s)
+        if st != N.OK:
+            N.check(st, self._entry)
+
+
+def prepare_tensor_amax(x: torch.Tensor, out: torch.Tensor, *,
+                        workspace: Optional[torch.Tensor] = None) -> Launch:
+    """tensor_amax(x, out) as a Launch."""
+    _need(x, torch.bfloat16, "x")
+    _need(out, torch.float32, "out", 1)
+    ws = _ws(workspace, x.device)
+    return Launch("nvfp4_tensor_amax", (_ptr(x), x.numel(), _ptr(out), _ptr(ws)), x.device,
+                  (x, out, ws))
+
+
 def tensor_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None, *,
                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """max |x| over a bf16 tensor, as a 1-element float32 device tensor."""
     _need(x, torch.bfloat16, "x")
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=x.device)
-    _need(out, torch.float32, "out", 1)
-    ws = _ws(workspace, x.device)
-    N.check(N.lib().nvfp4_tensor_amax(_ptr(x), x.numel(), _ptr(out), _ptr(ws), _stream(x.device)),
-            "nvfp4_tensor_amax")
+    prepare_tensor_amax(x, out, workspace=workspace)()
     return out
 
 
@@ -145,6 +173,24 @@ def _quant_args(x, rows, cols, amax, global_max, fmt, select, rounding, ax, seed
         count4=_ptr(out.get("count4")), workspace=_ptr(ws) if "count4" in out else None)
 
 
+def prepare_quantize(x: torch.Tensor, amax: torch.Tensor, *, fmt: str = "e4m3",
+                     select: str = "4over6", rounding: str = "rne", axes: str = "row",
+                     seed: int = 0, global_max: float = 0.0, count4: bool = False,
+                     out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None):
+    """quantize() as a Launch: returns (launch, Quantized) with the outputs
+    the launch writes."""
+    rows, cols = _need_2d(x, torch.bfloat16, "x")
+    _need(amax, torch.float32, "amax", 1)
+    ax = _AXES[axes]
+    out = _quant_outputs(out, rows, cols, ax, count4, x.device)
+    ws = _ws(workspace, x.device) if "count4" in out else None
+    args = _quant_args(x, rows, cols, amax, global_max, fmt, select, rounding, ax, seed, out, ws)
+    gm = float(global_max) if global_max else default_global_max(fmt, select)
+    q = Quantized(out.get("codes"), out.get("scales"), out.get("codes_t"), out.get("scales_t"),
+                  amax, gm, fmt, out.get("count4"))
+    return Launch("nvfp4_quantize", (ctypes.byref(args),), x.device, (x, amax, out, ws, args)), q
+
+
 def quantize(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: str = "e4m3",
              select: str = "4over6", rounding: str = "rne", axes: str = "row", seed: int = 0,
              global_max: float = 0.0, count4: bool = False, out: Optional[dict] = None,
@@ -153,18 +199,14 @@ def quantize(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: str =
     tensor (default: the fresh tensor amax).  axes: "row", "col" or "both".
     out: optional preallocated {"codes", "scales", "codes_t", "scales_t",
     "count4"} tensors (count4 is added to, not cleared)."""
-    rows, cols = _need_2d(x, torch.bfloat16, "x")
+    _need_2d(x, torch.bfloat16, "x")
     if amax is None:
         amax = tensor_amax(x, workspace=workspace)
-    _need(amax, torch.float32, "amax", 1)
-    ax = _AXES[axes]
-    out = _quant_outputs(out, rows, cols, ax, count4, x.device)
-    ws = _ws(workspace, x.device) if "count4" in out else None
-    args = _quant_args(x, rows, cols, amax, global_max, fmt, select, rounding, ax, seed, out, ws)
-    N.check(N.lib().nvfp4_quantize(args, _stream(x.device)), "nvfp4_quantize")
-    gm = float(global_max) if global_max else default_global_max(fmt, select)
-    return Quantized(out.get("codes"), out.get("scales"), out.get("codes_t"),
-                     out.get("scales_t"), amax, gm, fmt, out.get("count4"))
+    launch, q = prepare_quantize(x, amax, fmt=fmt, select=select, rounding=rounding, axes=axes,
+                                 seed=seed, global_max=global_max, count4=count4, out=out,
+                                 workspace=workspace)
+    launch()
+    return q
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
@@ -175,6 +217,22 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
     """x_hat = q * D[scale] * alpha.  Returns x_hat (or None if out_dtype is
     None), plus the per-block effective scales if asked, plus the binary64
     SSE tensor if x_ref is given (sse, if passed, is overwritten)."""
+    launch, res = prepare_dequantize(codes, scales, amax, global_max=global_max, fmt=fmt,
+                                     out_dtype=out_dtype, want_block_scale=want_block_scale,
+                                     x_ref=x_ref, sse=sse, out=out, workspace=workspace,
+                                     _entry=_entry)
+    launch()
+    return res
+
+
+def prepare_dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
+                       global_max: float, fmt: str = "e4m3", out_dtype=torch.float32,
+                       want_block_scale: bool = False, x_ref: Optional[torch.Tensor] = None,
+                       sse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       _entry: str = "nvfp4_dequantize"):
+    """dequantize() as a Launch: returns (launch, result) with the result
+    dequantize() would return."""
     rows, half = _need_2d(codes, torch.uint8, "codes")
     cols = 2 * half
     _need(scales, torch.uint8, "scales", rows * (cols // 16))
@@ -199,17 +257,16 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
             sse = torch.empty(1, dtype=torch.float64, device=dev)
         _need(sse, torch.float64, "sse", 1)
         ws = _ws(workspace, dev)
-    st = getattr(N.lib(), _entry)(_ptr(codes), _ptr(scales), rows, cols, _ptr(amax),
-                                  float(global_max), _FMT[fmt], _ptr(of32), _ptr(ob16), _ptr(bs),
-                                  _ptr(x_ref), _ptr(sse) if x_ref is not None else None,
-                                  _ptr(ws), _stream(dev))
-    N.check(st, _entry)
+    args = (_ptr(codes), _ptr(scales), rows, cols, _ptr(amax), ctypes.c_float(float(global_max)),
+            _FMT[fmt], _ptr(of32), _ptr(ob16), _ptr(bs), _ptr(x_ref),
+            _ptr(sse) if x_ref is not None else None, _ptr(ws))
     res = [out]
     if want_block_scale:
         res.append(bs)
     if x_ref is not None:
         res.append(sse)
-    return res[0] if len(res) == 1 else tuple(res)
+    keep = (codes, scales, amax, out, bs, x_ref, sse, ws)
+    return Launch(_entry, args, dev, keep), (res[0] if len(res) == 1 else tuple(res))
 
 
 # ---------------------------------------------------------------- per-row outer scales

@@ -17,10 +17,14 @@
 // zero before a launch; every launch that runs to completion leaves them
 // zero.  Launches that use one workspace must not overlap.
 //
-// Ordering: the arrivals are agent-scope acquire-release read-modify-writes,
-// so a workgroup's slot store happens-before the last workgroup's reads of
-// it (HIP memory model; on gfx950 the release writes back and the acquire
-// invalidates this XCD's L2 as needed).
+// Ordering without cache maintenance: every access to a slot or a counter is
+// a device-scope atomic read-modify-write, performed where the address is
+// coherent for the whole GPU (all XCDs).  A workgroup publishes its slot with
+// an exchange and arrives only after the exchange has returned (so it has
+// been performed); the last workgroup reads the slots with read-modify-writes
+// after its own arrival has returned.  No release or acquire fence is needed,
+// so no XCD's L2 is written back or invalidated (a fence per workgroup costs
+// microseconds when the kernel's outputs are still dirty in L2).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,25 +45,30 @@ __device__ __forceinline__ bool grid_arrive(uint8_t* ws, uint64_t value) {
   const uint32_t G = gridDim.x, b = blockIdx.x;
   uint64_t* slots = reinterpret_cast<uint64_t*>(ws);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + kCtrOffset);
-  __hip_atomic_store(&slots[b], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t prev = __hip_atomic_exchange(&slots[b], value, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  // consume the exchange's result: the arrival below is issued only once the
+  // exchange has returned
+  __asm__ volatile("" :: "v"((uint32_t)prev), "v"((uint32_t)(prev >> 32)) : "memory");
   const uint32_t grp = b % kGroups;
   const uint32_t gsize = G / kGroups + (grp < G % kGroups ? 1u : 0u);
   const uint32_t ngroups = G < (uint32_t)kGroups ? G : (uint32_t)kGroups;
   uint32_t* gc = ctr + grp * kCtrStride;
-  if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != gsize - 1)
+  if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gsize - 1)
     return false;
   // every member of this group has arrived: no further update in this launch
-  __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_exchange(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t* top = ctr + kGroups * kCtrStride;
-  if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1)
+  if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1)
     return false;
-  __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_exchange(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
-__device__ __forceinline__ uint64_t slot_load(const uint8_t* ws, uint32_t i) {
-  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(ws) + i, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+// Slot i, read with a read-modify-write (adds 0) where it is coherent.
+__device__ __forceinline__ uint64_t slot_load(uint8_t* ws, uint32_t i) {
+  return __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(ws) + i, (uint64_t)0, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The combinations: an identity, a binary operation, and the slot encoding.
@@ -136,6 +145,44 @@ __device__ __forceinline__ bool grid_reduce(uint8_t* ws, typename R::T v, typena
   for (int i = 1; i < BLOCK / 64; ++i) t = R::op(t, red[i]);
   *total = t;
   return true;
+}
+
+// A grid sum of non-negative integers below 2^40 per launch, added to *out:
+// each workgroup's part travels inside its arrival (one 64-bit add of
+// 2^40 + part to its group word: arrivals in the high bits, the running sum
+// in the low 40), so a workgroup waits on one atomic round trip, the last of
+// a group on two, and no slot is written or read.  The group words and the
+// top word are the first kGroups + 1 counter lines of the workspace, viewed
+// as 64-bit words (zero on entry, zero again on exit).  Every thread of every
+// workgroup calls it once with its own part.
+template <int BLOCK>
+__device__ __forceinline__ void grid_count_add(uint8_t* ws, uint32_t part,
+                                               unsigned long long* out) {
+  static_assert(BLOCK % 64 == 0 && BLOCK <= 1024, "whole wavefronts");
+  constexpr uint64_t kOne = 1ull << 40, kLow = kOne - 1;
+  __shared__ uint32_t red[BLOCK / 64];
+  for (int off = 32; off >= 1; off >>= 1) part += (uint32_t)__shfl_xor((int)part, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  uint64_t t = 0;
+  for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
+  const uint32_t G = gridDim.x, b = blockIdx.x;
+  uint64_t* words = reinterpret_cast<uint64_t*>(ws + kCtrOffset);
+  const uint32_t grp = b % kGroups;
+  const uint32_t gsize = G / kGroups + (grp < G % kGroups ? 1u : 0u);
+  const uint32_t ngroups = G < (uint32_t)kGroups ? G : (uint32_t)kGroups;
+  uint64_t* gw = words + grp * (kCtrStride / 2);
+  const uint64_t g = __hip_atomic_fetch_add(gw, kOne + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((g >> 40) != gsize - 1) return;
+  __hip_atomic_exchange(gw, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t gsum = (g & kLow) + t;
+  uint64_t* top = words + kGroups * (kCtrStride / 2);
+  const uint64_t a = __hip_atomic_fetch_add(top, kOne + gsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((a >> 40) != ngroups - 1) return;
+  __hip_atomic_exchange(top, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t total = (a & kLow) + gsum;
+  if (total != 0) atomicAdd(out, (unsigned long long)total);
 }
 
 }  // namespace nvfp4

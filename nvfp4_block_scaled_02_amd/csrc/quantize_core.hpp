@@ -414,14 +414,13 @@ __device__ __forceinline__ uint32_t hash_base(uint64_t seed, uint64_t idx0, uint
   return (uint32_t)idx0 ^ key;
 }
 
-// Adds the grid's per-lane 4/6 counts to *count4: the workgroups' sums meet
-// in the workspace (grid_reduce.hpp) and the last workgroup adds the total
-// with one atomic, so a counting launch keeps the launch shape of a
-// non-counting one.  Every workgroup of the grid must call it.
+// Adds the grid's per-lane 4/6 counts to *count4 in the same launch
+// (grid_count_add: the count rides on each workgroup's arrival), so a
+// counting launch keeps the launch shape of a non-counting one.  Every
+// workgroup of the grid must call it.
 template <int BLOCK>
 __device__ __forceinline__ void flush_count(unsigned long long* count4, uint32_t n4, uint8_t* ws) {
-  uint64_t total;
-  if (grid_reduce<SumU64, BLOCK>(ws, (uint64_t)n4, &total) && total != 0) atomicAdd(count4, total);
+  grid_count_add<BLOCK>(ws, n4, count4);
 }
 
 // Writes the wavefront's 128 chunks (lane l: chunks l and 64 + l) to its LDS

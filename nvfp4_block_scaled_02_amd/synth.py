@@ -11,6 +11,9 @@ to bfloat16 with round-to-nearest-even through torch):
   activation  8192 x 4096 Student-t(3) x 0.5; 8 fixed channels x 50       (seed 2)
   qat         W 14336 x 4096 N(0,0.02) bf16; G N(0,1e-3) float32          (seed 3)
   gradient    16384 x 8192 N(0,1) x per-row 10^U(-3,0)                    (seed 4)
+  heavy       4096 x 4096  N(0,1) x per-element U(1,9): the heavy-tailed
+              activation stand-in of the "UE5M3" blog's scale-format
+              experiment (实验)                                          (seed 5)
 `rows` gives a smaller instance of the same recipe (per-row factors, outlier
 channels and outlier positions are drawn at the full shape first, so the kept
 rows see the same ones).  No public dataset
@@ -27,8 +30,9 @@ SHAPES = {
     "activation": (8192, 4096),
     "qat": (14336, 4096),
     "gradient": (16384, 8192),
+    "heavy": (4096, 4096),
 }
-SEEDS = {"weight-1k": 0, "weight": 1, "activation": 2, "qat": 3, "gradient": 4}
+SEEDS = {"weight-1k": 0, "weight": 1, "activation": 2, "qat": 3, "gradient": 4, "heavy": 5}
 
 
 def to_bf16_bits(a) -> np.ndarray:
@@ -67,6 +71,8 @@ def make(name: str, rows: int = None):
     elif name == "gradient":
         f = 10.0 ** rng.uniform(-3.0, 0.0, size=R)
         x = rng.standard_normal((r, C)) * f[:r, None]
+    elif name == "heavy":
+        x = rng.standard_normal((r, C)) * rng.uniform(1.0, 9.0, size=(r, C))
     else:
         raise KeyError(name)
     return {"x": to_bf16_bits(x)}

@@ -132,6 +132,8 @@ def _load():
                                       ctypes.c_int, ctypes.c_uint64, _f32p]
     lib.or_num_threads.restype = ctypes.c_int
     lib.or_num_threads.argtypes = []
+    lib.or_set_num_threads.restype = None
+    lib.or_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -202,6 +204,12 @@ def f32_to_bf16(f):
 
 def num_threads():
     return _load().or_num_threads()
+
+
+def set_num_threads(n):
+    """OpenMP threads of the oracle's parallel loops (results do not depend
+    on it)."""
+    _load().or_set_num_threads(int(n))
 
 
 def default_global_max(fmt, select):

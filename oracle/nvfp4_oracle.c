@@ -991,3 +991,12 @@ int or_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets that number (n >= 1); the results do not depend on it. */
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

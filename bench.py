@@ -102,11 +102,12 @@ class Timer:
     """HIP events on the stream the kernels are launched on (torch's current
     stream, which the binding passes to every call)."""
 
-    def __init__(self, torch, dev, eager=True):
+    def __init__(self, torch, dev, eager=True, profile=False):
         self.torch = torch
         self.stream = torch.cuda.current_stream(dev)
         self.modes = {}
         self.eager = eager
+        self.profile = profile
 
     def settle(self, fn, seconds=1.0):
         """Runs fn(i) for about `seconds` of wall time: the GPU's clocks
@@ -128,8 +129,14 @@ class Timer:
         graphs enabled the calls are captured into a HIP graph (kernel nodes
         only: every output and the workspace are preallocated) and its
         replays are timed instead; if the capture fails the calls run
-        eagerly."""
+        eagerly.  In profile mode (--profile-once) fn(0) and fn(1) run once
+        each, untimed, for the PMC counters."""
         torch = self.torch
+        if self.profile:
+            fn(0)
+            fn(1 % nsets)
+            torch.cuda.synchronize()
+            return 1.0
         for i in range(max(nsets, 8)):
             fn(i)
         torch.cuda.synchronize()
@@ -170,16 +177,22 @@ class Timer:
         return times[len(times) // 2]
 
 
-def profile_once(torch, dev, launches, nsets):
-    """One 256 MiB copy (the reference for the PMC byte counters), then each
-    launch of the step on two buffer sets, in step order."""
+def calibration_copy(torch, dev):
+    """One 256 MiB device copy: the reference the PMC byte counters are scaled
+    by (the copy reads and writes 256 MiB)."""
     big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     torch.empty_like(big).copy_(big)
+    torch.cuda.synchronize()
+    del big
+
+
+def profile_once(torch, dev, launches, nsets):
+    """Each launch of the step on two buffer sets, in step order."""
     for i in range(2):
         for f in launches:
             f(i % nsets)
     torch.cuda.synchronize()
-    log(f"profile-once done: one 256 MiB copy, {len(launches)} launches x 2")
+    log(f"profile-once done: {len(launches)} launches x 2")
 
 
 def kernel_entry(us, n, bpe):
@@ -355,7 +368,8 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
 
     if args.profile_once:
         sse1 = torch.zeros(1, dtype=torch.float64, device=dev)
-        profile_once(torch, dev, [amax_k, quant_k, lambda i: deq_k(i, sse1)], nsets)
+        profile_once(torch, dev, [amax_k, quant_k, lambda i: deq_k(i, sse1), quant_count_k, quant6_k],
+                     nsets)
         return None
 
     def step(i):
@@ -395,6 +409,8 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
     })
     bpe = {"quantize_4over6": B_QUANT, "quantize_4over6_count": B_QUANT, "quantize_6": B_QUANT,
            "tensor_amax": B_AMAX, "dequantize_f32_mse": B_DEQ_MSE}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     log(f"kernels: {json.dumps(kernels)}")
     q = kernels["quantize_4over6"]
@@ -481,6 +497,8 @@ def run_weight(args, torch, np, nv, synth, dev, timer, small):
         step_keys = ["tensor_amax", "quantize_4over6_count"]
         bpe = {"tensor_amax": B_AMAX, "quantize_4over6_count": B_QUANT, "quantize_4over6": B_QUANT}
         metric = "NVFP4 4/6 quantize GB/s at 4096x4096 bf16 weight (with 4/6 count)"
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = sum(us[k] for k in step_keys) / 1e3
     step_bytes = n * sum(bpe[k] for k in step_keys)
@@ -533,6 +551,8 @@ def run_qat(args, torch, np, nv, synth, dev, timer):
     bpe = {"fakequant_fwd_tied": B_FQ_FWD["tied"], "fakequant_bwd_tied": B_FQ_BWD["tied"],
            "fakequant_fwd_dual": B_FQ_FWD["dual"], "fakequant_bwd_dual": B_FQ_BWD["dual"],
            "fakequant_fwd_dual_amax": B_FQ_FWD["dual"], "fakequant_bwd_dual_amax": B_FQ_BWD["dual"]}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = (us["fakequant_fwd_dual"] + us["fakequant_bwd_dual"]) / 1e3
     step_bytes = n * (bpe["fakequant_fwd_dual"] + bpe["fakequant_bwd_dual"])
@@ -574,6 +594,8 @@ def run_activation_pertoken(args, torch, np, nv, synth, dev, timer):
     }
     bpe = {"row_amax": B_AMAX, "quantize_rowscaled_4over6": B_QUANT,
            "dequantize_rowscaled_f32_mse": B_DEQ_MSE}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = sum(us.values()) / 1e3
     step_bytes = n * sum(bpe.values())
@@ -615,6 +637,8 @@ def run_weight_2d(args, torch, np, nv, synth, dev, timer):
             reps, nsets),
     }
     bpe = {"tensor_amax": B_AMAX, "quantize_2d_both": B_FUSED, "quantize_2d_row": B_QUANT}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = (us["tensor_amax"] + us["quantize_2d_both"]) / 1e3
     step_bytes = n * (B_AMAX + B_FUSED)
@@ -669,15 +693,14 @@ def run_requant(args, torch, np, nv, synth, dev, timer):
         c, s, ra = src[i % nsets]
         nv.dequantized_amax(c, s, row_amaxes=ra, global_max=gm, out=dqa[i % nsets], workspace=ws)
 
-    if args.profile_once:
-        profile_once(torch, dev, [rq_mx, dq_amax, rq_nv], nsets)
-        return None
     reps = max(args.steps, 100)
     us = {"requant_t_mxfp8_sr": timer.avg_us(rq_mx, reps, nsets),
           "dequantized_amax": timer.avg_us(dq_amax, reps, nsets),
           "requant_t_nvfp4_sr": timer.avg_us(rq_nv, reps, nsets)}
     bpe = {"requant_t_mxfp8_sr": B_RQ_MX, "dequantized_amax": B_DQ_AMAX,
            "requant_t_nvfp4_sr": B_RQ_NV}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = us["requant_t_mxfp8_sr"] / 1e3
     line = base_line("NVFP4 -> MXFP8 transposed SR re-quantization GB/s at 8192x4096",
@@ -717,6 +740,8 @@ def run_select(args, torch, np, nv, synth, dev, timer):
           "quantize_4over6_mae": timer.avg_us(q("4over6-mae", True), reps, nsets),
           "quantize_4over6_maxerr": timer.avg_us(q("4over6-maxerr", True), reps, nsets),
           "quantize_sweep_mse": timer.avg_us(q("sweep", False), max(args.steps // 10, 5), nsets)}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, B_QUANT) for k in us}
     ms_step = us["quantize_sweep_mse"] / 1e3
     line = base_line("NVFP4 MSE scale sweep (all E4M3 codes) GB/s at 8192x4096 bf16",
@@ -771,6 +796,8 @@ def run_rht(args, torch, np, nv, synth, dev, timer):
     }
     bpe = {"rht_amax_col": B_AMAX, "quantize_rht_col_4over6": B_QUANT, "rht_amax_row": B_AMAX,
            "quantize_rht_row_4over6": B_QUANT, "dequantize_rht_f32": B_DEQ}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = (us["rht_amax_col"] + us["quantize_rht_col_4over6"]) / 1e3
     line = base_line("NVFP4 RHT + column-wise 4/6 quantize step GB/s at 8192x4096 bf16",
@@ -798,16 +825,6 @@ def run_gradient(args, torch, np, nv, synth, dev, timer):
              "codes_t": torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev),
              "scales_t": torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev)}
             for _ in range(nsets)]
-    if args.profile_once:
-        profile_once(torch, dev, [
-            lambda i: nv.quantize(xs[i], stale, fmt="ue5m3", select="6", rounding="sr",
-                                  axes="both", seed=1234, out=outs[i]),
-            lambda i: nv.quantize(xs[i], stale, fmt="ue5m3", select="6", rounding="sr", axes="row",
-                                  seed=1234, out={"codes": outs[i]["codes"], "scales": outs[i]["scales"]}),
-            lambda i: nv.quantize(xs[i], stale, fmt="ue5m3", select="6", rounding="sr", axes="col",
-                                  seed=1234, out={"codes_t": outs[i]["codes_t"],
-                                                  "scales_t": outs[i]["scales_t"]})], nsets)
-        return None
     reps = max(args.steps, 20)
     us = {
         "quantize_fused_row_col_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
@@ -823,6 +840,8 @@ def run_gradient(args, torch, np, nv, synth, dev, timer):
     }
     bpe = {"quantize_fused_row_col_sr_ue5m3": B_FUSED, "quantize_row_sr_ue5m3": B_QUANT,
            "quantize_col_sr_ue5m3": B_QUANT}
+    if args.profile_once:
+        return None
     kernels = {k: kernel_entry(us[k], n, bpe[k]) for k in us}
     ms_step = us["quantize_fused_row_col_sr_ue5m3"] / 1e3
     line = base_line("NVFP4 fused row+column SR quantize GB/s at 16384x8192 bf16 (UE5M3, stale amax)",
@@ -873,7 +892,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time per-kernel launches by replaying a HIP graph of them")
     ap.add_argument("--profile-once", action="store_true",
-                    help="run a 256 MiB copy and each kernel of the workload twice (for PMC counters)")
+                    help="run a 256 MiB copy, then each timed kernel of the workload twice, untimed "
+                         "(for PMC counters); prints no line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -889,7 +909,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    timer = Timer(torch, dev, eager=not args.graph)
+    timer = Timer(torch, dev, eager=not args.graph, profile=args.profile_once)
+    if args.profile_once:
+        calibration_copy(torch, dev)
     if args.workload == "activation":
         line = run_activation(args, torch, np, nv, synth, dev, timer)
     elif args.workload in ("weight-1k", "weight"):

@@ -305,32 +305,36 @@ quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_b
 // pieces written at different times, cost extra DRAM writes and bandwidth on
 // MI355X; 4-byte pieces per tile, as an unstaged 64-row tile would write for
 // its scales, run at a fraction of the write bandwidth.
-// Loads the lane's chunks of the tile at rows r0.., strip c0.. (chunk
+// Loads the lane's chunks of the tile at rows r0.. of the strip (chunk
 // k = u * kThreads + lane: tile row k / 16, columns (k % 16) * 8 ..+8).  The
 // loads are unconditional, with addresses clamped into the tensor (cols % 8
-// == 0, so a chunk is whole or absent); chunks outside the tensor are zeroed
-// where they are used (tile_chunk).  The number of loads in flight is then
-// the same on every path, so waiting for the oldest tile never waits for the
-// newer ones.
+// == 0, so a chunk is whole or absent): xu is the lane's chunk column in the
+// strip, clamped once per strip; row_off[u] = (tile row of load u) * cols, a
+// per-lane constant, is clamped to the tensor's last row by one minimum
+// against a wavefront-uniform bound (min(a, b) * cols == min(a * cols, b *
+// cols)).  Chunks outside the tensor are zeroed where a partial tile is
+// stored into LDS.  The loads are branch-free so that waiting for the oldest
+// tile never waits for the newer ones.
 constexpr int kLoads = kSW * kTR / kChunk / kThreads;  // 2
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t rows,
-                                          int64_t cols, int64_t r0, int64_t c0,
-                                          uint4 (&w)[kLoads]) {
-#pragma unroll
-  for (int u = 0; u < kLoads; ++u) {
-    const int k = u * kThreads + threadIdx.x;
-    int64_t r = r0 + (k >> 4), c = c0 + (k & 15) * 8;
-    r = r < rows ? r : rows - 1;
-    c = c < cols ? c : cols - 8;
-    w[u] = ld_nt(reinterpret_cast<const uint4*>(x + r * cols + c));
-  }
+constexpr int kLoadRows = kThreads / (kSW / 8);        // tile rows per load (16)
+
+__device__ __forceinline__ bool whole_tile(int64_t rows, int64_t cols, int64_t r0, int64_t c0) {
+  return r0 + kTR <= rows && c0 + kSW <= cols;
 }
 
-__device__ __forceinline__ uint4 tile_chunk(const uint4 (&w)[kLoads], int u, int64_t rows,
-                                            int64_t cols, int64_t r0, int64_t c0) {
-  const int k = u * kThreads + threadIdx.x;
-  const bool ok = r0 + (k >> 4) < rows && c0 + (k & 15) * 8 < cols;
-  return ok ? w[u] : make_uint4(0, 0, 0, 0);
+// (last row of the tile inside the tensor - r0) * cols
+__device__ __forceinline__ int64_t last_row_off(int64_t rows, int64_t cols, int64_t r0) {
+  return (rows - 1 - r0 < kTR - 1 ? rows - 1 - r0 : kTR - 1) * cols;
+}
+
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ xu,
+                                          const int64_t (&row_off)[kLoads], int64_t rows,
+                                          int64_t cols, int64_t r0, uint4 (&w)[kLoads]) {
+  const int64_t lim = last_row_off(rows, cols, r0);
+  const uint16_t* p = xu + r0 * cols;
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u)
+    w[u] = ld_nt(reinterpret_cast<const uint4*>(p + (row_off[u] < lim ? row_off[u] : lim)));
 }
 
 // Amax of 16x16 tile t from its 16 row-block values in LDS (NaN-propagating).
@@ -354,7 +358,9 @@ __device__ __forceinline__ float tile_amax(const float* am, int t) {
 // lane b quantizes row block b (tile row b / 8, columns (b % 8) * 16 ..+16)
 // from two 16-byte LDS reads, and column block b (tile column b % 128, rows
 // (b / 128) * 16 ..+16) from sixteen 16-bit reads; both with the
-// one-lane-per-block quantizer.
+// one-lane-per-block quantizer.  Every per-tile address and SR index is a
+// per-lane constant of the walk (or of the unit) plus a wavefront-uniform
+// term, and whole tiles skip the bounds checks a partial tile needs.
 //
 // TILE2D (16x16 tile scales, max->6, RNE): after the tile is in LDS each
 // lane stores its row block's amax in LDS, and after a second barrier every
@@ -372,6 +378,7 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
                       unsigned long long* count4, uint8_t* ws, int64_t seg,
                       uint32_t rht_signs = 0) {
   static_assert(kSW * kTR / 16 == kThreads, "one row block and one column block per lane");
+  static_assert(kLoads * kLoadRows == kTR, "the loads cover the tile");
   static_assert(!(RHT && (DO_ROW || TILE2D)), "the transform applies to column blocks only here");
   constexpr int kAhead = DO_ROW ? 2 : 1;
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
@@ -391,12 +398,26 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
   const int lane = threadIdx.x;
   const int rb_row = lane >> 3, rb_col = (lane & 7) * 16;  // row block of this lane
   const int cb_col = lane & (kSW - 1), cb_row = (lane / kSW) * 16;  // column block
+  // per-lane constants of the walk: the row offsets of the lane's load
+  // chunks, its row block's SR index and output offsets at the tile origin
+  int64_t row_off[kLoads];
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) row_off[u] = (int64_t)(u * kLoadRows + (lane >> 4)) * cols;
+  const uint64_t row_idx_l = (uint64_t)rb_row * (uint64_t)cols + (uint64_t)rb_col;
+  const int64_t row_code_l = (int64_t)rb_row * (cols >> 1) + (rb_col >> 1);
+  const int64_t row_scale_l = (int64_t)rb_row * (cols >> 4) + (rb_col >> 4);
   for (int64_t unit = v; unit < units; unit += G) {
     const int64_t g = unit / tiles_c;
     const int64_t c0 = (unit - g * tiles_c) * kSW;
     const int64_t tr0 = g * seg;
     const int64_t tr1 = tr0 + seg < tiles_r ? tr0 + seg : tiles_r;
     int64_t ct_lo = tr0, st_lo = tr0;  // first tile of the open stages
+    // the lane's column block's SR index at row 0 of the strip; its load
+    // chunk's column, clamped into the tensor, and whether it is inside
+    const uint64_t col_idx_l = (uint64_t)(c0 + cb_col) * (uint64_t)rows + (uint64_t)cb_row;
+    const int64_t lc = (lane & 15) * 8;
+    const uint16_t* const xu = x + c0 + (lc < cols - 8 - c0 ? lc : cols - 8 - c0);
+    const bool col_in = lc < cols - c0;
     // kAhead tiles are in flight ahead of the one being processed: two for
     // the fused walk, one for the column-only walk (whose registers then fit
     // five wavefronts per SIMD instead of four, measured 3.5% faster).  The
@@ -406,13 +427,23 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
     // (unused).
     auto step = [&](const uint4 (&w)[kLoads], uint4 (&ahead)[kLoads], int64_t tr) {
       const int64_t r0 = tr * kTR;
-      load_tile(x, rows, cols, (tr + kAhead < tr1 ? tr + kAhead : tr1 - 1) * kTR, c0, ahead);
+      const bool whole = whole_tile(rows, cols, r0, c0);
+      load_tile(xu, row_off, rows, cols, (tr + kAhead < tr1 ? tr + kAhead : tr1 - 1) * kTR, ahead);
       // ---- into LDS, row-major
+      if (whole) {
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int k = u * kThreads + lane;
-        *reinterpret_cast<uint4*>(tile + (k >> 4) * kTilePitch + (k & 15) * 16) =
-            tile_chunk(w, u, rows, cols, r0, c0);
+        for (int u = 0; u < kLoads; ++u) {
+          const int k = u * kThreads + lane;
+          *reinterpret_cast<uint4*>(tile + (k >> 4) * kTilePitch + (k & 15) * 16) = w[u];
+        }
+      } else {
+        const int64_t lim = last_row_off(rows, cols, r0);
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+          const int k = u * kThreads + lane;
+          *reinterpret_cast<uint4*>(tile + (k >> 4) * kTilePitch + (k & 15) * 16) =
+              col_in && row_off[u] <= lim ? w[u] : make_uint4(0, 0, 0, 0);
+        }
       }
       lds_sync();
       if constexpr (TILE2D) {
@@ -426,19 +457,19 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
       if constexpr (DO_ROW) {
         const uint4 wa = *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2);
         const uint4 wb = *reinterpret_cast<const uint4*>(tile + rb_row * kTilePitch + rb_col * 2 + 16);
-        const int64_t r = r0 + rb_row, c = c0 + rb_col;
         BlockOut o;
         if constexpr (TILE2D) {
           float xr[16];
           unpack16(wa, wb, xr);
           o = quantize_block_amax<FMT>(xr, tab, ts, tile_amax(am, (rb_row >> 4) * 8 + (rb_col >> 4)));
         } else {
-          const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)r * (uint64_t)cols + (uint64_t)c, key0);
+          const uint32_t hb = hash_base<ROUND, WIDE>(seed, row_idx_l + (uint64_t)(r0 * cols + c0), key0);
           o = quantize_block<FMT, SELECT, ROUND>(wa, wb, tab, ts, hb);
         }
-        if (r < rows && c < cols) {
-          st_nt(make_uint2(o.c0, o.c1), reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c >> 1)));
-          scales[r * (cols >> 4) + (c >> 4)] = (uint8_t)o.scale;
+        if (whole || (r0 + rb_row < rows && c0 + rb_col < cols)) {
+          st_nt(make_uint2(o.c0, o.c1),
+                reinterpret_cast<uint2*>(codes + (r0 * (cols >> 1) + (c0 >> 1)) + row_code_l));
+          scales[(r0 * (cols >> 4) + (c0 >> 4)) + row_scale_l] = (uint8_t)o.scale;
           n4 += o.four;
         }
       }
@@ -449,20 +480,19 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
         for (int i = 0; i < 16; ++i)
           xc[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(
                                       tile + (cb_row + i) * kTilePitch + cb_col * 2) << 16);
-        const int64_t c = c0 + cb_col, r = r0 + cb_row;
         if constexpr (RHT) rht16(xc, rht_signs);
         BlockOut o;
         if constexpr (TILE2D) {
           o = quantize_block_amax<FMT>(xc, tab, ts, tile_amax(am, (cb_row >> 4) * 8 + (cb_col >> 4)));
         } else {
-          const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)c * (uint64_t)rows + (uint64_t)r, key0);
+          const uint32_t hb = hash_base<ROUND, WIDE>(seed, col_idx_l + (uint64_t)r0, key0);
           o = quantize_block_x<FMT, SELECT, ROUND>(xc, tab, ts, hb);
         }
         const int wd = (int)(tr % kCtTiles) * (kTR / 8) + (cb_row >> 3);
         ct[cb_col * kCtPitch + wd] = o.c0;
         ct[cb_col * kCtPitch + wd + 1] = o.c1;
         st[cb_col * kStPitch + (int)(tr % kStTiles) * (kTR / 16) + (cb_row >> 4)] = (uint8_t)o.scale;
-        if (r < rows && c < cols) n4 += o.four;
+        if (whole || (r0 + cb_row < rows && c0 + cb_col < cols)) n4 += o.four;
       }
       lds_sync();  // staged outputs complete; the tile may be rewritten
       // ---- flush closed stages
@@ -479,10 +509,10 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
       }
     };
     uint4 A[kLoads], B[kLoads], C[kLoads];
-    load_tile(x, rows, cols, tr0 * kTR, c0, A);
+    load_tile(xu, row_off, rows, cols, tr0 * kTR, A);
     int64_t tr = tr0;
     if constexpr (kAhead == 2) {
-      load_tile(x, rows, cols, (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, c0, B);
+      load_tile(xu, row_off, rows, cols, (tr0 + 1 < tr1 ? tr0 + 1 : tr1 - 1) * kTR, B);
       for (; tr + 3 <= tr1; tr += 3) {
         step(A, C, tr);
         step(B, A, tr + 1);

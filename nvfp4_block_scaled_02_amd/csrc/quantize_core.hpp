@@ -475,26 +475,34 @@ constexpr int kStPitch = kStBytes + 4;          // LDS pitch (bytes), padded
 // tile indices within one stage) of the strip at c0.  Only rows < rows and
 // columns < cols are written.  Consecutive lanes write consecutive words (or
 // bytes) of one column, so a wavefront store covers whole 64-byte pieces.
+// Each lane keeps one position in the stage (a word or byte of a column) and
+// walks the columns in steps of kThreads / kCtWords (or / kStBytes), so an
+// address is a per-lane offset plus a wavefront-uniform one.
 // NT: non-temporal code stores (measured faster for the re-quantization's
 // walk, slower for the quantizer's column-wise walk).
 template <bool NT = false>
 __device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __restrict__ codes_t,
                                               int64_t rows, int64_t cols, int64_t c0,
                                               int64_t t_lo, int64_t t_hi) {
+  constexpr int kStep = kThreads / kCtWords;  // columns per pass (16)
   const int64_t row0 = (t_lo / kCtTiles) * kCtTiles * kTR;  // stage origin (rows)
   const int w_lo = (int)(t_lo % kCtTiles) * (kTR / 8);
   int64_t w_end = (rows - row0) / 8;  // words (8 rows each) inside the tensor
   int w_hi = (int)((t_hi - 1) % kCtTiles + 1) * (kTR / 8);
   if (w_end < w_hi) w_hi = (int)w_end;
+  const int wd = threadIdx.x % kCtWords, cl = threadIdx.x / kCtWords;
+  if (wd < w_lo || wd >= w_hi) return;
   const int64_t stride = rows >> 1;
-  // rolled: the flush runs once per stage, and unrolling lets the compiler
-  // keep every per-lane address live across the whole walk
+  uint8_t* const base = codes_t + c0 * stride + (row0 >> 1);  // uniform
+  const int64_t lane_off = (int64_t)cl * stride + wd * 4;
+  const bool whole_strip = c0 + kSW <= cols;
+  // rolled: unrolled, the compiler hoists every pass's address out of the
+  // walk and keeps them all live (twice the registers)
 #pragma unroll 1
-  for (int u = 0; u < kSW * kCtWords / kThreads; ++u) {
-    const int j = u * kThreads + threadIdx.x;
-    const int col = j / kCtWords, wd = j % kCtWords;
-    if (wd >= w_lo && wd < w_hi && c0 + col < cols) {
-      uint32_t* p = reinterpret_cast<uint32_t*>(codes_t + (c0 + col) * stride + (row0 >> 1) + wd * 4);
+  for (int u = 0; u < kSW / kStep; ++u) {
+    const int col = u * kStep + cl;
+    if (whole_strip || c0 + col < cols) {
+      uint32_t* p = reinterpret_cast<uint32_t*>(base + (int64_t)u * kStep * stride + lane_off);
       if constexpr (NT) st_nt(ct[col * kCtPitch + wd], p);
       else *p = ct[col * kCtPitch + wd];
     }
@@ -504,18 +512,25 @@ __device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __res
 __device__ __forceinline__ void flush_scales_t(const uint8_t* st, uint8_t* __restrict__ scales_t,
                                                int64_t rows, int64_t cols, int64_t c0,
                                                int64_t t_lo, int64_t t_hi) {
+  constexpr int kStep = kThreads / kStBytes;  // columns per pass (4)
   const int64_t row0 = (t_lo / kStTiles) * kStTiles * kTR;
   const int b_lo = (int)(t_lo % kStTiles) * (kTR / 16);
   int64_t b_end = (rows - row0) / 16;
   int b_hi = (int)((t_hi - 1) % kStTiles + 1) * (kTR / 16);
   if (b_end < b_hi) b_hi = (int)b_end;
+  const int bt = threadIdx.x % kStBytes, cl = threadIdx.x / kStBytes;
+  if (bt < b_lo || bt >= b_hi) return;
   const int64_t stride = rows >> 4;
+  uint8_t* const base = scales_t + c0 * stride + (row0 >> 4);  // uniform
+  const int64_t lane_off = (int64_t)cl * stride + bt;
+  const bool whole_strip = c0 + kSW <= cols;
+  // rolled: unrolled, the compiler hoists every pass's address out of the
+  // walk and keeps them all live (twice the registers)
 #pragma unroll 1
-  for (int u = 0; u < kSW * kStBytes / kThreads; ++u) {
-    const int j = u * kThreads + threadIdx.x;
-    const int col = j / kStBytes, b = j % kStBytes;
-    if (b >= b_lo && b < b_hi && c0 + col < cols)
-      scales_t[(c0 + col) * stride + (row0 >> 4) + b] = st[col * kStPitch + b];
+  for (int u = 0; u < kSW / kStep; ++u) {
+    const int col = u * kStep + cl;
+    if (whole_strip || c0 + col < cols)
+      base[(int64_t)u * kStep * stride + lane_off] = st[col * kStPitch + bt];
   }
 }
 

@@ -41,6 +41,8 @@
  *  - Arguments are validated on the host before anything is launched; a
  *    non-zero status means nothing was launched (NVFP4_ERR_HIP: a launch was
  *    attempted and HIP reported an error).
+ *  - Sizes: rows, cols and numel are >= 0 and a tensor holds at most
+ *    NVFP4_MAX_ELEMENTS elements; anything else -> NVFP4_ERR_INVALID.
  *  - bfloat16 values travel as their 16-bit patterns (uint16_t).
  *  - Tensors are dense row-major [rows, cols].  Data pointers (x, codes,
  *    out_f32, out_bf16, grad tensors) must be 16-byte aligned; the row-wise
@@ -61,10 +63,16 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 6
+#define NVFP4_ABI_VERSION 7
 
 /* Size of a workspace (see the conventions above). */
 #define NVFP4_WORKSPACE_BYTES 66688
+
+/* Largest tensor any call accepts, in elements (rows * cols, or numel):
+ * 2^44, about 120 times what one MI355X's 288 GB holds in bfloat16.  The
+ * bound keeps every byte offset, index and per-launch count the library
+ * forms well inside 64 bits. */
+#define NVFP4_MAX_ELEMENTS (INT64_C(1) << 44)
 
 /* Status codes. */
 enum {
@@ -115,7 +123,7 @@ size_t nvfp4_workspace_bytes(void);
  *   workspace  a workspace (see above).
  * A NaN anywhere gives NaN; otherwise an infinity gives +inf.
  * Errors: x (numel > 0), amax_out or workspace NULL or misaligned, or
- * numel < 0 -> NVFP4_ERR_INVALID.
+ * numel < 0 or > NVFP4_MAX_ELEMENTS -> NVFP4_ERR_INVALID.
  */
 int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* workspace,
                       hipStream_t stream);

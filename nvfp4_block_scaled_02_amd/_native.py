@@ -9,7 +9,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
-ABI_VERSION = 6  # NVFP4_ABI_VERSION of include/nvfp4.h that these signatures follow
+ABI_VERSION = 7  # NVFP4_ABI_VERSION of include/nvfp4.h that these signatures follow
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 SCALE_E4M3, SCALE_UE5M3 = 0, 1

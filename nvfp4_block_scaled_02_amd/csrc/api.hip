@@ -34,7 +34,7 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static bool size_ok(int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 0) return false;
-  if (cols != 0 && rows > (INT64_C(1) << 62) / cols) return false;
+  if (cols != 0 && rows > NVFP4_MAX_ELEMENTS / cols) return false;
   return true;
 }
 
@@ -152,7 +152,8 @@ static bool ws_ok(const void* ws) { return ws != nullptr && aligned16(ws); }
 
 int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* workspace,
                       hipStream_t stream) {
-  if (numel < 0 || !amax_out || !ws_ok(workspace)) return NVFP4_ERR_INVALID;
+  if (numel < 0 || numel > NVFP4_MAX_ELEMENTS || !amax_out || !ws_ok(workspace))
+    return NVFP4_ERR_INVALID;
   if (numel > 0 && (!x || !aligned16(x))) return NVFP4_ERR_INVALID;
   if (((uintptr_t)amax_out & 3u) != 0) return NVFP4_ERR_INVALID;
   return status_of(launch_tensor_amax(x, numel, amax_out, static_cast<uint8_t*>(workspace), stream));
@@ -160,7 +161,7 @@ int nvfp4_tensor_amax(const uint16_t* x, int64_t numel, float* amax_out, void* w
 
 int nvfp4_tensor_amax_noalloc(const uint16_t* x, int64_t numel, float* amax_out,
                               hipStream_t stream) {
-  if (numel < 0 || !amax_out) return NVFP4_ERR_INVALID;
+  if (numel < 0 || numel > NVFP4_MAX_ELEMENTS || !amax_out) return NVFP4_ERR_INVALID;
   if (numel > 0 && (!x || !aligned16(x))) return NVFP4_ERR_INVALID;
   if (((uintptr_t)amax_out & 3u) != 0) return NVFP4_ERR_INVALID;
   // the kernel's grid (one workgroup per CU at most) must fit the scratch's slots

@@ -147,10 +147,12 @@ __device__ __forceinline__ bool grid_reduce(uint8_t* ws, typename R::T v, typena
   return true;
 }
 
-// A grid sum of non-negative integers below 2^40 per launch, added to *out:
-// each workgroup's part travels inside its arrival (one 64-bit add of
-// 2^40 + part to its group word: arrivals in the high bits, the running sum
-// in the low 40), so a workgroup waits on one atomic round trip, the last of
+// A grid sum of non-negative integers, at most 2^40 per launch (one per
+// block of a tensor of at most 2^44 elements), added to *out: each
+// workgroup's part travels inside its arrival (one 64-bit add of 2^41 + part
+// to its group word: arrivals in the high 23 bits, which hold every grid of
+// at most kSlots workgroups, the running sum in the low 41), so a workgroup
+// waits on one atomic round trip, the last of
 // a group on two, and no slot is written or read.  The group words and the
 // top word are the first kGroups + 1 counter lines of the workspace, viewed
 // as 64-bit words (zero on entry, zero again on exit).  Every thread of every
@@ -159,7 +161,9 @@ template <int BLOCK>
 __device__ __forceinline__ void grid_count_add(uint8_t* ws, uint32_t part,
                                                unsigned long long* out) {
   static_assert(BLOCK % 64 == 0 && BLOCK <= 1024, "whole wavefronts");
-  constexpr uint64_t kOne = 1ull << 40, kLow = kOne - 1;
+  constexpr int kSumBits = 41;
+  constexpr uint64_t kOne = 1ull << kSumBits, kLow = kOne - 1;
+  static_assert(kSlots < (1 << (64 - kSumBits)), "arrivals fit above the sum");
   __shared__ uint32_t red[BLOCK / 64];
   for (int off = 32; off >= 1; off >>= 1) part += (uint32_t)__shfl_xor((int)part, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
@@ -174,12 +178,12 @@ __device__ __forceinline__ void grid_count_add(uint8_t* ws, uint32_t part,
   const uint32_t ngroups = G < (uint32_t)kGroups ? G : (uint32_t)kGroups;
   uint64_t* gw = words + grp * (kCtrStride / 2);
   const uint64_t g = __hip_atomic_fetch_add(gw, kOne + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((g >> 40) != gsize - 1) return;
+  if ((g >> kSumBits) != gsize - 1) return;
   __hip_atomic_exchange(gw, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t gsum = (g & kLow) + t;
   uint64_t* top = words + kGroups * (kCtrStride / 2);
   const uint64_t a = __hip_atomic_fetch_add(top, kOne + gsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((a >> 40) != ngroups - 1) return;
+  if ((a >> kSumBits) != ngroups - 1) return;
   __hip_atomic_exchange(top, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t total = (a & kLow) + gsum;
   if (total != 0) atomicAdd(out, (unsigned long long)total);

@@ -73,6 +73,8 @@ def _q(**kw):
     dict(axes=3, scales_t=None), dict(axes=2, cols=20, rows=16), dict(x=FAKE_ODD),
     dict(codes=FAKE_ODD), dict(scales=FAKE + 2), dict(count4=FAKE_ODD, ws=FAKE),
     dict(rows=1 << 40, cols=1 << 40),
+    # more than NVFP4_MAX_ELEMENTS = 2^44 elements
+    dict(rows=(1 << 40) + 1, cols=16), dict(rows=1 << 31, cols=1 << 31),
     # the 4/6 count needs a workspace, 16-byte aligned
     dict(count4=FAKE), dict(count4=FAKE, ws=FAKE_ODD),
 ])
@@ -154,6 +156,10 @@ def test_amax_rejects():
     assert lib.nvfp4_tensor_amax(FAKE_ODD, 16, FAKE, FAKE, None) == N.ERR_INVALID
     assert lib.nvfp4_tensor_amax(FAKE, 16, FAKE, None, None) == N.ERR_INVALID
     assert lib.nvfp4_tensor_amax(FAKE, 16, FAKE, FAKE_ODD, None) == N.ERR_INVALID
+    # more than NVFP4_MAX_ELEMENTS = 2^44 elements
+    assert lib.nvfp4_tensor_amax(FAKE, (1 << 44) + 1, FAKE, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax(FAKE, (1 << 63) - 1, FAKE, FAKE, None) == N.ERR_INVALID
+    assert lib.nvfp4_tensor_amax_noalloc(FAKE, (1 << 44) + 16, FAKE, None) == N.ERR_INVALID
 
 
 def test_fakequant_rejects():

@@ -195,6 +195,14 @@ def profile_once(torch, dev, launches, nsets):
     log(f"profile-once done: {len(launches)} launches x 2")
 
 
+def prepared(nsets, make):
+    """Timing callable over nsets prepared launches: make(k) returns
+    nv.prepare(...) for buffer set k; the callable issues launch i % nsets
+    (arguments checked once, one ctypes call per launch)."""
+    launches = [make(k)[0] for k in range(nsets)]
+    return lambda i: launches[i % nsets]()
+
+
 def kernel_entry(us, n, bpe):
     gbps = n * bpe / (us * 1e-6) / 1e9
     return {"us": round(us, 3), "bytes_per_elem": round(bpe, 4), "gbps": round(gbps, 1),
@@ -532,21 +540,22 @@ def run_qat(args, torch, np, nv, synth, dev, timer):
     outs = [{"dx": torch.empty((rows, cols), dtype=torch.float32, device=dev),
              "ds_pre": torch.empty_like(s), "ds_post": torch.empty_like(s)} for _ in range(nsets)]
     reps = max(args.steps, 20)
+    P = nv.prepare
     us = {
-        "fakequant_fwd_tied": timer.avg_us(lambda i: nv.fakequant_fwd(
-            xs[i % 2], ss[i % 2], out=xq[i % 2]), reps, nsets),
-        "fakequant_bwd_tied": timer.avg_us(lambda i: nv.fakequant_bwd(
-            xs[i % 2], gs[i % 2], ss[i % 2], out={"dx": outs[i % 2]["dx"], "ds_pre": outs[i % 2]["ds_pre"]}),
-            reps, nsets),
-        "fakequant_fwd_dual": timer.avg_us(lambda i: nv.fakequant_fwd(
-            xs[i % 2], ss[i % 2], sp[i % 2], out=xq[i % 2]), reps, nsets),
-        "fakequant_bwd_dual": timer.avg_us(lambda i: nv.fakequant_bwd(
-            xs[i % 2], gs[i % 2], ss[i % 2], sp[i % 2], out=outs[i % 2]), reps, nsets),
+        "fakequant_fwd_tied": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.fakequant_fwd, xs[k], ss[k], out=xq[k])), reps, nsets),
+        "fakequant_bwd_tied": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.fakequant_bwd, xs[k], gs[k], ss[k],
+            out={"dx": outs[k]["dx"], "ds_pre": outs[k]["ds_pre"]})), reps, nsets),
+        "fakequant_fwd_dual": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.fakequant_fwd, xs[k], ss[k], sp[k], out=xq[k])), reps, nsets),
+        "fakequant_bwd_dual": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.fakequant_bwd, xs[k], gs[k], ss[k], sp[k], out=outs[k])), reps, nsets),
         # the amax reparameterization (block amaxes 6 s in place of the scales)
-        "fakequant_fwd_dual_amax": timer.avg_us(lambda i: nv.fakequant_fwd(
-            xs[i % 2], aa[i % 2], ap[i % 2], out=xq[i % 2], amax=True), reps, nsets),
-        "fakequant_bwd_dual_amax": timer.avg_us(lambda i: nv.fakequant_bwd(
-            xs[i % 2], gs[i % 2], aa[i % 2], ap[i % 2], out=outs[i % 2], amax=True), reps, nsets),
+        "fakequant_fwd_dual_amax": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.fakequant_fwd, xs[k], aa[k], ap[k], out=xq[k], amax=True)), reps, nsets),
+        "fakequant_bwd_dual_amax": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.fakequant_bwd, xs[k], gs[k], aa[k], ap[k], out=outs[k], amax=True)), reps, nsets),
     }
     bpe = {"fakequant_fwd_tied": B_FQ_FWD["tied"], "fakequant_bwd_tied": B_FQ_BWD["tied"],
            "fakequant_fwd_dual": B_FQ_FWD["dual"], "fakequant_bwd_dual": B_FQ_BWD["dual"],
@@ -583,14 +592,17 @@ def run_activation_pertoken(args, torch, np, nv, synth, dev, timer):
     sse = torch.zeros(1, dtype=torch.float64, device=dev)
     ws = nv.workspace(dev)
     reps = max(args.steps, 100)
+    P = nv.prepare
+    for k in range(nsets):
+        nv.row_amax(xs[k], out=ras[k])
     us = {
-        "row_amax": timer.avg_us(lambda i: nv.row_amax(xs[i % nsets], out=ras[i % nsets]),
+        "row_amax": timer.avg_us(prepared(nsets, lambda k: P(nv.row_amax, xs[k], out=ras[k])),
                                  reps, nsets),
-        "quantize_rowscaled_4over6": timer.avg_us(lambda i: nv.quantize_rowscaled(
-            xs[i % nsets], ras[i % nsets], select="4over6", out=outs[i % nsets]), reps, nsets),
-        "dequantize_rowscaled_f32_mse": timer.avg_us(lambda i: nv.dequantize_rowscaled(
-            outs[i % nsets]["codes"], outs[i % nsets]["scales"], ras[i % nsets], global_max=gm,
-            x_ref=xs[i % nsets], sse=sse, out=xh[i % nsets], workspace=ws), reps, nsets),
+        "quantize_rowscaled_4over6": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.quantize_rowscaled, xs[k], ras[k], select="4over6", out=outs[k])), reps, nsets),
+        "dequantize_rowscaled_f32_mse": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.dequantize_rowscaled, outs[k]["codes"], outs[k]["scales"], ras[k], global_max=gm,
+            x_ref=xs[k], sse=sse, out=xh[k], workspace=ws)), reps, nsets),
     }
     bpe = {"row_amax": B_AMAX, "quantize_rowscaled_4over6": B_QUANT,
            "dequantize_rowscaled_f32_mse": B_DEQ_MSE}
@@ -626,15 +638,15 @@ def run_weight_2d(args, torch, np, nv, synth, dev, timer):
             for _ in range(nsets)]
     reps = max(args.steps, 100)
     ws = nv.workspace(dev)
+    P = nv.prepare
     us = {
-        "tensor_amax": timer.avg_us(lambda i: nv.tensor_amax(xs[i % nsets], out=amaxs[i % nsets],
-                                                             workspace=ws), reps, nsets),
-        "quantize_2d_both": timer.avg_us(lambda i: nv.quantize_2d(
-            xs[i % nsets], amaxs[i % nsets], out=outs[i % nsets]), reps, nsets),
-        "quantize_2d_row": timer.avg_us(lambda i: nv.quantize_2d(
-            xs[i % nsets], amaxs[i % nsets], transpose=False,
-            out={"codes": outs[i % nsets]["codes"], "scales": outs[i % nsets]["scales"]}),
-            reps, nsets),
+        "tensor_amax": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.tensor_amax, xs[k], out=amaxs[k], workspace=ws)), reps, nsets),
+        "quantize_2d_both": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.quantize_2d, xs[k], amaxs[k], out=outs[k])), reps, nsets),
+        "quantize_2d_row": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.quantize_2d, xs[k], amaxs[k], transpose=False,
+            out={"codes": outs[k]["codes"], "scales": outs[k]["scales"]})), reps, nsets),
     }
     bpe = {"tensor_amax": B_AMAX, "quantize_2d_both": B_FUSED, "quantize_2d_row": B_QUANT}
     if args.profile_once:
@@ -678,20 +690,16 @@ def run_requant(args, torch, np, nv, synth, dev, timer):
                             workspace=ws)
     del x0
 
-    def rq_mx(i):
-        c, s, ra = src[i % nsets]
-        nv.requantize_t(c, s, row_amaxes=ra, global_max=gm, target="mxfp8", seed=1234,
-                        out={"out_t": mx[i % nsets][0], "scales_t": mx[i % nsets][1]})
-
-    def rq_nv(i):
-        c, s, ra = src[i % nsets]
-        nv.requantize_t(c, s, row_amaxes=ra, global_max=gm, target="nvfp4", seed=1234,
-                        dst_amax=dqa[i % nsets],
-                        out={"out_t": nvo[i % nsets][0], "scales_t": nvo[i % nsets][1]})
-
-    def dq_amax(i):
-        c, s, ra = src[i % nsets]
-        nv.dequantized_amax(c, s, row_amaxes=ra, global_max=gm, out=dqa[i % nsets], workspace=ws)
+    P = nv.prepare
+    rq_mx = prepared(nsets, lambda k: P(
+        nv.requantize_t, src[k][0], src[k][1], row_amaxes=src[k][2], global_max=gm,
+        target="mxfp8", seed=1234, out={"out_t": mx[k][0], "scales_t": mx[k][1]}))
+    rq_nv = prepared(nsets, lambda k: P(
+        nv.requantize_t, src[k][0], src[k][1], row_amaxes=src[k][2], global_max=gm,
+        target="nvfp4", seed=1234, dst_amax=dqa[k], out={"out_t": nvo[k][0], "scales_t": nvo[k][1]}))
+    dq_amax = prepared(nsets, lambda k: P(
+        nv.dequantized_amax, src[k][0], src[k][1], row_amaxes=src[k][2], global_max=gm,
+        out=dqa[k], workspace=ws))
 
     reps = max(args.steps, 100)
     us = {"requant_t_mxfp8_sr": timer.avg_us(rq_mx, reps, nsets),
@@ -732,8 +740,9 @@ def run_select(args, torch, np, nv, synth, dev, timer):
     ws = nv.workspace(dev)
 
     def q(select, count):
-        return lambda i: nv.quantize(xs[i % nsets], amax, select=select,
-                                     out=(outs if count else nocount)[i % nsets], workspace=ws)
+        return prepared(nsets, lambda k: nv.prepare(
+            nv.quantize, xs[k], amax, select=select, out=(outs if count else nocount)[k],
+            workspace=ws))
 
     reps = max(args.steps, 100)
     us = {"quantize_4over6_mse": timer.avg_us(q("4over6", True), reps, nsets),
@@ -781,18 +790,19 @@ def run_rht(args, torch, np, nv, synth, dev, timer):
     gm = nv.default_global_max("e4m3", "4over6")
     ws = nv.workspace(dev)
     reps = max(args.steps, 100)
+    P = nv.prepare
     us = {
-        "rht_amax_col": timer.avg_us(lambda i: nv.rht_amax(xs[i % nsets], axis="col", sign_seed=5,
-                                                           out=ac[i % nsets], workspace=ws), reps, nsets),
-        "quantize_rht_col_4over6": timer.avg_us(lambda i: nv.quantize_rht(
-            xs[i % nsets], ac[i % nsets], axis="col", sign_seed=5, out=oc[i % nsets]), reps, nsets),
-        "rht_amax_row": timer.avg_us(lambda i: nv.rht_amax(xs[i % nsets], axis="row", sign_seed=5,
-                                                           out=ar[i % nsets], workspace=ws), reps, nsets),
-        "quantize_rht_row_4over6": timer.avg_us(lambda i: nv.quantize_rht(
-            xs[i % nsets], ar[i % nsets], axis="row", sign_seed=5, out=orow[i % nsets]), reps, nsets),
-        "dequantize_rht_f32": timer.avg_us(lambda i: nv.dequantize_rht(
-            orow[i % nsets]["codes"], orow[i % nsets]["scales"], ar[i % nsets], global_max=gm,
-            sign_seed=5, out=xh[i % nsets]), reps, nsets),
+        "rht_amax_col": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.rht_amax, xs[k], axis="col", sign_seed=5, out=ac[k], workspace=ws)), reps, nsets),
+        "quantize_rht_col_4over6": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.quantize_rht, xs[k], ac[k], axis="col", sign_seed=5, out=oc[k])), reps, nsets),
+        "rht_amax_row": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.rht_amax, xs[k], axis="row", sign_seed=5, out=ar[k], workspace=ws)), reps, nsets),
+        "quantize_rht_row_4over6": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.quantize_rht, xs[k], ar[k], axis="row", sign_seed=5, out=orow[k])), reps, nsets),
+        "dequantize_rht_f32": timer.avg_us(prepared(nsets, lambda k: P(
+            nv.dequantize_rht, orow[k]["codes"], orow[k]["scales"], ar[k], global_max=gm,
+            sign_seed=5, out=xh[k])), reps, nsets),
     }
     bpe = {"rht_amax_col": B_AMAX, "quantize_rht_col_4over6": B_QUANT, "rht_amax_row": B_AMAX,
            "quantize_rht_row_4over6": B_QUANT, "dequantize_rht_f32": B_DEQ}
@@ -826,16 +836,16 @@ def run_gradient(args, torch, np, nv, synth, dev, timer):
              "scales_t": torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev)}
             for _ in range(nsets)]
     reps = max(args.steps, 20)
+    kw = dict(fmt="ue5m3", select="6", rounding="sr", seed=1234)
     us = {
-        "quantize_fused_row_col_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
-            xs[i % 2], stale, fmt="ue5m3", select="6", rounding="sr", axes="both", seed=1234,
-            out=outs[i % 2]), reps, nsets),
-        "quantize_row_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
-            xs[i % 2], stale, fmt="ue5m3", select="6", rounding="sr", axes="row", seed=1234,
-            out={"codes": outs[i % 2]["codes"], "scales": outs[i % 2]["scales"]}), reps, nsets),
-        "quantize_col_sr_ue5m3": timer.avg_us(lambda i: nv.quantize(
-            xs[i % 2], stale, fmt="ue5m3", select="6", rounding="sr", axes="col", seed=1234,
-            out={"codes_t": outs[i % 2]["codes_t"], "scales_t": outs[i % 2]["scales_t"]}),
+        "quantize_fused_row_col_sr_ue5m3": timer.avg_us(prepared(nsets, lambda k: nv.prepare(
+            nv.quantize, xs[k], stale, axes="both", out=outs[k], **kw)), reps, nsets),
+        "quantize_row_sr_ue5m3": timer.avg_us(prepared(nsets, lambda k: nv.prepare(
+            nv.quantize, xs[k], stale, axes="row",
+            out={"codes": outs[k]["codes"], "scales": outs[k]["scales"]}, **kw)), reps, nsets),
+        "quantize_col_sr_ue5m3": timer.avg_us(prepared(nsets, lambda k: nv.prepare(
+            nv.quantize, xs[k], stale, axes="col",
+            out={"codes_t": outs[k]["codes_t"], "scales_t": outs[k]["scales_t"]}, **kw)),
             reps, nsets),
     }
     bpe = {"quantize_fused_row_col_sr_ue5m3": B_FUSED, "quantize_row_sr_ue5m3": B_QUANT,

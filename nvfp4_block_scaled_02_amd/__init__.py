@@ -7,11 +7,11 @@ does not load the library; the first call does, and raises if it is not built.
 from .api import (Launch, Quantized, default_global_max, dequantize, dequantize_rowscaled,
                   dequantize_rht, dequantized_amax, fakequant_bwd, fakequant_fwd, quantize,
                   quantize_2d, quantize_rht, quantize_rowscaled, requantize_t, rht_amax, row_amax,
-                  tensor_amax, workspace, prepare_quantize, prepare_dequantize,
+                  tensor_amax, workspace, prepare, prepare_quantize, prepare_dequantize,
                   prepare_tensor_amax)
 
 __all__ = ["Launch", "Quantized", "default_global_max", "dequantize", "dequantize_rowscaled",
            "dequantize_rht", "dequantized_amax", "fakequant_bwd", "fakequant_fwd", "quantize",
            "quantize_2d", "quantize_rht", "quantize_rowscaled", "requantize_t", "rht_amax",
-           "row_amax", "tensor_amax", "workspace", "prepare_quantize",
+           "row_amax", "tensor_amax", "workspace", "prepare", "prepare_quantize",
            "prepare_dequantize", "prepare_tensor_amax"]

@@ -11,8 +11,14 @@ Calls that combine one value per workgroup across a launch (the amax calls,
 the 4/6 count, the squared-error report) need a workspace: by default one
 zero-filled buffer per (device, stream) is created on first use and reused
 (every call leaves it zeroed); ``workspace=`` passes another one.
+
+``prepare(fn, ...)`` runs any single-launch call with its arguments checked
+and its outputs allocated, but returns the launch (a ``Launch``) instead of
+issuing it: loops that launch the same call many times (serving, timing,
+graph capture) then pay one ctypes call per launch.
 """
 import ctypes
+import threading
 from dataclasses import dataclass
 from typing import Optional
 
@@ -93,8 +99,8 @@ def _ws(given: Optional[torch.Tensor], dev):
 class Launch:
     """One entry point with its arguments checked once: each call issues the
     launch again on `stream` (default: the current stream of the device)
-    without re-checking anything.  It keeps its tensors alive.  For loops
-    that launch the same call many times (serving, graph capture, timing)."""
+    without re-checking anything.  It keeps its tensors alive.  Made by
+    prepare()."""
 
     def __init__(self, entry: str, args: tuple, device, keep):
         self._fn = getattr(N.lib(), entry)
@@ -110,14 +116,37 @@ class Launch:
             N.check(st, self._entry)
 
 
-def prepare_tensor_amax(x: torch.Tensor, out: torch.Tensor, *,
-                        workspace: Optional[torch.Tensor] = None) -> Launch:
-    """tensor_amax(x, out) as a Launch."""
-    _need(x, torch.bfloat16, "x")
-    _need(out, torch.float32, "out", 1)
-    ws = _ws(workspace, x.device)
-    return Launch("nvfp4_tensor_amax", (_ptr(x), x.numel(), _ptr(out), _ptr(ws)), x.device,
-                  (x, out, ws))
+_CAPTURE = threading.local()
+
+
+def _invoke(entry: str, args: tuple, device, keep):
+    """Issues entry(*args, stream) on the current stream of `device` now, or,
+    inside prepare(), records it as a Launch instead."""
+    launch = Launch(entry, args, device, keep)
+    rec = getattr(_CAPTURE, "launches", None)
+    if rec is not None:
+        rec.append(launch)
+    else:
+        launch()
+
+
+def prepare(fn, *args, **kwargs):
+    """Runs fn(*args, **kwargs) -- a call of this module that issues exactly
+    one library call -- with its arguments checked and its outputs allocated,
+    but without launching.  Returns (launch, result): calling `launch()`
+    issues the call, writing the outputs in `result`."""
+    prev = getattr(_CAPTURE, "launches", None)
+    _CAPTURE.launches = []
+    try:
+        result = fn(*args, **kwargs)
+        launches = _CAPTURE.launches
+    finally:
+        _CAPTURE.launches = prev
+    if len(launches) != 1:
+        raise ValueError(f"{getattr(fn, '__name__', fn)} issues {len(launches)} library calls "
+                         "with these arguments; prepare() needs exactly one (pass the amax it "
+                         "would otherwise compute)")
+    return launches[0], result
 
 
 def tensor_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None, *,
@@ -126,8 +155,17 @@ def tensor_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None, *,
     _need(x, torch.bfloat16, "x")
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=x.device)
-    prepare_tensor_amax(x, out, workspace=workspace)()
+    _need(out, torch.float32, "out", 1)
+    ws = _ws(workspace, x.device)
+    _invoke("nvfp4_tensor_amax", (_ptr(x), x.numel(), _ptr(out), _ptr(ws)), x.device,
+            (x, out, ws))
     return out
+
+
+def prepare_tensor_amax(x: torch.Tensor, out: torch.Tensor, *,
+                        workspace: Optional[torch.Tensor] = None) -> Launch:
+    """tensor_amax(x, out) as a Launch."""
+    return prepare(tensor_amax, x, out, workspace=workspace)[0]
 
 
 @dataclass
@@ -173,24 +211,6 @@ def _quant_args(x, rows, cols, amax, global_max, fmt, select, rounding, ax, seed
         count4=_ptr(out.get("count4")), workspace=_ptr(ws) if "count4" in out else None)
 
 
-def prepare_quantize(x: torch.Tensor, amax: torch.Tensor, *, fmt: str = "e4m3",
-                     select: str = "4over6", rounding: str = "rne", axes: str = "row",
-                     seed: int = 0, global_max: float = 0.0, count4: bool = False,
-                     out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None):
-    """quantize() as a Launch: returns (launch, Quantized) with the outputs
-    the launch writes."""
-    rows, cols = _need_2d(x, torch.bfloat16, "x")
-    _need(amax, torch.float32, "amax", 1)
-    ax = _AXES[axes]
-    out = _quant_outputs(out, rows, cols, ax, count4, x.device)
-    ws = _ws(workspace, x.device) if "count4" in out else None
-    args = _quant_args(x, rows, cols, amax, global_max, fmt, select, rounding, ax, seed, out, ws)
-    gm = float(global_max) if global_max else default_global_max(fmt, select)
-    q = Quantized(out.get("codes"), out.get("scales"), out.get("codes_t"), out.get("scales_t"),
-                  amax, gm, fmt, out.get("count4"))
-    return Launch("nvfp4_quantize", (ctypes.byref(args),), x.device, (x, amax, out, ws, args)), q
-
-
 def quantize(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: str = "e4m3",
              select: str = "4over6", rounding: str = "rne", axes: str = "row", seed: int = 0,
              global_max: float = 0.0, count4: bool = False, out: Optional[dict] = None,
@@ -199,14 +219,24 @@ def quantize(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: str =
     tensor (default: the fresh tensor amax).  axes: "row", "col" or "both".
     out: optional preallocated {"codes", "scales", "codes_t", "scales_t",
     "count4"} tensors (count4 is added to, not cleared)."""
-    _need_2d(x, torch.bfloat16, "x")
+    rows, cols = _need_2d(x, torch.bfloat16, "x")
     if amax is None:
         amax = tensor_amax(x, workspace=workspace)
-    launch, q = prepare_quantize(x, amax, fmt=fmt, select=select, rounding=rounding, axes=axes,
-                                 seed=seed, global_max=global_max, count4=count4, out=out,
-                                 workspace=workspace)
-    launch()
-    return q
+    _need(amax, torch.float32, "amax", 1)
+    ax = _AXES[axes]
+    out = _quant_outputs(out, rows, cols, ax, count4, x.device)
+    ws = _ws(workspace, x.device) if "count4" in out else None
+    args = _quant_args(x, rows, cols, amax, global_max, fmt, select, rounding, ax, seed, out, ws)
+    _invoke("nvfp4_quantize", (ctypes.byref(args),), x.device, (x, amax, out, ws, args))
+    gm = float(global_max) if global_max else default_global_max(fmt, select)
+    return Quantized(out.get("codes"), out.get("scales"), out.get("codes_t"), out.get("scales_t"),
+                     amax, gm, fmt, out.get("count4"))
+
+
+def prepare_quantize(x: torch.Tensor, amax: torch.Tensor, **kwargs):
+    """quantize() as a Launch: returns (launch, Quantized) with the outputs
+    the launch writes."""
+    return prepare(quantize, x, amax, **kwargs)
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
@@ -217,22 +247,6 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
     """x_hat = q * D[scale] * alpha.  Returns x_hat (or None if out_dtype is
     None), plus the per-block effective scales if asked, plus the binary64
     SSE tensor if x_ref is given (sse, if passed, is overwritten)."""
-    launch, res = prepare_dequantize(codes, scales, amax, global_max=global_max, fmt=fmt,
-                                     out_dtype=out_dtype, want_block_scale=want_block_scale,
-                                     x_ref=x_ref, sse=sse, out=out, workspace=workspace,
-                                     _entry=_entry)
-    launch()
-    return res
-
-
-def prepare_dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, *,
-                       global_max: float, fmt: str = "e4m3", out_dtype=torch.float32,
-                       want_block_scale: bool = False, x_ref: Optional[torch.Tensor] = None,
-                       sse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None,
-                       _entry: str = "nvfp4_dequantize"):
-    """dequantize() as a Launch: returns (launch, result) with the result
-    dequantize() would return."""
     rows, half = _need_2d(codes, torch.uint8, "codes")
     cols = 2 * half
     _need(scales, torch.uint8, "scales", rows * (cols // 16))
@@ -265,8 +279,14 @@ def prepare_dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Te
         res.append(bs)
     if x_ref is not None:
         res.append(sse)
-    keep = (codes, scales, amax, out, bs, x_ref, sse, ws)
-    return Launch(_entry, args, dev, keep), (res[0] if len(res) == 1 else tuple(res))
+    _invoke(_entry, args, dev, (codes, scales, amax, out, bs, x_ref, sse, ws))
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def prepare_dequantize(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor, **kwargs):
+    """dequantize() as a Launch: returns (launch, result) with the result
+    dequantize() would return."""
+    return prepare(dequantize, codes, scales, amax, **kwargs)
 
 
 # ---------------------------------------------------------------- per-row outer scales
@@ -276,8 +296,7 @@ def row_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tenso
     if out is None:
         out = torch.empty(rows, dtype=torch.float32, device=x.device)
     _need(out, torch.float32, "out", rows)
-    N.check(N.lib().nvfp4_row_amax(_ptr(x), rows, cols, _ptr(out), _stream(x.device)),
-            "nvfp4_row_amax")
+    _invoke("nvfp4_row_amax", (_ptr(x), rows, cols, _ptr(out)), x.device, (x, out))
     return out
 
 
@@ -297,7 +316,8 @@ def quantize_rowscaled(x: torch.Tensor, row_amaxes: Optional[torch.Tensor] = Non
     ws = _ws(workspace, x.device) if "count4" in out else None
     args = _quant_args(x, rows, cols, row_amaxes, global_max, fmt, select, rounding, N.AXIS_ROW,
                        seed, out, ws)
-    N.check(N.lib().nvfp4_quantize_rowscaled(args, _stream(x.device)), "nvfp4_quantize_rowscaled")
+    _invoke("nvfp4_quantize_rowscaled", (ctypes.byref(args),), x.device,
+            (x, row_amaxes, out, ws, args))
     gm = float(global_max) if global_max else default_global_max(fmt, select)
     return Quantized(out["codes"], out["scales"], None, None, row_amaxes, gm, fmt,
                      out.get("count4"))
@@ -329,7 +349,7 @@ def quantize_2d(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, fmt: st
     out = _quant_outputs(out, rows, cols, ax, False, x.device)
     out.pop("count4", None)
     args = _quant_args(x, rows, cols, amax, global_max, fmt, "6", "rne", ax, 0, out, None)
-    N.check(N.lib().nvfp4_quantize_2d(args, _stream(x.device)), "nvfp4_quantize_2d")
+    _invoke("nvfp4_quantize_2d", (ctypes.byref(args),), x.device, (x, amax, out, args))
     gm = float(global_max) if global_max else default_global_max(fmt, "6")
     return Quantized(out["codes"], out["scales"], out.get("codes_t"), out.get("scales_t"), amax,
                      gm, fmt, None)
@@ -365,10 +385,10 @@ def dequantized_amax(codes: torch.Tensor, scales: torch.Tensor, *,
         out = torch.empty(1, dtype=torch.float32, device=dev)
     _need(out, torch.float32, "out", 1)
     ws = _ws(workspace, dev)
-    st = N.lib().nvfp4_dequantized_amax(_ptr(codes), _ptr(scales), rows, cols, _ptr(amax),
-                                        _ptr(row_amaxes), float(global_max), _FMT[fmt], _ptr(out),
-                                        _ptr(ws), _stream(dev))
-    N.check(st, "nvfp4_dequantized_amax")
+    _invoke("nvfp4_dequantized_amax",
+            (_ptr(codes), _ptr(scales), rows, cols, _ptr(amax), _ptr(row_amaxes),
+             ctypes.c_float(float(global_max)), _FMT[fmt], _ptr(out), _ptr(ws)),
+            dev, (codes, scales, amax, row_amaxes, out, ws))
     return out
 
 
@@ -401,11 +421,12 @@ def requantize_t(codes: torch.Tensor, scales: torch.Tensor, *,
         raise ValueError(f"unknown target {target!r}")
     _need(out["out_t"], torch.uint8, "out_t", n_t)
     _need(out["scales_t"], torch.uint8, "scales_t", n_s)
-    st = N.lib().nvfp4_requantize_t(
-        _ptr(codes), _ptr(scales), rows, cols, _ptr(amax), _ptr(row_amaxes), float(global_max),
-        _FMT[fmt], _TARGET[target], _ptr(dst_amax), float(dst_global_max), _FMT[dst_fmt],
-        int(seed) & _U64, _ptr(out["out_t"]), _ptr(out["scales_t"]), _stream(dev))
-    N.check(st, "nvfp4_requantize_t")
+    _invoke("nvfp4_requantize_t",
+            (_ptr(codes), _ptr(scales), rows, cols, _ptr(amax), _ptr(row_amaxes),
+             ctypes.c_float(float(global_max)), _FMT[fmt], _TARGET[target], _ptr(dst_amax),
+             ctypes.c_float(float(dst_global_max)), _FMT[dst_fmt], int(seed) & _U64,
+             _ptr(out["out_t"]), _ptr(out["scales_t"])),
+            dev, (codes, scales, amax, row_amaxes, dst_amax, out))
     return out["out_t"], out["scales_t"]
 
 
@@ -423,9 +444,9 @@ def rht_amax(x: torch.Tensor, *, axis: str = "row", sign_seed: int = 0,
         out = torch.empty(1, dtype=torch.float32, device=x.device)
     _need(out, torch.float32, "out", 1)
     ws = _ws(workspace, x.device)
-    st = N.lib().nvfp4_rht_amax(_ptr(x), rows, cols, _AXIS1[axis], int(sign_seed) & _U64,
-                                _ptr(out), _ptr(ws), _stream(x.device))
-    N.check(st, "nvfp4_rht_amax")
+    _invoke("nvfp4_rht_amax",
+            (_ptr(x), rows, cols, _AXIS1[axis], int(sign_seed) & _U64, _ptr(out), _ptr(ws)),
+            x.device, (x, out, ws))
     return out
 
 
@@ -449,8 +470,8 @@ def quantize_rht(x: torch.Tensor, amax: Optional[torch.Tensor] = None, *, axis: 
     o = _quant_outputs(given, rows, cols, ax, count4, x.device)
     ws = _ws(workspace, x.device) if "count4" in o else None
     args = _quant_args(x, rows, cols, amax, global_max, fmt, select, rounding, ax, seed, o, ws)
-    N.check(N.lib().nvfp4_quantize_rht(args, int(sign_seed) & _U64, _stream(x.device)),
-            "nvfp4_quantize_rht")
+    _invoke("nvfp4_quantize_rht", (ctypes.byref(args), int(sign_seed) & _U64), x.device,
+            (x, amax, o, ws, args))
     gm = float(global_max) if global_max else default_global_max(fmt, select)
     c, s = (o["codes"], o["scales"]) if ax == N.AXIS_ROW else (o["codes_t"], o["scales_t"])
     return Quantized(c, s, None, None, amax, gm, fmt, o.get("count4"))
@@ -467,10 +488,10 @@ def dequantize_rht(codes: torch.Tensor, scales: torch.Tensor, amax: torch.Tensor
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
     _need(out, torch.float32, "out", rows * cols)
-    st = N.lib().nvfp4_dequantize_rht(_ptr(codes), _ptr(scales), rows, cols, _ptr(amax),
-                                      float(global_max), _FMT[fmt], int(sign_seed) & _U64,
-                                      _ptr(out), _stream(codes.device))
-    N.check(st, "nvfp4_dequantize_rht")
+    _invoke("nvfp4_dequantize_rht",
+            (_ptr(codes), _ptr(scales), rows, cols, _ptr(amax), ctypes.c_float(float(global_max)),
+             _FMT[fmt], int(sign_seed) & _U64, _ptr(out)),
+            codes.device, (codes, scales, amax, out))
     return out
 
 
@@ -488,9 +509,8 @@ def fakequant_fwd(x: torch.Tensor, s_pre: torch.Tensor, s_post: Optional[torch.T
         out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
     _need(out, torch.float32, "out", rows * cols)
     entry = "nvfp4_fakequant_fwd_amax" if amax else "nvfp4_fakequant_fwd"
-    st = getattr(N.lib(), entry)(_ptr(x), rows, cols, _ptr(s_pre), _ptr(s_post), _ptr(out),
-                                 _stream(x.device))
-    N.check(st, entry)
+    _invoke(entry, (_ptr(x), rows, cols, _ptr(s_pre), _ptr(s_post), _ptr(out)), x.device,
+            (x, s_pre, s_post, out))
     return out
 
 
@@ -523,7 +543,6 @@ def fakequant_bwd(x: torch.Tensor, grad: torch.Tensor, s_pre: torch.Tensor,
             dpost = torch.empty(s_post.shape, dtype=torch.float32, device=dev)
         _need(dpost, torch.float32, "ds_post", nb)
     entry = "nvfp4_fakequant_bwd_amax" if amax else "nvfp4_fakequant_bwd"
-    st = getattr(N.lib(), entry)(_ptr(x), _ptr(grad), rows, cols, _ptr(s_pre), _ptr(s_post),
-                                 _ptr(dx), _ptr(dpre), _ptr(dpost), _stream(dev))
-    N.check(st, entry)
+    _invoke(entry, (_ptr(x), _ptr(grad), rows, cols, _ptr(s_pre), _ptr(s_post), _ptr(dx),
+                    _ptr(dpre), _ptr(dpost)), dev, (x, grad, s_pre, s_post, dx, dpre, dpost))
     return (dx, dpre) if s_post is None else (dx, dpre, dpost)

@@ -97,6 +97,24 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
 // memory rate on the max->6 path.  Codes are stored 8 bytes per lane, scale
 // bytes 1 per lane: whole 512- and 64-byte pieces per wavefront.  Register
 // use is held to 64 so that 8 wavefronts per SIMD stay resident.
+//
+// Work distribution: workgroup b owns the groups b*W + j + k*nwaves (W
+// wavefronts per workgroup, slot j < W, round k: the grid-stride order), as
+// a list of tasks t = k*W + j that its wavefronts take in order from a
+// counter in LDS.  Each wavefront starts with task j = its index and takes
+// its next task before computing the current one, so its next loads still go
+// out right after its stores.  The wavefronts of a SIMD do not progress
+// alike (the older ones win the VALU arbitration); with a fixed share each,
+// the workgroup waited for its slowest wavefronts (1.7-2.7 us of spread at
+// 8192x4096).  Taking tasks as they finish shortened the SR row stream at
+// 16384x8192 from 63.4 to 61.8 us and the scale sweep from 524 to 518 us
+// (same box, outputs identical).  The Four-Over-Six and max->6 RNE kernels
+// keep the fixed grid-stride share (tasks j, j + W, ...): in a stripped-down
+// copy the counter took 8192x4096 from 16.4 to 15.7 us, but in the full
+// kernel it measured 16.5-17.5 against 16.6-17.1 us, and at 4096x4096 (two
+// groups per wavefront, little to even out) 10.3 against 9.9 us.  With
+// fewer than three groups per wavefront the dynamic kernels keep the fixed
+// share as well.
 template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK, bool RHT>
 __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t nblocks,
                                             const float* __restrict__ amax, float sg, uint64_t seed,
@@ -104,14 +122,22 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
                                             uint8_t* __restrict__ scales,
                                             unsigned long long* count4, uint8_t* ws,
                                             uint32_t rht_signs) {
+  constexpr int W = BLOCK / 64;  // wavefronts per workgroup
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint4 stage[BLOCK * 2];
+  __shared__ uint64_t next_task;
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
   uint4* reg = stage + wv * 128;  // this wavefront's 2 KiB
   const int64_t nchunks = nblocks * 2;
   const int64_t nwhole = nblocks / 64;  // groups of 64 blocks
-  const int64_t nwaves = (int64_t)gridDim.x * (BLOCK / 64);
-  int64_t g = (int64_t)blockIdx.x * (BLOCK / 64) + wv;
+  const int64_t nwaves = (int64_t)gridDim.x * W;
+  const int64_t g0 = (int64_t)blockIdx.x * W;
+  constexpr bool kDynamic = ROUND == ROUND_SR || SELECT == SELECT_SWEEP;
+  const bool dynamic = kDynamic && nwhole >= 3 * nwaves;
+  // task t of this workgroup -> its group (increasing in t)
+  auto group_of = [&](uint64_t t) -> int64_t { return g0 + (int64_t)(t % W) + (int64_t)(t / W) * nwaves; };
+  uint64_t t = (uint64_t)wv;
+  int64_t g = group_of(t);
   // The first group's loads go out before the outer scale is read and the
   // table built, so their latency overlaps that start-up instead of
   // following it (every workgroup of the grid is resident from the start).
@@ -125,11 +151,18 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
   const TensorScale ts = tensor_scale(*amax, sg);
   if (threadIdx.x < FmtTraits<FMT>::kCodes)
     tab[threadIdx.x] = scale_entry(FMT, threadIdx.x, ts.alpha);
+  if (kDynamic && threadIdx.x == 0) next_task = W;  // tasks 0..W-1: the first groups above
   __syncthreads();
   uint32_t n4 = 0;
   // whole groups, unchecked; the next group's loads are issued after this
   // group's stores (not before its arithmetic: that would cost registers)
-  for (; g < nwhole; g += nwaves) {
+  while (g < nwhole) {
+    uint64_t tn = 0;
+    if (kDynamic && dynamic) {
+      if (l == 0) tn = __hip_atomic_fetch_add(&next_task, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      tn = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tn >> 32)) << 32) |
+           __builtin_amdgcn_readfirstlane((uint32_t)tn);
+    }
     bounce_pair(reg, l, a, b);
     const int64_t bk = g * 64 + l;
     const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
@@ -138,13 +171,18 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
     st_nt(make_uint2(o.c0, o.c1), codes + bk);
     scales[bk] = (uint8_t)o.scale;
     n4 += o.four;
-    const int64_t gn = g + nwaves;
-    if (gn < nwhole) {
-      a = ld_nt(x + gn * 128 + l);
-      b = ld_nt(x + gn * 128 + 64 + l);
+    if (kDynamic && dynamic) {
+      t = tn;
+      g = group_of(t);
+    } else {
+      g += nwaves;
+    }
+    if (g < nwhole) {
+      a = ld_nt(x + g * 128 + l);
+      b = ld_nt(x + g * 128 + 64 + l);
     }
   }
-  // the partial last group (nblocks % 64 blocks), if this wavefront owns it
+  // the partial last group (nblocks % 64 blocks), if this wavefront drew it
   if (g == nwhole && nblocks % 64 != 0) {
     const int64_t c0 = g * 128;
     const uint4 a = c0 + l < nchunks ? ld_nt(x + c0 + l) : make_uint4(0, 0, 0, 0);

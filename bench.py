@@ -19,7 +19,7 @@ Timing: the GPU clocks are first settled by about a second of steps; then
 stream, synchronized on both sides).  Per-kernel figures time back-to-back
 launches of one kernel, bracketed by HIP events on the launch stream (the
 host issues a launch in less time than the kernels here take, so the queue
-never drains); the median of five such runs is reported.  `--graph` replays
+never drains); the median of nine such runs is reported.  `--graph` replays
 a HIP graph of the same launches instead (measured: the same for most
 kernels, 2 us slower for the Four-Over-Six quantizer).
 
@@ -123,7 +123,7 @@ class Timer:
             torch.cuda.synchronize()
         return i
 
-    def avg_us(self, fn, reps, nsets, name=None, repeats=5):
+    def avg_us(self, fn, reps, nsets, name=None, repeats=9):
         """Average duration of one fn(i) over `reps` back-to-back calls,
         timed by events on this stream; the median of `repeats` runs.  With
         graphs enabled the calls are captured into a HIP graph (kernel nodes
@@ -437,7 +437,7 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
                     "gelem_per_s": round(n / (ms_step * 1e-3) / 1e9, 2)}
     finish(line, kernels, args, {k: measured_traffic(k) for k in kernels},
            roofline_kernel="quantize_4over6")
-    line["timing"] = {"kernels": f"median of 5 runs of {reps} back-to-back launches "
+    line["timing"] = {"kernels": f"median of 9 runs of {reps} back-to-back launches "
                                  "(HIP events on the launch stream)", "modes": timer.modes}
     t6, t46, t46c = us["quantize_6"], us["quantize_4over6"], us["quantize_4over6_count"]
     line["overhead_4over6"] = {

@@ -107,14 +107,12 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
 // alike (the older ones win the VALU arbitration); with a fixed share each,
 // the workgroup waited for its slowest wavefronts (1.7-2.7 us of spread at
 // 8192x4096).  Taking tasks as they finish shortened the SR row stream at
-// 16384x8192 from 63.4 to 61.8 us and the scale sweep from 524 to 518 us
-// (same box, outputs identical).  The Four-Over-Six and max->6 RNE kernels
-// keep the fixed grid-stride share (tasks j, j + W, ...): in a stripped-down
-// copy the counter took 8192x4096 from 16.4 to 15.7 us, but in the full
-// kernel it measured 16.5-17.5 against 16.6-17.1 us, and at 4096x4096 (two
-// groups per wavefront, little to even out) 10.3 against 9.9 us.  With
-// fewer than three groups per wavefront the dynamic kernels keep the fixed
-// share as well.
+// 16384x8192 from 63.0 to 60.0-60.8 us, the scale sweep from 526 to 519 us,
+// and the 4/6 quantizer at 8192x4096 from 16.08 to 15.80 us (17.65 to 17.20
+// with the count; medians of 21 interleaved runs; outputs identical).  With
+// fewer than three groups per wavefront (4096x4096: two) there is little to
+// even out and the counter only adds its latency, so each wavefront keeps the
+// fixed grid-stride share there (tasks j, j + W, ...).
 template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK, bool RHT>
 __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t nblocks,
                                             const float* __restrict__ amax, float sg, uint64_t seed,
@@ -132,8 +130,7 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
   const int64_t nwhole = nblocks / 64;  // groups of 64 blocks
   const int64_t nwaves = (int64_t)gridDim.x * W;
   const int64_t g0 = (int64_t)blockIdx.x * W;
-  constexpr bool kDynamic = ROUND == ROUND_SR || SELECT == SELECT_SWEEP;
-  const bool dynamic = kDynamic && nwhole >= 3 * nwaves;
+  const bool dynamic = nwhole >= 3 * nwaves;
   // task t of this workgroup -> its group (increasing in t)
   auto group_of = [&](uint64_t t) -> int64_t { return g0 + (int64_t)(t % W) + (int64_t)(t / W) * nwaves; };
   uint64_t t = (uint64_t)wv;
@@ -151,14 +148,14 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
   const TensorScale ts = tensor_scale(*amax, sg);
   if (threadIdx.x < FmtTraits<FMT>::kCodes)
     tab[threadIdx.x] = scale_entry(FMT, threadIdx.x, ts.alpha);
-  if (kDynamic && threadIdx.x == 0) next_task = W;  // tasks 0..W-1: the first groups above
+  if (threadIdx.x == 0) next_task = W;  // tasks 0..W-1: the first groups above
   __syncthreads();
   uint32_t n4 = 0;
   // whole groups, unchecked; the next group's loads are issued after this
   // group's stores (not before its arithmetic: that would cost registers)
   while (g < nwhole) {
     uint64_t tn = 0;
-    if (kDynamic && dynamic) {
+    if (dynamic) {
       if (l == 0) tn = __hip_atomic_fetch_add(&next_task, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       tn = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tn >> 32)) << 32) |
            __builtin_amdgcn_readfirstlane((uint32_t)tn);
@@ -171,7 +168,7 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
     st_nt(make_uint2(o.c0, o.c1), codes + bk);
     scales[bk] = (uint8_t)o.scale;
     n4 += o.four;
-    if (kDynamic && dynamic) {
+    if (dynamic) {
       t = tn;
       g = group_of(t);
     } else {

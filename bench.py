@@ -305,22 +305,37 @@ def copy_ceiling(torch, dev, timer):
 
 
 def scale_format_mse(torch, np, nv, synth, dev, ws):
-    """E4M3 vs UE5M3 block scales on the heavy-tailed 4096x4096 stand-in
-    ("UE5M3" blog, 实验): max->6 RNE quantization with each format's own
-    outer scale (FP8 max 448 / 114688), dequantized, per-tensor MSE and
-    relative error."""
-    xb = synth.make("heavy")["x"]
-    x = to_dev(torch, np, xb, dev)
-    e2 = float((x.double() ** 2).sum().item())
-    amax = nv.tensor_amax(x, workspace=ws)
-    res = {"workload": "heavy 4096x4096 bf16 N(0,1) x U(1,9) per element (seed 5), max->6, RNE"}
-    for fmt in ("e4m3", "ue5m3"):
-        q = nv.quantize(x, amax, fmt=fmt, select="6")
-        sse = torch.empty(1, dtype=torch.float64, device=dev)
-        nv.dequantize(q.codes, q.scales, amax, global_max=q.global_max, fmt=fmt, x_ref=x,
-                      sse=sse, out_dtype=None, workspace=ws)
-        v = float(sse.item())
-        res[fmt] = {"mse": v / x.numel(), "rel_error": (v / e2) ** 0.5}
+    """E4M3 vs UE5M3 block scales ("UE5M3" blog, 实验): max->6 RNE quantization
+    with each format's own outer scale (FP8 max 448 / 114688), dequantized.
+    Two 4096x4096 stand-ins: the blog's heavy-tailed activation (N(0,1) x
+    U(1,9) per element), and block magnitudes spread over 24 binades (wider
+    than E4M3's range under the outer scale).  Per format: MSE, relative error
+    ||x - x_hat|| / ||x||, the mean over blocks of each block's relative error,
+    and the fraction of nonzero blocks that dequantize to all zeros."""
+    res = {}
+    for name, desc in (("heavy", "N(0,1) x U(1,9) per element (seed 5)"),
+                       ("wide", "N(0,1) x 2^(-24 U(0,1)) per 16-element block (seed 6)")):
+        xb = synth.make(name)["x"]
+        x = to_dev(torch, np, xb, dev)
+        xf = x.double()
+        e2 = float((xf ** 2).sum().item())
+        blk2 = (xf ** 2).view(-1, 16).sum(dim=1)
+        nz = blk2 > 0
+        amax = nv.tensor_amax(x, workspace=ws)
+        r = {"workload": f"{name} 4096x4096 bf16 {desc}, max->6, RNE"}
+        for fmt in ("e4m3", "ue5m3"):
+            q = nv.quantize(x, amax, fmt=fmt, select="6")
+            sse = torch.empty(1, dtype=torch.float64, device=dev)
+            xh = nv.dequantize(q.codes, q.scales, amax, global_max=q.global_max, fmt=fmt, x_ref=x,
+                               sse=sse, workspace=ws)[0]
+            v = float(sse.item())
+            eb = ((xf - xh.double()) ** 2).view(-1, 16).sum(dim=1)
+            rel_b = torch.sqrt(eb[nz] / blk2[nz])
+            zero_b = ((xh.view(-1, 16) == 0).all(dim=1) & nz)
+            r[fmt] = {"mse": v / x.numel(), "rel_error": (v / e2) ** 0.5,
+                      "mean_block_rel_error": round(float(rel_b.mean().item()), 6),
+                      "zeroed_block_fraction": round(float(zero_b.sum().item()) / int(nz.sum().item()), 6)}
+        res[name] = r
     return res
 
 

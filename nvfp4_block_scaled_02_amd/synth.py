@@ -14,6 +14,9 @@ to bfloat16 with round-to-nearest-even through torch):
   heavy       4096 x 4096  N(0,1) x per-element U(1,9): the heavy-tailed
               activation stand-in of the "UE5M3" blog's scale-format
               experiment (实验)                                          (seed 5)
+  wide        4096 x 4096  N(0,1) x 2^(-24 U(0,1)) per 16-element block: block
+              magnitudes spanning 24 binades, wider than the E4M3 block-scale
+              range under a per-tensor outer scale (about 17.8 binades)  (seed 6)
 `rows` gives a smaller instance of the same recipe (per-row factors, outlier
 channels and outlier positions are drawn at the full shape first, so the kept
 rows see the same ones).  No public dataset
@@ -31,8 +34,10 @@ SHAPES = {
     "qat": (14336, 4096),
     "gradient": (16384, 8192),
     "heavy": (4096, 4096),
+    "wide": (4096, 4096),
 }
-SEEDS = {"weight-1k": 0, "weight": 1, "activation": 2, "qat": 3, "gradient": 4, "heavy": 5}
+SEEDS = {"weight-1k": 0, "weight": 1, "activation": 2, "qat": 3, "gradient": 4, "heavy": 5,
+         "wide": 6}
 
 
 def to_bf16_bits(a) -> np.ndarray:
@@ -73,6 +78,9 @@ def make(name: str, rows: int = None):
         x = rng.standard_normal((r, C)) * f[:r, None]
     elif name == "heavy":
         x = rng.standard_normal((r, C)) * rng.uniform(1.0, 9.0, size=(r, C))
+    elif name == "wide":
+        f = 2.0 ** (-24.0 * rng.uniform(0.0, 1.0, size=(R, C // 16)))
+        x = (rng.standard_normal((r, C // 16, 16)) * f[:r, :, None]).reshape(r, C)
     else:
         raise KeyError(name)
     return {"x": to_bf16_bits(x)}

@@ -123,23 +123,25 @@ class Timer:
             torch.cuda.synchronize()
         return i
 
-    def avg_us(self, fn, reps, nsets, name=None, repeats=9):
+    def avg_us(self, fn, reps, nsets, name=None, repeats=9, lead=20, settle_s=0.2):
         """Average duration of one fn(i) over `reps` back-to-back calls,
-        timed by events on this stream; the median of `repeats` runs.  With
-        graphs enabled the calls are captured into a HIP graph (kernel nodes
-        only: every output and the workspace are preallocated) and its
-        replays are timed instead; if the capture fails the calls run
-        eagerly.  In profile mode (--profile-once) fn(0) and fn(1) run once
-        each, untimed, for the PMC counters."""
+        timed by events on this stream; the median of `repeats` runs.  The
+        calls run untimed for `settle_s` seconds first, and every timed run
+        follows `lead` untimed calls issued without a synchronization in
+        between, so that the timed region starts on a busy GPU (timed right
+        after the host has waited for an idle GPU, the same launches run
+        10-20% slower for a while).  With graphs enabled the calls are
+        captured into a HIP graph (kernel nodes only: every output and the
+        workspace are preallocated) and its replays are timed instead; if the
+        capture fails the calls run eagerly.  In profile mode (--profile-once)
+        fn(0) and fn(1) run once each, untimed, for the PMC counters."""
         torch = self.torch
         if self.profile:
             fn(0)
             fn(1 % nsets)
             torch.cuda.synchronize()
             return 1.0
-        for i in range(max(nsets, 8)):
-            fn(i)
-        torch.cuda.synchronize()
+        self.settle(fn, settle_s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         times = []
         try:
@@ -152,6 +154,7 @@ class Timer:
             g.replay()
             torch.cuda.synchronize()
             for _ in range(repeats):
+                g.replay()
                 e0.record(self.stream)
                 g.replay()
                 e1.record(self.stream)
@@ -164,6 +167,8 @@ class Timer:
                 log(f"graph capture failed ({ex!r}); timing eager launches")
             torch.cuda.synchronize()
             for _ in range(repeats):
+                for i in range(lead):
+                    fn(i)
                 e0.record(self.stream)
                 for i in range(reps):
                     fn(i)
@@ -452,8 +457,10 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
                     "gelem_per_s": round(n / (ms_step * 1e-3) / 1e9, 2)}
     finish(line, kernels, args, {k: measured_traffic(k) for k in kernels},
            roofline_kernel="quantize_4over6")
-    line["timing"] = {"kernels": f"median of 9 runs of {reps} back-to-back launches "
-                                 "(HIP events on the launch stream)", "modes": timer.modes}
+    line["timing"] = {"kernels": f"median of 9 runs of {reps} back-to-back launches (HIP events on "
+                                 "the launch stream), each run right behind 20 untimed launches, "
+                                 "after 0.2 s of untimed launches of the same kernel",
+                      "modes": timer.modes}
     t6, t46, t46c = us["quantize_6"], us["quantize_4over6"], us["quantize_4over6_count"]
     line["overhead_4over6"] = {
         "vs_max6_pct": round((t46 - t6) / t6 * 100, 1),

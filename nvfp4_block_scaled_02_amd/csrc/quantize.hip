@@ -133,7 +133,7 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
   const bool dynamic = nwhole >= 3 * nwaves;
   // task t of this workgroup -> its group (increasing in t)
   auto group_of = [&](uint64_t t) -> int64_t { return g0 + (int64_t)(t % W) + (int64_t)(t / W) * nwaves; };
-  uint64_t t = (uint64_t)wv;
+  uint64_t t = (uint64_t)__builtin_amdgcn_readfirstlane(wv);  // wave-uniform
   int64_t g = group_of(t);
   // The first group's loads go out before the outer scale is read and the
   // table built, so their latency overlaps that start-up instead of
@@ -145,6 +145,12 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
   const int64_t c0 = (g < nwhole ? g : 0) * 128 + l;
   uint4 a = ld_nt(x + (c0 < nchunks ? c0 : nchunks - 1));
   uint4 b = ld_nt(x + (c0 + 64 < nchunks ? c0 + 64 : nchunks - 1));
+  // two 1024-lane workgroups per CU: issue priority from progress (measured
+  // on this launch shape only; with eight 256-lane workgroups per CU the
+  // later half of the grid is not the later workgroup of each CU)
+  constexpr bool kPrio = BLOCK == 1024;
+  const ProgressPriority prio((uint64_t)(nwhole / gridDim.x));
+  if (kPrio) prio.set(t);
   const TensorScale ts = tensor_scale(*amax, sg);
   if (threadIdx.x < FmtTraits<FMT>::kCodes)
     tab[threadIdx.x] = scale_entry(FMT, threadIdx.x, ts.alpha);
@@ -159,7 +165,10 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
       if (l == 0) tn = __hip_atomic_fetch_add(&next_task, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       tn = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tn >> 32)) << 32) |
            __builtin_amdgcn_readfirstlane((uint32_t)tn);
+    } else {
+      tn = t + W;
     }
+    if (kPrio) prio.set(tn);
     bounce_pair(reg, l, a, b);
     const int64_t bk = g * 64 + l;
     const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)bk * 16, key0);
@@ -168,12 +177,8 @@ __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t
     st_nt(make_uint2(o.c0, o.c1), codes + bk);
     scales[bk] = (uint8_t)o.scale;
     n4 += o.four;
-    if (dynamic) {
-      t = tn;
-      g = group_of(t);
-    } else {
-      g += nwaves;
-    }
+    t = tn;
+    g = group_of(t);
     if (g < nwhole) {
       a = ld_nt(x + g * 128 + l);
       b = ld_nt(x + g * 128 + 64 + l);

@@ -440,39 +440,6 @@ __device__ __forceinline__ void bounce_pair(uint4* reg, int l, uint4 a, uint4 b)
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ---------------------------------------------------------------- issue priority
-// A SIMD issues from its oldest ready wavefront first, so of the workgroups
-// that share a CU the one dispatched first runs ahead; once it has finished,
-// the later one runs its remaining work at half the occupancy.  The
-// persistent kernels counter that with the wavefront issue priority: the
-// later-dispatched half of the grid starts one level above the earlier half,
-// and every wavefront drops one level at each third of its workgroup's task
-// list, so the workgroup that is ahead yields to the one that is behind.
-// Same-box A/B on the one-lane-per-block quantizer (two 1024-lane workgroups
-// per CU, steady-state timing, outputs identical): scale sweep 517 -> 507 us,
-// SR row stream at 16384x8192 60.0 -> 59.5 us, counting 4/6 at 4096x4096
-// 10.87 -> 10.68 us; the 4/6 quantizer at 8192x4096 even (15.9 us).
-struct ProgressPriority {
-  uint64_t c1, c2, c3;  // tasks at which the level drops: ceil(kT/3), k = 1, 2, 3
-  int top;              // level at task 0
-  // tasks: about the number of tasks of one workgroup (T above)
-  __device__ explicit ProgressPriority(uint64_t tasks) {
-    const uint64_t T = tasks > 0 ? tasks : 1;
-    c1 = (T + 2) / 3;
-    c2 = (2 * T + 2) / 3;
-    c3 = T;
-    top = 2 + (blockIdx.x >= gridDim.x / 2 ? 1 : 0);
-  }
-  // sets the calling wavefront's priority for its task `task` (uniform)
-  __device__ __forceinline__ void set(uint64_t task) const {
-    const int v = top - (task >= c1 ? 1 : 0) - (task >= c2 ? 1 : 0) - (task >= c3 ? 1 : 0);
-    if (v >= 3) asm volatile("s_setprio 3");
-    else if (v == 2) asm volatile("s_setprio 2");
-    else if (v == 1) asm volatile("s_setprio 1");
-    else asm volatile("s_setprio 0");
-  }
-};
-
 // Workgroups of kThreads lanes of kernel KERN one CU holds at once (its
 // register and LDS use), at least 1; looked up once per kernel.
 template <auto KERN>

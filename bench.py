@@ -428,9 +428,11 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
     quant_k(0)
     torch.cuda.synchronize()
     assert all(torch.equal(ref[k], outs[0][k]) for k in ref), "graph replay differs from eager"
+    # max->6 (another kernel) is timed between the two 4/6 loops, so that a
+    # kernel trace shows the non-counting loop as a run of its own
+    us["quantize_6"] = timer.avg_us(quant6_k, reps, nsets, "quantize_6")
     us.update({
         "quantize_4over6_count": timer.avg_us(quant_count_k, reps, nsets, "quantize_4over6_count"),
-        "quantize_6": timer.avg_us(quant6_k, reps, nsets, "quantize_6"),
         "tensor_amax": timer.avg_us(amax_k, reps, nsets, "tensor_amax"),
         "dequantize_f32_mse": timer.avg_us(lambda i: deq_k(i, sse_k), reps, nsets,
                                            "dequantize_f32_mse"),

@@ -19,7 +19,9 @@ Timing: the GPU clocks are first settled by about a second of steps; then
 stream, synchronized on both sides).  Per-kernel figures time back-to-back
 launches of one kernel, bracketed by HIP events on the launch stream (the
 host issues a launch in less time than the kernels here take, so the queue
-never drains); the median of nine such runs is reported.  `--graph` replays
+never drains); the median of nine such runs is reported.  Each kernel first
+runs untimed for 0.2 s and each timed run follows 20 untimed launches, so
+the timed region starts on a busy GPU (steady state).  `--graph` replays
 a HIP graph of the same launches instead (measured: the same for most
 kernels, 2 us slower for the Four-Over-Six quantizer).
 

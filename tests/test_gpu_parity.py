@@ -174,6 +174,24 @@ def test_small_ragged_4over6_without_count(rows, cols):
                       oracle_quantize(xb, A, select="4over6"), f"{rows}x{cols} 4/6 without count")
 
 
+@pytest.mark.parametrize("select,rounding,fmt,count4", [("4over6", "rne", "e4m3", False),
+                                                      ("4over6", "rne", "e4m3", True),
+                                                      ("6", "sr", "ue5m3", False)])
+def test_task_counter_with_partial_group(select, rounding, fmt, count4):
+    """6151x4112: 24,700 whole groups of 64 blocks and a partial group of 7.
+    On a 256-CU GPU this takes the 1024-lane launch with the workgroups'
+    task counters (three or more groups per wavefront), so the partial group
+    goes to whichever wavefront draws task nwhole."""
+    rows, cols = 6151, 4112
+    rng = np.random.default_rng(6151)
+    xb = synth.to_bf16_bits((rng.standard_t(3, size=(rows, cols)) * 0.5).astype(np.float32))
+    A = float(O.tensor_amax(xb))
+    log(f"task counter {rows}x{cols} {select} {rounding} {fmt} count4={count4}")
+    got = run_quantize(xb, A, fmt=fmt, select=select, rounding=rounding, seed=77, count4=count4)
+    ref = oracle_quantize(xb, A, fmt=fmt, select=select, rounding=rounding, seed=77)
+    assert_same_quant(got, ref, f"{rows}x{cols} {select} {rounding} {fmt}")
+
+
 def test_config3_activation_8192x4096_with_mse():
     xb = synth.make("activation")["x"]
     x = dev_bf16(xb)

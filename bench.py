@@ -19,7 +19,9 @@ Timing: the GPU clocks are first settled by about a second of steps; then
 stream, synchronized on both sides).  Per-kernel figures time back-to-back
 launches of one kernel, bracketed by HIP events on the launch stream (the
 host issues a launch in less time than the kernels here take, so the queue
-never drains); the median of nine such runs is reported.  Each kernel first
+never drains); the median of nine such runs is reported.  The launch-bound
+256x1024 workload replays a HIP graph of its launches by default (--eager
+for eager launches: there the host's launch cost sets the pace).  Each kernel first
 runs untimed for 0.2 s and each timed run follows 20 untimed launches, so
 the timed region starts on a busy GPU (steady state).  `--graph` replays
 a HIP graph of the same launches instead (measured: the same for most
@@ -547,7 +549,9 @@ def run_weight(args, torch, np, nv, synth, dev, timer, small):
     line = base_line(metric, step_bytes / (ms_step * 1e-3) / 1e9, "GB/s", args, ms_step,
                      f"{name} {rows}x{cols} bf16 (synthetic, seed {synth.SEEDS[name]})",
                      {"rows": rows, "cols": cols, "elements": n,
-                      "timing": "sum of per-kernel event averages"}, n)
+                      "timing": "sum of per-kernel event averages" +
+                                (", each over replays of a HIP graph of back-to-back launches"
+                                 if not timer.eager else ", eager launches")}, n)
     line["us_per_step"] = round(ms_step * 1e3, 2)
     return finish(line, kernels, args)
 
@@ -935,6 +939,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time per-kernel launches by replaying a HIP graph of them")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches also where graph replay is the default "
+                         "(the launch-bound 256x1024 workload)")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 256 MiB copy, then each timed kernel of the workload twice, untimed "
                          "(for PMC counters); prints no line")
@@ -953,7 +960,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    timer = Timer(torch, dev, eager=not args.graph, profile=args.profile_once)
+    # the 256x1024 workload is bound by launch overhead: its launches are
+    # replayed from a HIP graph unless --eager
+    use_graph = args.graph or (args.workload == "weight-1k" and not args.eager)
+    timer = Timer(torch, dev, eager=not use_graph, profile=args.profile_once)
     if args.profile_once:
         calibration_copy(torch, dev)
     if args.workload == "activation":

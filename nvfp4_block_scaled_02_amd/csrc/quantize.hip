@@ -112,7 +112,10 @@ quantize_rows_kernel(const uint4* __restrict__ x, int64_t nchunks, const float* 
 // with the count; medians of 21 interleaved runs; outputs identical).  With
 // fewer than three groups per wavefront (4096x4096: two) there is little to
 // even out and the counter only adds its latency, so each wavefront keeps the
-// fixed grid-stride share there (tasks j, j + W, ...).
+// fixed grid-stride share there (tasks j, j + W, ...).  Across the two
+// workgroups of a CU the balance comes from the issue priority
+// (ProgressPriority, 1024-lane launches only): it follows the task index, in
+// both modes.
 template <int FMT, int SELECT, int ROUND, bool WIDE, int BLOCK, bool RHT>
 __device__ __forceinline__ void blocks_body(const uint4* __restrict__ x, int64_t nblocks,
                                             const float* __restrict__ amax, float sg, uint64_t seed,

@@ -14,15 +14,6 @@
 
 namespace nvfp4 {
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  // butterfly over the 64 lanes with ds_swizzle-free cross-lane moves
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-    v = v > o ? v : o;
-  }
-  return v;
-}
-
 constexpr int kAmaxUnroll = 4;
 constexpr int kAmaxThreads = 1024;
 
@@ -85,7 +76,7 @@ __global__ void __launch_bounds__(kThreads) row_amax_kernel(const uint4* __restr
       const uint32_t v = chunk_abs_max_bits(ld_nt(xr + i));
       m = m > v ? m : v;
     }
-    m = wave_max_u32(m);
+    m = wave_reduce<MaxU32>(m);
     if (l == 0) out[r] = __uint_as_float(m << 16);
   }
 }

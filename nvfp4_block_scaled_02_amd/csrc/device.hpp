@@ -78,6 +78,27 @@ __device__ __forceinline__ float xor1_f32(float v) {
   return __uint_as_float(xor1_u32(__float_as_uint(v)));
 }
 
+// Value of the lane whose index differs in bit 1, 2 or 3 (inside each row of
+// 16 lanes): quad_perm [2,3,0,1]; row_half_mirror (lane l <- l ^ 7 inside its
+// 8) then quad_perm [3,2,1,0] (l ^ 3); row_ror:8 (a rotation by half a row).
+__device__ __forceinline__ uint32_t xor2_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t xor4_u32(uint32_t v) {
+  const int m = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t xor8_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+}
+template <int D>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v) {
+  if constexpr (D == 1) return xor1_u32(v);
+  else if constexpr (D == 2) return xor2_u32(v);
+  else if constexpr (D == 4) return xor4_u32(v);
+  else return xor8_u32(v);
+}
+
 // Within each group of 4 lanes, lane k receives lane k-1's value (lane 0
 // keeps its own): quad_perm [0,0,1,2].
 __device__ __forceinline__ double shift1_in_quad_f64(double v) {

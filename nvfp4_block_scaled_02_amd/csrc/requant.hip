@@ -400,7 +400,7 @@ dq_amax_rows_kernel(const uint2* __restrict__ codes, const uint8_t* __restrict__
       for (int u = 0; u < kDqaUnroll; ++u) m = umax(m, qd_bits<FMT>(w[u], sb[u]));
     }
     for (; j < row_blocks; j += 64) m = umax(m, qd_bits<FMT>(ld_nt(cr + j), sr[j]));
-    for (int off = 32; off >= 1; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    m = wave_reduce<MaxU32>(m);
     const float v = __uint_as_float(m) * outer_alpha(row_amax[r], sg);
     best = umax(best, __float_as_uint(v) & 0x7FFFFFFFu);
   }

@@ -183,7 +183,7 @@ class Timer:
         if name:
             self.modes[name] = mode
         times.sort()
-        return times[len(times) // 2]
+        return Timing(times[len(times) // 2], times[0], times[-1])
 
 
 def calibration_copy(torch, dev):
@@ -212,11 +212,24 @@ def prepared(nsets, make):
     return lambda i: launches[i % nsets]()
 
 
+class Timing(float):
+    """A median launch time (microseconds) that also carries the fastest
+    and slowest of the runs it is the median of."""
+
+    def __new__(cls, median, lo, hi):
+        t = float.__new__(cls, median)
+        t.lo, t.hi = lo, hi
+        return t
+
+
 def kernel_entry(us, n, bpe):
     gbps = n * bpe / (us * 1e-6) / 1e9
-    return {"us": round(us, 3), "bytes_per_elem": round(bpe, 4), "gbps": round(gbps, 1),
-            "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-            "gelem_per_s": round(n / (us * 1e-6) / 1e9, 1)}
+    e = {"us": round(us, 3), "bytes_per_elem": round(bpe, 4), "gbps": round(gbps, 1),
+         "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+         "gelem_per_s": round(n / (us * 1e-6) / 1e9, 1)}
+    if isinstance(us, Timing):  # the spread of the runs behind the median
+        e["us_runs_min_max"] = [round(us.lo, 3), round(us.hi, 3)]
+    return e
 
 
 def finish(line, kernels, args, traffic=None, roofline_kernel=None):

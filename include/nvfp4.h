@@ -35,7 +35,9 @@
  *    of device memory (16-byte aligned) that the caller zero-fills once before
  *    its first use.  Each workgroup stores its value in its own slot and the
  *    last one to finish combines the slots in a fixed order, in the same
- *    launch; every call that runs to completion leaves the workspace's
+ *    launch (the 4/6 count instead travels in the workgroups' arrivals at a
+ *    few group counters and is added to the output per group: integer sums
+ *    do not depend on the order); every call that runs to completion leaves the workspace's
  *    counters zero again, so it is reused as is.  Calls that may run at the
  *    same time (other streams) need workspaces of their own.
  *  - Arguments are validated on the host before anything is launched; a

@@ -54,14 +54,17 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILE_DIR, "activation_8192x4096_traffic.json")
-# sources each activation-step kernel is built from (a change voids its PMC bytes)
-KERNEL_SOURCES = {
-    "tensor_amax": ["amax.hip", "grid_reduce.hpp", "device.hpp", "common.hpp"],
-    "quantize_4over6": ["quantize.hip", "quantize_core.hpp", "grid_reduce.hpp", "device.hpp",
-                        "common.hpp"],
-    "dequantize_f32_mse": ["dequantize.hip", "grid_reduce.hpp", "device.hpp", "common.hpp"],
+# the committed PMC summary of each workload (profiles/<name>_counters.json):
+# HBM bytes and VALU counters per kernel, with the hash of the sources they
+# were taken on
+PROFILE_NAMES = {
+    "activation": "activation_8192x4096_step", "weight-1k": "weight1k_256x1024",
+    "weight": "weight_4096x4096", "qat": "qat_14336x4096_fakequant",
+    "gradient": "gradient_16384x8192_sr_quantize",
+    "activation-pertoken": "activation_pertoken_8192x4096", "weight-2d": "weight2d_4096x4096",
+    "requant": "requant_8192x4096", "select": "select_8192x4096", "rht": "rht_8192x4096",
 }
+_COMMON_SOURCES = ["grid_reduce.hpp", "device.hpp", "common.hpp"]
 METRIC = "NVFP4 4/6 quantize GB/s (Gelem/s) at 8192x4096 bf16; % of HBM peak"
 
 # algorithmic bytes per element (read + written, each byte counted once)
@@ -89,17 +92,36 @@ def source_hash(files):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of an activation-step kernel from the committed
-    PMC summary, if it was taken on the current kernel source; else None."""
+def kernel_sources(key):
+    """The csrc files the kernel behind bench key `key` is built from (a
+    change to any of them voids its committed counters)."""
+    if key.startswith(("requant", "dequantized_amax")):
+        own = ["requant.hip", "quantize_core.hpp"]
+    elif "rht" in key:
+        own = ["rht.hip", "quantize.hip", "quantize_core.hpp"]
+    elif key.startswith("fakequant"):
+        own = ["fakequant.hip"]
+    elif key.startswith("dequantize"):
+        own = ["dequantize.hip"]
+    elif key.endswith("amax"):
+        own = ["amax.hip"]
+    else:
+        own = ["quantize.hip", "quantize_core.hpp"]
+    return own + _COMMON_SOURCES
+
+
+def measured_counters(workload, key):
+    """The committed PMC figures of one kernel of a workload (HBM bytes per
+    launch, VALU busy, VALU instructions per block), if they were taken on
+    the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)["kernels"][kernel]
+        with open(os.path.join(PROFILE_DIR, PROFILE_NAMES[workload] + "_counters.json")) as f:
+            t = json.load(f)["kernels"][key]
     except (OSError, ValueError, KeyError):
         return None
-    if t.get("source_sha256") != source_hash(KERNEL_SOURCES[kernel]):
+    if t.get("source_sha256") != source_hash(kernel_sources(key)):
         return None
-    return t.get("bytes_per_launch")
+    return t
 
 
 class Timer:
@@ -233,18 +255,35 @@ def kernel_entry(us, n, bpe):
 
 
 def finish(line, kernels, args, traffic=None, roofline_kernel=None):
-    """traffic: kernel -> measured HBM bytes per launch (or None).  The
-    roofline is the named kernel's (the metric's kernel), else the one with
-    the longest average."""
-    traffic = traffic or {}
+    """traffic: kernel -> measured HBM bytes per launch (or None); by default
+    the workload's committed PMC figures (only while they match the kernel
+    sources), which also give each kernel's VALU busy share.  The roofline is
+    the named kernel's (the metric's kernel), else the one with the longest
+    average; beside it, `valu` gives that kernel's VALU-issue ceiling: the
+    time its VALU instructions alone took (the launch time x VALU busy), so
+    busy_pct is the fraction of that ceiling the kernel reaches."""
+    counters = {}
+    if traffic is None:
+        workload = getattr(args, "workload", None)
+        counters = {k: measured_counters(workload, k) for k in kernels} if workload else {}
+        traffic = {k: (c or {}).get("bytes_per_launch") for k, c in counters.items()}
     for k, v in kernels.items():
         v["traffic_bytes"] = traffic.get(k)
+        if counters.get(k):
+            v["valu_busy_pct"] = counters[k].get("valu_busy_pct")
     dominant = roofline_kernel or max(kernels, key=lambda k: kernels[k]["us"])
     d = kernels[dominant]
     line["kernels"] = kernels
     line["roofline"] = {"kernel": dominant, "bound": "hbm", "achieved": d["gbps"],
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d["frac_hbm"],
                         "traffic": traffic.get(dominant)}
+    c = counters.get(dominant)
+    if c and c.get("valu_busy_pct") is not None:
+        busy = c["valu_busy_pct"]
+        line["valu"] = {"kernel": dominant, "busy_pct": busy,
+                        "issue_bound_us": round(d["us"] * busy / 100.0, 3),
+                        "instr_per_16_elem": c.get("valu_instr_per_block"),
+                        "source": "PMC VALUBusy and SQ_INSTS_VALU of the committed profile"}
     return line
 
 
@@ -474,7 +513,7 @@ def run_activation(args, torch, np, nv, synth, dev, timer):
     line["step"] = {"us": round(ms_step * 1e3, 2),
                     "gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                     "gelem_per_s": round(n / (ms_step * 1e-3) / 1e9, 2)}
-    finish(line, kernels, args, {k: measured_traffic(k) for k in kernels},
+    finish(line, kernels, args, None,
            roofline_kernel="quantize_4over6")
     line["timing"] = {"kernels": f"median of 9 runs of {reps} back-to-back launches (HIP events on "
                                  "the launch stream), each run right behind 20 untimed launches, "

@@ -49,6 +49,41 @@ def test_kernel_entry_and_roofline_arithmetic():
     assert bench.finish({}, dict(kernels), None)["roofline"]["kernel"] == "dequantize_f32_mse"
 
 
+def test_committed_counters_need_matching_sources(tmp_path, monkeypatch):
+    """A workload's committed PMC figures feed traffic and the VALU ceiling
+    only while the hash of the kernel's sources matches."""
+    n = 8192 * 4096
+    key = "quantize_4over6"
+    entry = {"bytes_per_launch": 86_100_000, "valu_busy_pct": 50.0, "valu_instr_per_block": 200.0,
+             "source_sha256": bench.source_hash(bench.kernel_sources(key))}
+    (tmp_path / "activation_8192x4096_step_counters.json").write_text(
+        json.dumps({"kernels": {key: entry}}))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    args = SimpleNamespace(workload="activation")
+    line = bench.finish({}, {key: bench.kernel_entry(16.0, n, bench.B_QUANT)}, args, None, key)
+    assert line["roofline"]["traffic"] == 86_100_000
+    assert line["kernels"][key]["valu_busy_pct"] == 50.0
+    assert line["valu"]["issue_bound_us"] == 8.0 and line["valu"]["busy_pct"] == 50.0
+    entry["source_sha256"] = "0" * 64  # taken on other sources: not reported
+    (tmp_path / "activation_8192x4096_step_counters.json").write_text(
+        json.dumps({"kernels": {key: entry}}))
+    line = bench.finish({}, {key: bench.kernel_entry(16.0, n, bench.B_QUANT)}, args, None, key)
+    assert line["roofline"]["traffic"] is None and "valu" not in line
+
+
+def test_committed_counters_match_the_current_sources():
+    """Every committed counters file names each kernel's sources as the bench
+    does (so a change to a kernel voids exactly its own figures)."""
+    for name in bench.PROFILE_NAMES.values():
+        path = os.path.join(bench.PROFILE_DIR, name + "_counters.json")
+        if not os.path.exists(path):
+            continue
+        with open(path) as f:
+            kernels = json.load(f)["kernels"]
+        for key, t in kernels.items():
+            assert t["sources"] == bench.kernel_sources(key), (name, key)
+
+
 def test_base_line_fields():
     args = SimpleNamespace(steps=7, warmup=3)
     line = bench.base_line(bench.METRIC, 1234.56, "GB/s", args, 0.07, "w", {"rows": 2}, 1000)

@@ -27,7 +27,10 @@ SELECT_4OVER6_MAE, SELECT_4OVER6_MAXERR, SELECT_SWEEP = 2, 3, 4
 ROUND_RNE, ROUND_SR = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# NVFP4_ORACLE_LIB names another build of nvfp4_oracle.c to load instead: the
+# test that plants a mistake in a copy of the oracle runs the pins against it
+_LIB_OVERRIDE = os.environ.get("NVFP4_ORACLE_LIB")
+_LIB_PATH = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _f32p = ctypes.POINTER(ctypes.c_float)
@@ -42,7 +45,8 @@ def _load():
     if _lib is not None:
         return _lib
     src = os.path.join(_HERE, "nvfp4_oracle.c")
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+    if not _LIB_OVERRIDE and (not os.path.exists(_LIB_PATH) or
+                              os.path.getmtime(_LIB_PATH) < os.path.getmtime(src)):
         _build.build()
     lib = ctypes.CDLL(_LIB_PATH)
     lib.or_e2m1_value.restype = ctypes.c_double

@@ -13,17 +13,18 @@ SRC = os.path.join(HERE, "nvfp4_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [
-        "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-        "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-        "-o", LIB + ".tmp", SRC, "-lm",
-    ]
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+          "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+    """Compile `src` (the oracle, or a copy of it) into the shared library `lib`."""
+    cmd = ["gcc", *CFLAGS, "-o", lib + ".tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -425,12 +425,14 @@ quantize_tiles_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
   static_assert(!(RHT && (DO_ROW || TILE2D)), "the transform applies to column blocks only here");
   constexpr int kAhead = DO_ROW ? 2 : 1;
   // Two tile buffers for the fused max->6 walks (row and column blocks, RNE
-  // or SR): tile t + 1 goes to the other buffer, so the barrier after a
-  // tile's reads is needed only where staged outputs are flushed (one tile in
-  // four).  Fused SR at 16384x8192: 122.1 / 122.5 vs 123.1 / 123.3 us
-  // (interleaved same-box runs).  The fused Four-Over-Six walks would grow
-  // from 122 to 129 VGPRs (4 -> 3 wavefronts per SIMD) and keep one buffer.
-  constexpr bool kDbuf = DO_ROW && DO_COL && !TILE2D && SELECT == SELECT_6;
+  // or SR, 16x16 tiles too): tile t + 1 goes to the other buffer, so the
+  // barrier after a tile's reads is needed only where staged outputs are
+  // flushed (one tile in four).  Fused SR at 16384x8192: 122.1 / 122.5 vs
+  // 123.1 / 123.3 us; 16x16 tiles, both layouts, at 4096x4096: 17.97 vs
+  // 18.08 us (interleaved same-box runs).  The fused Four-Over-Six walks
+  // would grow from 122 to 129 VGPRs (4 -> 3 wavefronts per SIMD) and keep
+  // one buffer.
+  constexpr bool kDbuf = DO_ROW && DO_COL && SELECT == SELECT_6;
   __shared__ f32x2 tab[FmtTraits<FMT>::kCodes];
   __shared__ __attribute__((aligned(16))) uint8_t tile_buf[(kDbuf ? 2 : 1) * kTR * kTilePitch];
   __shared__ uint32_t ct[DO_COL ? kSW * kCtPitch : 1];

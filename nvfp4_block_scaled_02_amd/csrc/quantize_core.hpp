@@ -483,9 +483,15 @@ constexpr int kStPitch = kStBytes + 4;          // LDS pitch (bytes), padded
 // per pass (same-box A/B against one read and one store per pass: column SR
 // at 16384x8192 82.2 -> 80.0 us, column 4/6 with the transform 27.7 -> 26.1,
 // 16x16 tiles both layouts 18.9 -> 18.2, NVFP4 re-quantization 25.3 -> 24.5;
-// outputs identical).  The uniform offset of each store is made opaque to the compiler
+// outputs identical).  The uniform offset of the passes is one running scalar
+// (+ columns per pass x row stride each pass), made opaque to the compiler
 // where it is used: otherwise it hoists every pass's address out of the walk
-// and keeps them all live (twice the registers).
+// and keeps them all live (twice the registers).  One running offset instead
+// of one opaque offset per pass also halves the walkers' scalar-register
+// spills (fused SR 48 -> 26, NVFP4 re-quantization 30+ -> 11): same-box,
+// column 4/6 with the transform 25.43 -> 24.60 us, NVFP4 re-quantization
+// 24.53 -> 23.81, 16x16 tiles both layouts 17.99 -> 17.61, column SR 80.1 ->
+// 79.5, fused SR 122.2 -> 121.6.
 // NT: non-temporal code stores (measured faster for the re-quantization's
 // walk, slower for the quantizer's column-wise walk).
 template <bool NT = false>
@@ -508,9 +514,10 @@ __device__ __forceinline__ void flush_codes_t(const uint32_t* ct, uint8_t* __res
   uint32_t v[kPasses];
 #pragma unroll
   for (int u = 0; u < kPasses; ++u) v[u] = ct[(u * kStep + cl) * kCtPitch + wd];
+  const int64_t step = (int64_t)kStep * stride;
+  int64_t su = 0;
 #pragma unroll
-  for (int u = 0; u < kPasses; ++u) {
-    int64_t su = (int64_t)u * kStep * stride;
+  for (int u = 0; u < kPasses; ++u, su += step) {
     asm volatile("" : "+s"(su));
     if (whole_strip || c0 + u * kStep + cl < cols) {
       uint32_t* p = reinterpret_cast<uint32_t*>(base + su + lane_off);
@@ -537,14 +544,15 @@ __device__ __forceinline__ void flush_scales_t(const uint8_t* st, uint8_t* __res
   uint8_t* const base = scales_t + c0 * stride + (row0 >> 4);  // uniform
   const int64_t lane_off = (int64_t)cl * stride + bt;
   const bool whole_strip = c0 + kSW <= cols;
+  const int64_t step = (int64_t)kStep * stride;
+  int64_t su = 0;
 #pragma unroll 1
   for (int u0 = 0; u0 < kSW / kStep; u0 += kBatch) {
     uint8_t v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) v[u] = st[((u0 + u) * kStep + cl) * kStPitch + bt];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      int64_t su = (int64_t)(u0 + u) * kStep * stride;
+    for (int u = 0; u < kBatch; ++u, su += step) {
       asm volatile("" : "+s"(su));
       if (whole_strip || c0 + (u0 + u) * kStep + cl < cols) base[su + lane_off] = v[u];
     }

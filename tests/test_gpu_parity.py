@@ -274,6 +274,51 @@ def test_zero_tensor_and_signed_zeros():
     assert np.all(got["scales"] == 0)
 
 
+def _bf16_bits(v):
+    return np.array([v], np.float32).view(np.uint32)[0] >> 16
+
+
+@pytest.mark.parametrize("rows,cols,axes", [(48, 144, "both"), (48, 136, "col"), (80, 272, "both")])
+@pytest.mark.parametrize("select,rounding,fmt", [("4over6", "rne", "e4m3"), ("6", "sr", "ue5m3")])
+def test_partial_tiles_with_non_finite_edges(rows, cols, axes, select, rounding, fmt):
+    """The strip walker loads a partial tile with addresses clamped to the
+    tensor's last row and last 8-column chunk, so the chunks of the tile that
+    lie outside the tensor repeat those edge values.  With NaN, infinity and
+    the largest bf16 on the last row and in the last columns, the stored
+    outputs and the 4/6 count must still be the oracle's: no block of the
+    tensor mixes with the repeated copies."""
+    rng = np.random.default_rng(rows * 1000 + cols)
+    xb = synth.to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32))
+    xb[rows - 1, 5] = _bf16_bits(np.inf)
+    xb[rows - 1, cols - 3] = _bf16_bits(np.nan)
+    xb[rows - 3, cols - 1] = 0x7F7F  # largest finite bf16
+    xb[rows - 1, cols - 20] = 0xFF80  # -inf
+    A = 3.0  # a stale, finite outer amax: the edge values clip or give NaN blocks
+    log(f"partial tiles {rows}x{cols} {axes} {select} {rounding} {fmt}")
+    got = run_quantize(xb, A, fmt=fmt, select=select, rounding=rounding, axes=axes, seed=9,
+                       count4=select == "4over6")
+    ref = oracle_quantize(xb, A, fmt=fmt, select=select, rounding=rounding, axes=axes, seed=9)
+    assert_same_quant(got, ref, f"partial tiles {rows}x{cols} {axes}")
+
+
+def test_partial_2d_tiles_with_non_finite_edges():
+    """The same for 16x16 tile scales: a NaN and an infinity on the last row
+    of a ragged tensor reach only their own tiles."""
+    rows, cols = 48, 144
+    rng = np.random.default_rng(3)
+    xb = synth.to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32))
+    xb[rows - 1, 3] = _bf16_bits(np.inf)
+    xb[rows - 1, cols - 2] = _bf16_bits(np.nan)
+    a = 4.0
+    q = nv.quantize_2d(dev_bf16(xb), _amax_t(a))
+    torch.cuda.synchronize()
+    got = [q.codes.cpu().numpy(), q.scales.cpu().numpy(), q.codes_t.cpu().numpy(),
+           q.scales_t.cpu().numpy()]
+    ref = O.quantize_2d(xb, a)
+    for g, r, k in zip(got, ref, ("codes", "scales", "codes_t", "scales_t")):
+        assert np.array_equal(g, r), k
+
+
 @pytest.mark.parametrize("bad", [float("nan"), float("inf"), -1.0])
 def test_unusable_amax_gives_nan_scales(bad):
     xb = synth.random_bf16(32, 64, seed=2)

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 7
+#define NVFP4_ABI_VERSION 8
 
 /* Size of a workspace (see the conventions above). */
 #define NVFP4_WORKSPACE_BYTES 66688
@@ -334,6 +334,21 @@ int nvfp4_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* row_ama
  *   row-major element index r * cols + c.
  */
 int nvfp4_quantize_rowscaled(const nvfp4_quant_args* args, hipStream_t stream);
+
+/*
+ * nvfp4_quantize_pertoken -- per-token quantization: nvfp4_row_amax and
+ * then nvfp4_quantize_rowscaled with those amaxes ("End-to-End 4-Bit
+ * Training", Recipe details: per-token outer scales), in one launch that
+ * reads each row once when cols <= 4096 (longer rows: those two launches).
+ *   row_amax_out  [rows] float, 4-byte aligned; written with the row amaxes
+ *                 (rules of nvfp4_row_amax), which the quantization uses.
+ *   args->amax    not read.  args->axes must be NVFP4_AXIS_ROW.
+ *   Other fields, outputs and errors as nvfp4_quantize_rowscaled; the codes,
+ *   scales and count4 are bit for bit those of nvfp4_row_amax followed by
+ *   nvfp4_quantize_rowscaled.  cols == 0 writes 0 to every row amax.
+ */
+int nvfp4_quantize_pertoken(const nvfp4_quant_args* args, float* row_amax_out,
+                            hipStream_t stream);
 
 /*
  * nvfp4_dequantize_rowscaled -- nvfp4_dequantize with per-row outer scales:

@@ -6,12 +6,12 @@ does not load the library; the first call does, and raises if it is not built.
 """
 from .api import (Launch, Quantized, default_global_max, dequantize, dequantize_rowscaled,
                   dequantize_rht, dequantized_amax, fakequant_bwd, fakequant_fwd, quantize,
-                  quantize_2d, quantize_rht, quantize_rowscaled, requantize_t, rht_amax, row_amax,
-                  tensor_amax, workspace, prepare, prepare_quantize, prepare_dequantize,
-                  prepare_tensor_amax)
+                  quantize_2d, quantize_pertoken, quantize_rht, quantize_rowscaled, requantize_t,
+                  rht_amax, row_amax, tensor_amax, workspace, prepare, prepare_quantize,
+                  prepare_dequantize, prepare_tensor_amax)
 
 __all__ = ["Launch", "Quantized", "default_global_max", "dequantize", "dequantize_rowscaled",
            "dequantize_rht", "dequantized_amax", "fakequant_bwd", "fakequant_fwd", "quantize",
-           "quantize_2d", "quantize_rht", "quantize_rowscaled", "requantize_t", "rht_amax",
-           "row_amax", "tensor_amax", "workspace", "prepare", "prepare_quantize",
+           "quantize_2d", "quantize_pertoken", "quantize_rht", "quantize_rowscaled", "requantize_t",
+           "rht_amax", "row_amax", "tensor_amax", "workspace", "prepare", "prepare_quantize",
            "prepare_dequantize", "prepare_tensor_amax"]

@@ -9,7 +9,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
-ABI_VERSION = 7  # NVFP4_ABI_VERSION of include/nvfp4.h that these signatures follow
+ABI_VERSION = 8  # NVFP4_ABI_VERSION of include/nvfp4.h that these signatures follow
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 SCALE_E4M3, SCALE_UE5M3 = 0, 1
@@ -51,6 +51,7 @@ SIGNATURES = {
                                 _vp, _vp]),
     "nvfp4_row_amax": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "nvfp4_quantize_rowscaled": (_int, [_qa, _vp]),
+    "nvfp4_quantize_pertoken": (_int, [_qa, _vp, _vp]),
     "nvfp4_dequantize_rowscaled": (_int, [_vp, _vp, _i64, _i64, _vp, _f32, _int, _vp, _vp, _vp,
                                           _vp, _vp, _vp, _vp]),
     "nvfp4_quantize_2d": (_int, [_qa, _vp]),

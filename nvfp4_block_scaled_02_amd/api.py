@@ -323,6 +323,29 @@ def quantize_rowscaled(x: torch.Tensor, row_amaxes: Optional[torch.Tensor] = Non
                      out.get("count4"))
 
 
+def quantize_pertoken(x: torch.Tensor, *, fmt: str = "e4m3", select: str = "4over6",
+                      rounding: str = "rne", seed: int = 0, global_max: float = 0.0,
+                      count4: bool = False, out: Optional[dict] = None,
+                      row_amaxes: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> Quantized:
+    """row_amax(x) and quantize_rowscaled(x, ...) in one launch: the row
+    amaxes are computed on the device and written to row_amaxes (new if not
+    given), which Quantized.amax holds."""
+    rows, cols = _need_2d(x, torch.bfloat16, "x")
+    if row_amaxes is None:
+        row_amaxes = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _need(row_amaxes, torch.float32, "row_amaxes", rows)
+    out = _quant_outputs(out, rows, cols, N.AXIS_ROW, count4, x.device)
+    ws = _ws(workspace, x.device) if "count4" in out else None
+    args = _quant_args(x, rows, cols, None, global_max, fmt, select, rounding, N.AXIS_ROW, seed,
+                       out, ws)
+    _invoke("nvfp4_quantize_pertoken", (ctypes.byref(args), _ptr(row_amaxes)), x.device,
+            (x, row_amaxes, out, ws, args))
+    gm = float(global_max) if global_max else default_global_max(fmt, select)
+    return Quantized(out["codes"], out["scales"], None, None, row_amaxes, gm, fmt,
+                     out.get("count4"))
+
+
 def dequantize_rowscaled(codes: torch.Tensor, scales: torch.Tensor, row_amaxes: torch.Tensor, *,
                          global_max: float, fmt: str = "e4m3", out_dtype=torch.float32,
                          want_block_scale: bool = False, x_ref: Optional[torch.Tensor] = None,

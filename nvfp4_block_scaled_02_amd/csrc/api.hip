@@ -264,6 +264,21 @@ int nvfp4_quantize_rowscaled(const nvfp4_quant_args* args, hipStream_t stream) {
   return status_of(launch_quantize_rowscaled(a, stream));
 }
 
+int nvfp4_quantize_pertoken(const nvfp4_quant_args* args, float* row_amax_out,
+                            hipStream_t stream) {
+  if (!args || args->axes != NVFP4_AXIS_ROW) return NVFP4_ERR_INVALID;
+  if (!row_amax_out || ((uintptr_t)row_amax_out & 3u)) return NVFP4_ERR_INVALID;
+  nvfp4_quant_args p = *args;
+  p.amax = row_amax_out;  // args->amax is not read
+  QuantizeArgs a;
+  const int st = quant_common(&p, a);
+  if (st != NVFP4_OK) return st;
+  if (a.rows == 0) return NVFP4_OK;
+  // empty rows: their amaxes (0) are the whole output
+  if (a.cols == 0) return status_of(launch_row_amax(a.x, a.rows, 0, row_amax_out, stream));
+  return status_of(launch_quantize_pertoken(a, row_amax_out, stream));
+}
+
 int nvfp4_dequantize_rowscaled(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                int64_t cols, const float* row_amax, float global_fp8_max,
                                int scale_fmt, float* out_f32, uint16_t* out_bf16,

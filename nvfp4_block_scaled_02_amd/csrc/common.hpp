@@ -84,6 +84,9 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
 hipError_t launch_row_amax(const uint16_t* x, int64_t rows, int64_t cols, float* out, hipStream_t s);
 // a.amax = one amax per row
 hipError_t launch_quantize_rowscaled(const QuantizeArgs& a, hipStream_t s);
+// the row amaxes computed in the same launch and written to row_amax_out
+// (a.amax unused), then as launch_quantize_rowscaled
+hipError_t launch_quantize_pertoken(const QuantizeArgs& a, float* row_amax_out, hipStream_t s);
 // 16x16 tile scales (max->6, RNE); a.axes = ROW or ROW | COL
 hipError_t launch_quantize_2d(const QuantizeArgs& a, hipStream_t s);
 hipError_t launch_dequantize(const DequantizeArgs& a, hipStream_t s);

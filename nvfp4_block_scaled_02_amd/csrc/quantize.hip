@@ -338,6 +338,91 @@ quantize_rowwave_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_b
   if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4, ws);
 }
 
+// Per-token quantization in one launch (row amax and row-scaled blocks),
+// rows of at most kPtChunks 16-byte chunks (4096 columns).  A wavefront owns
+// whole rows and reads each once: its lanes load the row (up to eight
+// 16-byte chunks each, all in flight together), take its amax (the row amax
+// kernel's rules: maxima of the sign-cleared bf16 patterns, so NaN beats
+// infinity beats every finite value) while copying it into the wavefront's
+// 8 KiB of LDS, write the amax, build the row's {S_EFF, INV_S} table, and
+// request the next row into the same registers before quantizing this one's
+// 64-block groups from LDS, so the next row's loads overlap this row's
+// arithmetic.  LDS (36 KiB per 256-lane workgroup) holds four workgroups per
+// CU; only the wavefront itself reads its row and table, and its LDS
+// operations complete in order, so no workgroup barrier is needed.
+constexpr int kPtChunks = 512;
+constexpr int kPtPerLane = kPtChunks / 64;
+
+template <int FMT, int SELECT, int ROUND, bool WIDE>
+__global__ void __launch_bounds__(kThreads)
+quantize_pertoken_kernel(const uint4* __restrict__ x, int64_t rows, int64_t row_blocks,
+                         float* __restrict__ row_amax, float sg, uint64_t seed, uint32_t key0,
+                         uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                         unsigned long long* count4, uint8_t* ws) {
+  constexpr int kTab = (FmtTraits<FMT>::kCodes + 63) / 64 * 64;
+  __shared__ __attribute__((aligned(16))) uint4 rowbuf[kThreads / 64][kPtChunks];
+  __shared__ f32x2 tabs[kThreads / 64][kTab];
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint4* buf = rowbuf[wv];
+  f32x2* tab = tabs[wv];
+  const int64_t nch = row_blocks * 2;  // <= kPtChunks
+  const int64_t ngroups = (row_blocks + 63) / 64;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  uint32_t n4 = 0;
+  int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + wv;
+  uint4 w[kPtPerLane];
+  auto load_row = [&](int64_t rr) {
+    const uint4* xr = x + rr * nch;
+#pragma unroll
+    for (int u = 0; u < kPtPerLane; ++u)
+      if (l + 64 * u < nch) w[u] = xr[l + 64 * u];
+  };
+  if (r < rows) load_row(r);
+  for (; r < rows; r += nwaves) {
+    // the previous row's LDS reads are done before its row and table are
+    // overwritten (program order; the fences keep the compiler to it)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kPtPerLane; ++u)
+      if (l + 64 * u < nch) {
+        buf[l + 64 * u] = w[u];
+        const uint32_t v = chunk_abs_max_bits(w[u]);
+        m = m > v ? m : v;
+      }
+    const float am = __uint_as_float(wave_reduce<MaxU32>(m) << 16);
+    if (l == 0) row_amax[r] = am;
+    TensorScale ts = tensor_scale(am, sg);
+    // the row's constants are uniform over the wavefront: keep them in SGPRs
+    ts.alpha = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ts.alpha)));
+    ts.k6 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ts.k6)));
+    ts.k4 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ts.k4)));
+#pragma unroll
+    for (int c = l; c < kTab; c += 64)
+      if (c < FmtTraits<FMT>::kCodes) tab[c] = scale_entry(FMT, (uint32_t)c, ts.alpha);
+    if (r + nwaves < rows) load_row(r + nwaves);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t ob0 = r * row_blocks + l;
+    for (int64_t g = 0; g < ngroups; ++g) {
+      const int64_t bk = g * 64 + l;  // the lane's block in the row
+      const int64_t ob = ob0 + g * 64;
+      const uint32_t hb = hash_base<ROUND, WIDE>(seed, (uint64_t)ob * 16, key0);
+      const BlockOut o = quantize_block<FMT, SELECT, ROUND>(buf[g * 128 + 2 * l], buf[g * 128 + 2 * l + 1],
+                                                            tab, ts, hb);
+      if (bk < row_blocks) {  // a partial last group's other lanes read stale chunks
+        st_nt(make_uint2(o.c0, o.c1), codes + ob);
+        scales[ob] = (uint8_t)o.scale;
+        n4 += o.four;
+      }
+    }
+  }
+  if (is_four_six(SELECT) && count4) flush_count<kThreads>(count4, n4, ws);
+}
+
 // ---------------------------------------------------------------- column-wise
 // Strip walker.  A workgroup owns a strip of kSW columns and walks down it in
 // tiles of kTR rows.  Each tile is read once (16-byte chunks, 256 bytes per
@@ -676,8 +761,7 @@ static hipError_t launch_fmt(const QuantizeArgs& a, hipStream_t s) {
 }
 
 template <int FMT, int SELECT, int ROUND, bool WIDE>
-static hipError_t launch_rowscaled_typed(const QuantizeArgs& a, hipStream_t s) {
-  const uint32_t key0 = sr_key(a.seed, 0u);
+static hipError_t launch_rowscaled_rows(const QuantizeArgs& a, uint32_t key0, hipStream_t s) {
   const int64_t cus = device_cu_count();
   const int64_t nblocks = a.rows * a.cols / 16;
   const int64_t row_blocks = a.cols / 16;
@@ -700,24 +784,55 @@ static hipError_t launch_rowscaled_typed(const QuantizeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// row_amax_out != nullptr: per-token quantization, the row amaxes computed
+// and written there (a.amax not read); one launch for rows of at most
+// kPtChunks chunks, else the row amax kernel and then the row-scaled one.
+template <int FMT, int SELECT, int ROUND, bool WIDE>
+static hipError_t launch_rowscaled_typed(const QuantizeArgs& a, float* row_amax_out, hipStream_t s) {
+  const uint32_t key0 = sr_key(a.seed, 0u);
+  const int64_t cus = device_cu_count();
+  const int64_t row_blocks = a.cols / 16;
+  if (row_amax_out && row_blocks * 2 <= kPtChunks) {
+    const int64_t grid = cap_grid((a.rows + kThreads / 64 - 1) / (kThreads / 64), cus * 4);
+    hipLaunchKernelGGL((quantize_pertoken_kernel<FMT, SELECT, ROUND, WIDE>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(a.x), a.rows,
+                       row_blocks, row_amax_out, a.sg, a.seed, key0,
+                       reinterpret_cast<uint2*>(a.codes), a.scales, a.count4, a.ws);
+    return hipGetLastError();
+  }
+  QuantizeArgs b = a;
+  if (row_amax_out) {
+    const hipError_t e = launch_row_amax(a.x, a.rows, a.cols, row_amax_out, s);
+    if (e != hipSuccess) return e;
+    b.amax = row_amax_out;
+  }
+  return launch_rowscaled_rows<FMT, SELECT, ROUND, WIDE>(b, key0, s);
+}
+
 template <int FMT>
-static hipError_t launch_rowscaled_fmt(const QuantizeArgs& a, hipStream_t s) {
+static hipError_t launch_rowscaled_fmt(const QuantizeArgs& a, float* row_amax_out, hipStream_t s) {
   if (a.rounding == ROUND_SR) {
     const bool wide = (uint64_t)a.rows * (uint64_t)a.cols > (1ull << 32);
-    return wide ? launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, true>(a, s)
-                : launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, false>(a, s);
+    return wide ? launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, true>(a, row_amax_out, s)
+                : launch_rowscaled_typed<FMT, SELECT_6, ROUND_SR, false>(a, row_amax_out, s);
   }
   switch (a.select) {
-    case SELECT_4OVER6: return launch_rowscaled_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, s);
-    case SELECT_4OVER6_MAE: return launch_rowscaled_typed<FMT, SELECT_4OVER6_MAE, ROUND_RNE, false>(a, s);
-    case SELECT_4OVER6_MAXERR: return launch_rowscaled_typed<FMT, SELECT_4OVER6_MAXERR, ROUND_RNE, false>(a, s);
-    case SELECT_SWEEP: return launch_rowscaled_typed<FMT, SELECT_SWEEP, ROUND_RNE, false>(a, s);
-    default: return launch_rowscaled_typed<FMT, SELECT_6, ROUND_RNE, false>(a, s);
+    case SELECT_4OVER6: return launch_rowscaled_typed<FMT, SELECT_4OVER6, ROUND_RNE, false>(a, row_amax_out, s);
+    case SELECT_4OVER6_MAE: return launch_rowscaled_typed<FMT, SELECT_4OVER6_MAE, ROUND_RNE, false>(a, row_amax_out, s);
+    case SELECT_4OVER6_MAXERR: return launch_rowscaled_typed<FMT, SELECT_4OVER6_MAXERR, ROUND_RNE, false>(a, row_amax_out, s);
+    case SELECT_SWEEP: return launch_rowscaled_typed<FMT, SELECT_SWEEP, ROUND_RNE, false>(a, row_amax_out, s);
+    default: return launch_rowscaled_typed<FMT, SELECT_6, ROUND_RNE, false>(a, row_amax_out, s);
   }
 }
 
 hipError_t launch_quantize_rowscaled(const QuantizeArgs& a, hipStream_t s) {
-  return a.fmt == FMT_E4M3 ? launch_rowscaled_fmt<FMT_E4M3>(a, s) : launch_rowscaled_fmt<FMT_UE5M3>(a, s);
+  return a.fmt == FMT_E4M3 ? launch_rowscaled_fmt<FMT_E4M3>(a, nullptr, s)
+                           : launch_rowscaled_fmt<FMT_UE5M3>(a, nullptr, s);
+}
+
+hipError_t launch_quantize_pertoken(const QuantizeArgs& a, float* row_amax_out, hipStream_t s) {
+  return a.fmt == FMT_E4M3 ? launch_rowscaled_fmt<FMT_E4M3>(a, row_amax_out, s)
+                           : launch_rowscaled_fmt<FMT_UE5M3>(a, row_amax_out, s);
 }
 
 // ---------------------------------------------------------------- transformed blocks

@@ -211,6 +211,28 @@ def test_quantize_rowscaled_empty_ok():
     assert _qrs(rows=0) == N.OK and _qrs(cols=0) == N.OK
 
 
+def _qpt(**kw):
+    ra = kw.pop("ra", FAKE)
+    kw.setdefault("amax", None)  # not read: the call computes the row amaxes
+    return N.lib().nvfp4_quantize_pertoken(_qargs(**kw), ra, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(ra=None), dict(ra=FAKE + 2), dict(rows=-1), dict(cols=24), dict(fmt=2),
+    dict(select=5), dict(rnd=2), dict(rnd=1, select=1), dict(gmax=-1.0), dict(codes=None),
+    dict(scales=None), dict(codes=FAKE_ODD), dict(x=FAKE_ODD), dict(count4=FAKE),
+    dict(axes=2), dict(axes=3),
+])
+def test_quantize_pertoken_rejects(kw):
+    assert _qpt(**kw) == N.ERR_INVALID
+
+
+def test_quantize_pertoken_empty_ok():
+    # no rows: nothing to write and no launch (cols == 0 with rows launches
+    # the row amax, which writes the empty rows' zeros; GPU tests cover it)
+    assert _qpt(rows=0) == N.OK
+
+
 def _dqrs(**kw):
     a = dict(codes=FAKE, scales=FAKE, rows=16, cols=32, ra=FAKE, gmax=448.0, fmt=0,
              f32=FAKE, b16=None, bs=None, xref=None, sse=None, ws=None)

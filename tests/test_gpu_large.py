@@ -156,6 +156,30 @@ def test_rowscaled_sr_past_2_32(big):
     log("row-scaled SR past 2^32: ok")
 
 
+def test_pertoken_sr_past_2_32(big):
+    """The one-launch per-token quantizer past element 2^32 (its WIDE hash
+    path): the same memory viewed as rows of 4096 columns, the longest rows
+    it takes in one launch."""
+    x = big.view(-1, 4096)
+    rows = x.shape[0]
+    first_wide = (1 << 32) // 4096  # the first row whose indices pass 2^32
+    sample = [0, 1, first_wide - 1, first_wide, first_wide + 1, rows - 1]
+    log(f"per-token SR quantize {rows}x4096")
+    q = nv.quantize_pertoken(x, fmt="ue5m3", select="6", rounding="sr", seed=77)
+    torch.cuda.synchronize()
+    xr = _rows_host(x, sample)
+    for i, r in enumerate(sample):
+        ra = O.row_amax(xr[i:i + 1])
+        _same(q.amax[r:r + 1].cpu().numpy().view(np.uint32), ra.view(np.uint32),
+              f"row amax, row {r}")
+        rc, rs, _ = O.quantize_rowscaled(xr[i:i + 1], ra, fmt=O.FMT_UE5M3, select=O.SELECT_6,
+                                         rounding=O.ROUND_SR, seed=77, row0=r)
+        _same(q.scales[r:r + 1].cpu().numpy(), rs, f"scales, row {r}")
+        _same(q.codes[r:r + 1].cpu().numpy(), rc, f"codes, row {r}")
+    del q
+    log("per-token SR past 2^32: ok")
+
+
 def _rand_u8(shape, lo, hi, seed):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
